@@ -1,0 +1,168 @@
+"""CPU oracle for the GEMM D = alpha*A*B + beta*C -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
+leg may import this package. The GPU library never calls it and shares no
+code with it; the product path fails loudly when its HIP library is missing.
+
+The arithmetic lives in ``oracle.c`` (plain fp64 loops, its own format
+decoders and its own round-to-nearest-even encoder); this module only
+marshals numpy arrays through ctypes. Grouped GEMM is, by its definition on
+the pages ("Python packages associated with CUTLASS", Current functionality:
+grouped GEMM runs independent problems in one call), a loop of single GEMMs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+DT = {"f32": 0, "f16": 1, "bf16": 2, "f8e4m3": 3}
+LAYOUT = {"row": 0, "col": 1}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc into liboracle.so next to it."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC",
+                               "-Wall", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        vp = ctypes.c_void_p
+        L.oracle_decode.restype = ctypes.c_double
+        L.oracle_decode.argtypes = [ctypes.c_int, ctypes.c_uint32]
+        L.oracle_encode.restype = ctypes.c_uint32
+        L.oracle_encode.argtypes = [ctypes.c_int, ctypes.c_double]
+        L.oracle_decode_n.argtypes = [ctypes.c_int, vp, ctypes.c_int64, vp]
+        L.oracle_encode_n.argtypes = [ctypes.c_int, vp, ctypes.c_int64, vp]
+        common = [ctypes.c_int] * 8 + [ctypes.c_int64] * 3 + [vp] * 3 + \
+                 [ctypes.c_float] * 4
+        L.oracle_gemm_rows.restype = ctypes.c_int
+        L.oracle_gemm_rows.argtypes = common + [i64p, ctypes.c_int64, vp, vp, vp]
+        L.oracle_gemm_entries.restype = ctypes.c_int
+        L.oracle_gemm_entries.argtypes = common + [i64p, i64p, ctypes.c_int64,
+                                                   vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def decode(dtype: str, bits) -> np.ndarray:
+    """Exact fp64 values of storage bit patterns of ``dtype``."""
+    b = np.ascontiguousarray(np.asarray(bits).astype(np.uint32))
+    out = np.empty(b.shape, dtype=np.float64)
+    lib().oracle_decode_n(DT[dtype], _ptr(b), b.size, _ptr(out))
+    return out
+
+
+def encode(dtype: str, values) -> np.ndarray:
+    """Round-to-nearest-even bit patterns of fp64 ``values`` in ``dtype``."""
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float64))
+    out = np.empty(v.shape, dtype=np.uint32)
+    lib().oracle_encode_n(DT[dtype], _ptr(v), v.size, _ptr(out))
+    return out
+
+
+class Result:
+    """Oracle outputs for selected rows or entries."""
+
+    def __init__(self, ref, S, d_bits, dtype_d):
+        self.ref = ref          # fp64 unrounded epilogue value
+        self.S = S              # |alpha s_A s_B| * sum_k |a b|
+        self.d_bits = d_bits    # element_D bits of the once-rounded value
+        self.dtype_d = dtype_d
+
+    @property
+    def d_exact(self) -> np.ndarray:
+        return decode(self.dtype_d, self.d_bits)
+
+
+def _scalars(p):
+    sa = 1.0 if p.scale_a is None else p.scale_a
+    sb = 1.0 if p.scale_b is None else p.scale_b
+    return float(p.alpha), float(p.beta), float(sa), float(sb)
+
+
+def _operands(p):
+    from synthetic import raw   # storage bytes only
+    A = raw(p.A)
+    B = raw(p.B)
+    C = raw(p.C) if (p.C is not None and p.beta != 0.0) else None
+    return A, B, C
+
+
+def _head(p, relu):
+    return (DT[p.dtype_ab], DT[p.dtype_ab], DT[p.dtype_cd], DT[p.dtype_cd],
+            LAYOUT[p.la], LAYOUT[p.lb], LAYOUT[p.lc], int(bool(relu)),
+            p.M, p.N, p.K)
+
+
+def gemm(p, relu: bool = False, rows: Optional[Sequence[int]] = None) -> Result:
+    """Full rows of D for the problem ``p`` (a ``synthetic.Problem``).
+
+    ``rows`` = None computes all M rows; outputs are [n_rows, N] arrays.
+    """
+    A, B, C = _operands(p)
+    al, be, sa, sb = _scalars(p)
+    if rows is None:
+        rows_arr, n = None, p.M
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = rows_arr.size
+    ref = np.empty((n, p.N), dtype=np.float64)
+    S = np.empty((n, p.N), dtype=np.float64)
+    d = np.empty((n, p.N), dtype=np.uint32)
+    rp = None if rows_arr is None else rows_arr.ctypes.data_as(
+        ctypes.POINTER(ctypes.c_int64))
+    rc = lib().oracle_gemm_rows(*_head(p, relu), _ptr(A), _ptr(B), _ptr(C),
+                                al, be, sa, sb, rp, n, _ptr(ref), _ptr(S),
+                                _ptr(d))
+    if rc != 0:
+        raise ValueError("oracle_gemm_rows: bad arguments")
+    return Result(ref, S, d, p.dtype_cd)
+
+
+def gemm_entries(p, ii, jj, relu: bool = False) -> Result:
+    """Selected outputs D[ii[t], jj[t]], each computed on its own."""
+    A, B, C = _operands(p)
+    al, be, sa, sb = _scalars(p)
+    ii = np.ascontiguousarray(np.asarray(ii, dtype=np.int64))
+    jj = np.ascontiguousarray(np.asarray(jj, dtype=np.int64))
+    n = ii.size
+    ref = np.empty(n, dtype=np.float64)
+    S = np.empty(n, dtype=np.float64)
+    d = np.empty(n, dtype=np.uint32)
+    P = ctypes.POINTER(ctypes.c_int64)
+    rc = lib().oracle_gemm_entries(*_head(p, relu), _ptr(A), _ptr(B), _ptr(C),
+                                   al, be, sa, sb, ii.ctypes.data_as(P),
+                                   jj.ctypes.data_as(P), n, _ptr(ref), _ptr(S),
+                                   _ptr(d))
+    if rc != 0:
+        raise ValueError("oracle_gemm_entries: bad arguments")
+    return Result(ref, S, d, p.dtype_cd)
+
+
+def grouped(problems: List, relu: bool = False) -> List[Result]:
+    """Grouped GEMM = the independent single GEMMs, one after another."""
+    return [gemm(p, relu) for p in problems]

@@ -1,0 +1,240 @@
+/*
+ * CPU oracle for D = alpha * A * B + beta * C   (TEST INFRASTRUCTURE ONLY)
+ *
+ * A plain, slow, obviously correct fp64 implementation of the general matrix
+ * multiply with the fused ReLU epilogue. Only the test-suite, the smoke check
+ * and the benchmark's CPU-baseline leg load this library; the GPU library
+ * never links or calls it, and it shares no code with the GPU library.
+ *
+ * What it follows on the pages:
+ *   - "CUTLASS Python 接口全解析" (gsyq.cn), section 2: plan.run computes
+ *     D = A * B + C; section 2.1: element_A/B/C/D/accumulator are separate
+ *     types bound to the plan, layouts RowMajor/ColumnMajor; section 2.3:
+ *     an elementwise activation (ReLU) fused into the epilogue.
+ *   - "CUTLASS Python接口" (kwkr.cn), section 3.3: D = alpha * A * B + beta * C
+ *     with fp32 accumulation; section 5.2: the activation is applied to the
+ *     result of the linear combination.
+ *   - "Python packages associated with CUTLASS", Current functionality:
+ *     GEMM, fused elementwise epilogue, grouped GEMM (independent problems).
+ *   - "Generating State-of-the-Art GEMMs with TorchInductor's CuteDSL backend",
+ *     section 5.1: FP8 GEMM as a scaled mm (per-tensor scales here).
+ *
+ * Definition computed, for each selected output (i, j):
+ *   acc     = sum_{k=0}^{K-1} a(i,k) * b(k,j)            fp64, increasing k
+ *   acc     = acc * s_A * s_B                             (scales; 1 unless fp8)
+ *   v       = alpha * acc + (beta != 0 ? beta * c(i,j) : 0)
+ *   v       = relu ? (v > 0 ? v : +0) : v
+ *   ref     = v                                           (fp64, unrounded)
+ *   d_exact = v rounded once, to nearest even, to element_D
+ *   S       = |alpha * s_A * s_B| * sum_k |a(i,k) * b(k,j)|  (tolerance scale)
+ * Operands are decoded exactly from their storage bits by this file's own
+ * decoders; products of fp32/fp16/bf16/e4m3 values are exact in fp64.
+ * Layouts: RowMajor X[r][c] = base[r*cols + c]; ColumnMajor X[r][c] =
+ * base[r + c*rows] (packed operands, leading dimension implied).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F8E4M3 = 3 };
+enum { LAYOUT_ROW = 0, LAYOUT_COL = 1 };
+
+/* ---- exact decoders, one per storage format (sign, exponent, fraction) ---- */
+
+static double dec_f32(uint32_t u) {
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+static double dec_f16(uint32_t u) {
+    int s = (u >> 15) & 1, e = (u >> 10) & 31, m = u & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)m, -24);
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + m), e - 25);
+    return s ? -v : v;
+}
+
+/* bfloat16: 1 sign, 8 exponent (bias 127), 7 fraction bits. */
+static double dec_bf16(uint32_t u) {
+    int s = (u >> 15) & 1, e = (u >> 7) & 255, m = u & 127;
+    double v;
+    if (e == 0) v = ldexp((double)m, -133);
+    else if (e == 255) v = m ? NAN : INFINITY;
+    else v = ldexp((double)(128 + m), e - 134);
+    return s ? -v : v;
+}
+
+/* OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent (bias 7), 3 fraction bits;
+ * no infinities, S.1111.111 is NaN, largest finite 448. */
+static double dec_e4m3(uint32_t u) {
+    int s = (u >> 7) & 1, e = (u >> 3) & 15, m = u & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);
+    else v = ldexp((double)(8 + m), e - 10);
+    return s ? -v : v;
+}
+
+double oracle_decode(int dtype, uint32_t bits) {
+    switch (dtype) {
+    case DT_F32: return dec_f32(bits);
+    case DT_F16: return dec_f16(bits);
+    case DT_BF16: return dec_bf16(bits);
+    case DT_F8E4M3: return dec_e4m3(bits);
+    }
+    return NAN;
+}
+
+/* ---- one rounding, to nearest even, from fp64 into fp32 / fp16 / bf16 ---- */
+
+uint32_t oracle_encode(int dtype, double v) {
+    int p, emin, emax, bias, ebits;
+    switch (dtype) {
+    case DT_F32: p = 24; emin = -126; emax = 127; bias = 127; ebits = 8; break;
+    case DT_F16: p = 11; emin = -14; emax = 15; bias = 15; ebits = 5; break;
+    case DT_BF16: p = 8; emin = -126; emax = 127; bias = 127; ebits = 8; break;
+    default: return 0xFFFFFFFFu;
+    }
+    const int fbits = p - 1;
+    const uint32_t sign = signbit(v) ? (1u << (ebits + fbits)) : 0u;
+    const uint32_t exp_all = ((1u << ebits) - 1u) << fbits;
+    if (isnan(v)) return exp_all | (1u << (fbits - 1));      /* quiet NaN */
+    double a = fabs(v);
+    if (isinf(a)) return sign | exp_all;
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);                 /* a = f * 2^e2, f in [0.5, 1) */
+    int E = e2 - 1;                /* a in [2^E, 2^(E+1)) */
+    if (E < emin) E = emin;        /* subnormal range shares emin's quantum */
+    double m = ldexp(a, fbits - E);            /* exact: power-of-two scale */
+    double mr = nearbyint(m);                  /* ties to even (default mode) */
+    if (mr >= ldexp(1.0, p)) { E += 1; mr = ldexp(1.0, fbits); }
+    if (E > emax) return sign | exp_all;       /* overflow -> infinity */
+    uint32_t mant = (uint32_t)mr;
+    if (mant < (1u << fbits)) return sign | mant;   /* subnormal (or zero) */
+    return sign | ((uint32_t)(E + bias) << fbits) | (mant - (1u << fbits));
+}
+
+/* ---- storage access -------------------------------------------------------- */
+
+static uint32_t load_bits(const void *base, int dtype, int64_t idx) {
+    switch (dtype) {
+    case DT_F32: return ((const uint32_t *)base)[idx];
+    case DT_F16:
+    case DT_BF16: return ((const uint16_t *)base)[idx];
+    case DT_F8E4M3: return ((const uint8_t *)base)[idx];
+    }
+    return 0;
+}
+
+/* Element (r, c) of a rows x cols operand stored packed in `layout`. */
+static double elem(const void *base, int dtype, int layout, int64_t rows,
+                   int64_t cols, int64_t r, int64_t c) {
+    int64_t idx = (layout == LAYOUT_ROW) ? r * cols + c : r + c * rows;
+    return oracle_decode(dtype, load_bits(base, dtype, idx));
+}
+
+static int valid_dtype(int d) { return d >= DT_F32 && d <= DT_F8E4M3; }
+
+/* Epilogue of one output: scales, linear combination, activation. */
+static double finish(double acc, double sab, double alpha, double beta,
+                     double c, int relu) {
+    double v = alpha * (acc * sab);
+    if (beta != 0.0) v += beta * c;
+    if (relu) v = (v > 0.0) ? v : 0.0;
+    return v;
+}
+
+/*
+ * Rows mode: computes every column j of each row i listed in `rows`
+ * (rows == NULL selects all M rows in order). Outputs are dense row-major
+ * [n_rows][N]: ref (fp64), S (fp64, optional), d_bits (element_D bits,
+ * optional). Returns 0 on success, -1 on bad arguments.
+ */
+int oracle_gemm_rows(int dtA, int dtB, int dtC, int dtD, int la, int lb,
+                     int lc, int relu, int64_t M, int64_t N, int64_t K,
+                     const void *A, const void *B, const void *C, float alpha,
+                     float beta, float scale_a, float scale_b,
+                     const int64_t *rows, int64_t n_rows, double *ref,
+                     double *S, uint32_t *d_bits) {
+    if (!valid_dtype(dtA) || !valid_dtype(dtB) || !valid_dtype(dtC) ||
+        !valid_dtype(dtD) || M < 0 || N < 0 || K < 0 || !ref)
+        return -1;
+    if (rows == NULL) n_rows = M;
+    const double al = (double)alpha, be = (double)beta;
+    const double sab = (double)scale_a * (double)scale_b;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t i = rows ? rows[r] : r;
+        if (i < 0 || i >= M) { bad = 1; continue; }
+        double *acc = (double *)calloc((size_t)(N ? N : 1), sizeof(double));
+        double *sab_abs = (double *)calloc((size_t)(N ? N : 1), sizeof(double));
+        for (int64_t k = 0; k < K; ++k) {
+            double a = elem(A, dtA, la, M, K, i, k);
+            for (int64_t j = 0; j < N; ++j) {
+                double p = a * elem(B, dtB, lb, K, N, k, j);
+                acc[j] += p;
+                sab_abs[j] += fabs(p);
+            }
+        }
+        for (int64_t j = 0; j < N; ++j) {
+            double c = (be != 0.0) ? elem(C, dtC, lc, M, N, i, j) : 0.0;
+            double v = finish(acc[j], sab, al, be, c, relu);
+            ref[r * N + j] = v;
+            if (S) S[r * N + j] = fabs(al * sab) * sab_abs[j];
+            if (d_bits) d_bits[r * N + j] = oracle_encode(dtD, v);
+        }
+        free(acc);
+        free(sab_abs);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Entries mode: computes the n listed outputs (ii[t], jj[t]) one by one.
+ * Outputs ref[t], S[t] (optional), d_bits[t] (optional).
+ */
+int oracle_gemm_entries(int dtA, int dtB, int dtC, int dtD, int la, int lb,
+                        int lc, int relu, int64_t M, int64_t N, int64_t K,
+                        const void *A, const void *B, const void *C,
+                        float alpha, float beta, float scale_a, float scale_b,
+                        const int64_t *ii, const int64_t *jj, int64_t n,
+                        double *ref, double *S, uint32_t *d_bits) {
+    if (!valid_dtype(dtA) || !valid_dtype(dtB) || !valid_dtype(dtC) ||
+        !valid_dtype(dtD) || M < 0 || N < 0 || K < 0 || !ref || !ii || !jj)
+        return -1;
+    const double al = (double)alpha, be = (double)beta;
+    const double sab = (double)scale_a * (double)scale_b;
+    int bad = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t i = ii[t], j = jj[t];
+        if (i < 0 || i >= M || j < 0 || j >= N) { bad = 1; continue; }
+        double acc = 0.0, sabs = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double p = elem(A, dtA, la, M, K, i, k) * elem(B, dtB, lb, K, N, k, j);
+            acc += p;
+            sabs += fabs(p);
+        }
+        double c = (be != 0.0) ? elem(C, dtC, lc, M, N, i, j) : 0.0;
+        double v = finish(acc, sab, al, be, c, relu);
+        ref[t] = v;
+        if (S) S[t] = fabs(al * sab) * sabs;
+        if (d_bits) d_bits[t] = oracle_encode(dtD, v);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Vector helpers for the tests: decode / encode n values. */
+void oracle_decode_n(int dtype, const uint32_t *bits, int64_t n, double *out) {
+    for (int64_t t = 0; t < n; ++t) out[t] = oracle_decode(dtype, bits[t]);
+}
+
+void oracle_encode_n(int dtype, const double *v, int64_t n, uint32_t *out) {
+    for (int64_t t = 0; t < n; ++t) out[t] = oracle_encode(dtype, v[t]);
+}

@@ -1,0 +1,224 @@
+"""Seeded synthetic inputs for the GEMM D = alpha*A*B + beta*C.
+
+This module is shared by the CPU oracle side and the HIP side. It holds
+random draws and storage-format casts only -- none of the GEMM arithmetic.
+
+Draws follow the distributions the pages use for their examples:
+``torch.rand`` (U[0,1)) in the CUTLASS Python walkthrough ("CUTLASS Python
+接口全解析", section 2.1, fp32 128x256 @ 256x64 with C = 0) and ``torch.randn``
+(N(0,1)) in the CUTLASS Python blog ("CUTLASS Python接口", section 3.3,
+fp16 1024^3). Weight-like operands use N(0, 0.02^2).
+
+Every array is drawn in fp32 with ``numpy.random.default_rng(seed)`` in a
+fixed order (A, then B, then C of each problem) and then cast once, with
+round-to-nearest-even, to the storage type. fp8 operands are quantized per
+tensor: s = max|X| / 448 (fp32), X_q = e4m3fn(clamp(X / s, -448, 448)).
+
+Each generator returns CPU torch tensors in *storage layout*: a RowMajor
+R x C operand is a contiguous [R, C] tensor; a ColumnMajor one is a
+contiguous [C, R] tensor (its transpose). Move them to the GPU with
+``.to(device)``; hand their bytes to the oracle with :func:`raw`.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional, Tuple
+
+import numpy as np
+import torch
+
+# dtype names used across the repository (they match the C enum names)
+F32, F16, BF16, F8 = "f32", "f16", "bf16", "f8e4m3"
+ROW, COL = "row", "col"
+
+TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16,
+               F8: torch.float8_e4m3fn}
+ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, F8: 1}
+E4M3_MAX = 448.0
+
+
+def cast(x32: np.ndarray, dtype: str) -> torch.Tensor:
+    """RNE cast of an fp32 numpy array to the storage dtype (CPU tensor)."""
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
+    if dtype == F8:
+        t = t.clamp(-E4M3_MAX, E4M3_MAX)
+    return t.to(TORCH_DTYPE[dtype])
+
+
+def raw(t: torch.Tensor) -> np.ndarray:
+    """The storage bits of a CPU tensor as a numpy array (no copy when possible)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float32:
+        return t.numpy()
+    if t.dtype in (torch.float16, torch.bfloat16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def to_storage(x32: np.ndarray, layout: str) -> np.ndarray:
+    """Logical [R, C] array -> contiguous storage array for ``layout``."""
+    return np.ascontiguousarray(x32 if layout == ROW else x32.T)
+
+
+@dataclass
+class Problem:
+    """One GEMM's operands in storage layout plus its scalars."""
+    M: int
+    N: int
+    K: int
+    A: torch.Tensor
+    B: torch.Tensor
+    C: Optional[torch.Tensor]
+    alpha: float = 1.0
+    beta: float = 0.0
+    scale_a: Optional[float] = None   # fp8 per-tensor scales (fp32 values)
+    scale_b: Optional[float] = None
+    dtype_ab: str = BF16
+    dtype_cd: str = BF16
+    la: str = ROW
+    lb: str = ROW
+    lc: str = ROW
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+def _draw(rng, shape, dist: str, std: float = 1.0) -> np.ndarray:
+    if dist == "uniform":
+        return rng.random(shape, dtype=np.float32)
+    if dist == "normal":
+        x = rng.standard_normal(shape, dtype=np.float32)
+        return x if std == 1.0 else (x * np.float32(std)).astype(np.float32)
+    if dist == "ones":
+        return np.ones(shape, dtype=np.float32)
+    if dist == "zeros":
+        return np.zeros(shape, dtype=np.float32)
+    raise ValueError(dist)
+
+
+def quantize_e4m3(x32: np.ndarray) -> Tuple[torch.Tensor, float]:
+    """Per-tensor fp8 quantization of an fp32 array: (X_q, s) with X ~ s * X_q."""
+    amax = float(np.max(np.abs(x32))) if x32.size else 0.0
+    s = np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+    q = cast((x32 / s).astype(np.float32), F8)
+    return q, float(s)
+
+
+def make_problem(M: int, N: int, K: int, *, dtype_ab: str, dtype_cd: str,
+                 la: str = ROW, lb: str = ROW, lc: str = ROW,
+                 dist_a: str = "normal", dist_b: str = "normal",
+                 dist_c: Optional[str] = None, std_b: float = 1.0,
+                 alpha: float = 1.0, beta: float = 0.0,
+                 seed: int = 0, rng=None) -> Problem:
+    """Draw A (M x K), B (K x N) and, if ``dist_c`` is given, C (M x N)."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    a32 = _draw(rng, (M, K), dist_a)
+    b32 = _draw(rng, (K, N), dist_b, std_b)
+    c = None
+    if dist_c is not None:
+        c32 = _draw(rng, (M, N), dist_c)
+        c = cast(to_storage(c32, lc), dtype_cd)
+    sa = sb = None
+    if dtype_ab == F8:
+        A, sa = quantize_e4m3(to_storage(a32, la))
+        B, sb = quantize_e4m3(to_storage(b32, lb))
+    else:
+        A = cast(to_storage(a32, la), dtype_ab)
+        B = cast(to_storage(b32, lb), dtype_ab)
+    return Problem(M, N, K, A, B, c, alpha, beta, sa, sb, dtype_ab, dtype_cd,
+                   la, lb, lc)
+
+
+def integer_problem(M: int, N: int, K: int, *, dtype_ab: str, dtype_cd: str,
+                    la: str = ROW, lb: str = ROW, lc: str = ROW,
+                    lo: int = -2, hi: int = 2, beta: float = 1.0,
+                    alpha: float = 1.0, with_c: bool = True,
+                    seed: int = 0) -> Problem:
+    """Integer-valued operands in [lo, hi] (exact in every storage type)."""
+    rng = np.random.default_rng(seed)
+    a32 = rng.integers(lo, hi + 1, size=(M, K)).astype(np.float32)
+    b32 = rng.integers(lo, hi + 1, size=(K, N)).astype(np.float32)
+    c = None
+    if with_c:
+        c32 = rng.integers(lo, hi + 1, size=(M, N)).astype(np.float32)
+        c = cast(to_storage(c32, lc), dtype_cd)
+    A = cast(to_storage(a32, la), dtype_ab)
+    B = cast(to_storage(b32, lb), dtype_ab)
+    sa = sb = (1.0 if dtype_ab == F8 else None)
+    return Problem(M, N, K, A, B, c, alpha, beta if with_c else 0.0, sa, sb,
+                   dtype_ab, dtype_cd, la, lb, lc)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads (shapes and distributions of the pages' examples)
+# ---------------------------------------------------------------------------
+
+def config1(seed: int = 0) -> Problem:
+    """fp32 RowMajor 128x64x256, A, B ~ U[0,1), C = 0, alpha = beta = 1."""
+    return make_problem(128, 64, 256, dtype_ab=F32, dtype_cd=F32,
+                        dist_a="uniform", dist_b="uniform", dist_c="zeros",
+                        alpha=1.0, beta=1.0, seed=seed)
+
+
+def config1_ones(n: int = 1024, dtype: str = F32) -> Problem:
+    """All-ones n x n x n with C = 1, alpha = beta = 1 (closed form D = K + 1)."""
+    return make_problem(n, n, n, dtype_ab=dtype, dtype_cd=dtype,
+                        dist_a="ones", dist_b="ones", dist_c="ones",
+                        alpha=1.0, beta=1.0)
+
+
+def config2(seed: int = 0, n: int = 1024) -> Problem:
+    """fp16 RowMajor n^3, A, B, C ~ N(0,1), alpha = beta = 1 (ReLU epilogue)."""
+    return make_problem(n, n, n, dtype_ab=F16, dtype_cd=F16,
+                        dist_c="normal", alpha=1.0, beta=1.0, seed=seed)
+
+
+GROUPED_NK = (128, 256, 512, 1024, 4096)
+
+
+def config3_shapes(seed: int = 0, count: int = 64) -> List[Tuple[int, int, int]]:
+    """M uniform in {32, ..., 2048} step 32; N, K uniform in GROUPED_NK."""
+    rng = np.random.default_rng(seed)
+    Ms = rng.integers(1, 65, size=count) * 32
+    Ns = rng.choice(GROUPED_NK, size=count)
+    Ks = rng.choice(GROUPED_NK, size=count)
+    return [(int(m), int(n), int(k)) for m, n, k in zip(Ms, Ns, Ks)]
+
+
+def config3(seed: int = 0, count: int = 64,
+            shapes: Optional[List[Tuple[int, int, int]]] = None) -> List[Problem]:
+    """Grouped fp16 RowMajor problems, entries ~ N(0,1), beta = 0."""
+    shapes = config3_shapes(seed, count) if shapes is None else shapes
+    rng = np.random.default_rng(seed + 1)
+    return [make_problem(m, n, k, dtype_ab=F16, dtype_cd=F16, rng=rng)
+            for (m, n, k) in shapes]
+
+
+# Transformer-layer bf16 GEMMs (hidden 8192, FFN 28672, 64 q / 8 kv heads of 128)
+LAYER_SHAPES = {
+    "qkv": (4096, 10240, 8192),
+    "o": (4096, 8192, 8192),
+    "gate_up": (4096, 57344, 8192),
+    "down": (4096, 8192, 28672),
+}
+
+
+def config4(name: str, seed: int = 0, lb: str = COL, scale: int = 1) -> Problem:
+    """bf16 A ~ N(0,1), weights ~ N(0, 0.02^2); B stored [N, K] (ColumnMajor)
+    by default, like nn.Linear weights. ``scale`` divides M (for quick runs)."""
+    M, N, K = LAYER_SHAPES[name]
+    return make_problem(M // scale, N, K, dtype_ab=BF16, dtype_cd=BF16,
+                        la=ROW, lb=lb, std_b=0.02, seed=seed)
+
+
+DECODE_MS = (16, 64, 128)
+DECODE_NK = ((8192, 28672), (57344, 8192))
+
+
+def config5(M: int, N: int, K: int, seed: int = 0) -> Problem:
+    """fp8 e4m3 A, B ~ N(0,1) quantized per tensor, bf16 D, beta = 0; B [N, K]."""
+    return make_problem(M, N, K, dtype_ab=F8, dtype_cd=BF16, la=ROW, lb=COL,
+                        seed=seed)

@@ -1,0 +1,391 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+None of these retypes the oracle's formula: the expected values come from
+format definitions checked against independent library decoders, closed
+forms (all-ones, identity, permutation), exact rational arithmetic on tiny
+integer inputs, numpy's float64 matmul, and invariants of the epilogue.
+"""
+import itertools
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import acceptance
+import synthetic as syn
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+LAYOUTS = ("row", "col")
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_decode_f16_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32)
+    got = oracle.decode("f16", bits)
+    want = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all()
+
+
+def test_decode_bf16_all_patterns():
+    # bfloat16 is by definition the upper 16 bits of an IEEE binary32
+    bits = np.arange(65536, dtype=np.uint32)
+    got = oracle.decode("bf16", bits)
+    with np.errstate(invalid="ignore"):
+        want = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all()
+
+
+def test_decode_e4m3_table():
+    bits = np.arange(256, dtype=np.uint32)
+    got = oracle.decode("f8e4m3", bits)
+    want = torch.from_numpy(bits.astype(np.uint8)).view(torch.float8_e4m3fn) \
+        .to(torch.float64).numpy()
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all()
+    fin = got[np.isfinite(got)]
+    assert fin.size == 254                      # only S.1111.111 is NaN
+    assert fin.max() == 448.0 and fin.min() == -448.0
+    assert np.min(fin[fin > 0]) == 2.0 ** -9    # smallest subnormal
+    assert not np.isinf(got).any()
+
+
+def test_decode_f32_random_patterns():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 2**32, size=20000, dtype=np.uint64).astype(np.uint32)
+    got = oracle.decode("f32", bits)
+    with np.errstate(invalid="ignore"):
+        want = bits.view(np.float32).astype(np.float64)
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all()
+
+
+# ---------------------------------------------------------------- encoder
+
+def _finite_table(dtype):
+    bits = np.arange(65536, dtype=np.uint32)
+    vals = oracle.decode(dtype, bits)
+    keep = np.isfinite(vals) & ~((vals == 0) & (bits >= 0x8000))  # drop -0
+    return vals[keep], bits[keep]
+
+
+def _brute_rne(dtype, x, table):
+    """Nearest finite value by exhaustive search; ties to even bit pattern."""
+    vals, bits = table
+    order = np.argsort(vals)
+    vals, bits = vals[order], bits[order]
+    out = []
+    for v in x:
+        if v > vals[-1] or v < vals[0]:
+            # beyond the largest finite: RNE overflows to infinity only past
+            # the halfway point to the next (unrepresentable) binade step
+            top = vals[-1]
+            step = top - vals[-2]
+            if abs(v) >= abs(top) + step / 2:
+                inf = {"f16": 0x7C00, "bf16": 0x7F80}[dtype]
+                out.append(np.uint32(inf | (0x8000 if v < 0 else 0)))
+                continue
+            out.append(bits[-1] if v > 0 else bits[0])
+            continue
+        i = np.searchsorted(vals, v)
+        cands = [j for j in (i - 1, i) if 0 <= j < len(vals)]
+        d = [abs(Fraction(float(vals[j])) - Fraction(float(v))) for j in cands]
+        m = min(d)
+        best = [cands[t] for t in range(len(cands)) if d[t] == m]
+        if len(best) > 1:
+            best = [j for j in best if bits[j] % 2 == 0]
+        b = bits[best[0]]
+        if v == 0 or (vals[best[0]] == 0 and np.signbit(v)):
+            b = np.uint32(0x8000) if np.signbit(v) else np.uint32(0)
+        out.append(b)
+    return np.array(out, dtype=np.uint32)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_encode_matches_exhaustive_nearest(dtype):
+    rng = np.random.default_rng(2)
+    table = _finite_table(dtype)
+    vals = table[0]
+    # random values, exact ties between neighbours, subnormals, overflow edge
+    x = list(rng.standard_normal(300) * np.exp2(rng.integers(-30, 30, 300)))
+    fin = np.sort(vals[vals > 0])
+    for t in rng.integers(0, fin.size - 1, 200):
+        x.append((fin[t] + fin[t + 1]) / 2)          # exact tie in fp64
+        x.append(-(fin[t] + fin[t + 1]) / 2)
+    x += [fin[0] / 2, fin[0] * 0.75, fin[-1] * 1.001, 1025.0, 1027.0, 1028.0]
+    x = np.array(x, dtype=np.float64)
+    got = oracle.encode(dtype, x)
+    want = _brute_rne(dtype, x, table)
+    assert (got == want).all(), np.where(got != want)
+
+
+def test_encode_f16_matches_numpy():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(50000) * np.exp2(rng.integers(-28, 18, 50000))
+    got = oracle.encode("f16", x)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16).astype(np.uint32)
+    assert (got == want).all()
+
+
+def test_encode_f32_matches_c_cast():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(50000) * np.exp2(rng.integers(-140, 120, 50000))
+    got = oracle.encode("f32", x)
+    want = x.astype(np.float32).view(np.uint32)
+    assert (got == want).all()
+
+
+def test_bf16_rounds_1025_to_1024():
+    # K + 1 = 1025 is a tie between 1024 and 1032 in bf16; even wins
+    assert oracle.decode("bf16", oracle.encode("bf16", [1025.0]))[0] == 1024.0
+
+
+# ---------------------------------------------------------------- GEMM pins
+
+def _read_golden(name):
+    kv = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    return kv
+
+
+def _golden_problem(kv):
+    M, N, K = int(kv["M"]), int(kv["N"]), int(kv["K"])
+    fill = lambda key, shape: np.full(shape, float(kv[key]), dtype=np.float32)
+    dt = kv["dtype"]
+    return syn.Problem(M, N, K, syn.cast(fill("fill_a", (M, K)), dt),
+                       syn.cast(fill("fill_b", (K, N)), dt),
+                       syn.cast(fill("fill_c", (M, N)), dt),
+                       float(kv["alpha"]), float(kv["beta"]), None, None,
+                       dt, dt, kv["layout"], kv["layout"], kv["layout"])
+
+
+@pytest.mark.parametrize("name,rows", [("ones_fp16_128.txt", None),
+                                       ("ones_fp16_1024.txt", [0, 517, 1023])])
+def test_golden_ones(name, rows):
+    kv = _read_golden(name)
+    p = _golden_problem(kv)
+    r = oracle.gemm(p, rows=rows)
+    assert (r.ref == float(kv["expect_all"])).all()
+    assert (r.d_exact == float(kv["expect_all"])).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_ones_closed_form_all_dtypes(dtype):
+    K = 256
+    p = syn.make_problem(64, 48, K, dtype_ab=dtype, dtype_cd=dtype,
+                         dist_a="ones", dist_b="ones", dist_c="ones", beta=1.0)
+    r = oracle.gemm(p)
+    assert (r.ref == K + 1).all()
+    assert (r.d_exact == oracle.decode(dtype, oracle.encode(dtype, [K + 1.0]))[0]).all()
+
+
+def _with_operand(p, which, logical, dtype):
+    layout = {"A": p.la, "B": p.lb, "C": p.lc}[which]
+    t = syn.cast(syn.to_storage(logical.astype(np.float32), layout), dtype)
+    setattr(p, which, t)
+    return p
+
+
+def _logical(p, which):
+    """Logical fp64 values of an operand, via torch's decoder (independent)."""
+    t = getattr(p, which).to(torch.float64).numpy()
+    layout = {"A": p.la, "B": p.lb, "C": p.lc}[which]
+    return t if layout == "row" else t.T
+
+
+@pytest.mark.parametrize("la,lb,lc", list(itertools.product(LAYOUTS, repeat=3)))
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_identity_and_permutation(la, lb, lc, dtype):
+    rng = np.random.default_rng(5)
+    M = K = 24
+    N = 17
+    p = syn.make_problem(M, N, K, dtype_ab=dtype, dtype_cd=dtype, la=la, lb=lb,
+                         lc=lc, dist_c="normal", alpha=1.0, beta=1.0, seed=6)
+    # A = I: D = B + C, each sum a single rounding of two exact values
+    _with_operand(p, "A", np.eye(M, dtype=np.float32), dtype)
+    r = oracle.gemm(p)
+    want = _logical(p, "B") + _logical(p, "C")
+    assert np.array_equal(r.ref, want)
+    # A = P (permutation), beta = 0: rows of B permuted, exactly
+    perm = rng.permutation(M)
+    P = np.zeros((M, K), dtype=np.float32)
+    P[np.arange(M), perm] = 1.0
+    _with_operand(p, "A", P, dtype)
+    p.beta = 0.0
+    r = oracle.gemm(p)
+    assert np.array_equal(r.ref, _logical(p, "B")[perm])
+    assert np.array_equal(r.d_exact, _logical(p, "B")[perm])
+
+
+def test_permutation_pin_catches_layout_mixup():
+    """A planted mistake (B read with the other layout) fails the pin."""
+    rng = np.random.default_rng(7)
+    M = K = N = 8
+    p = syn.make_problem(M, N, K, dtype_ab="f16", dtype_cd="f16", lb="row")
+    perm = rng.permutation(M)
+    P = np.zeros((M, K), dtype=np.float32)
+    P[np.arange(M), perm] = 1.0
+    _with_operand(p, "A", P, "f16")
+    good = oracle.gemm(p).ref
+    p.lb = "col"                                # the planted transposition
+    bad = oracle.gemm(p).ref
+    p.lb = "row"
+    want = _logical(p, "B")[perm]
+    assert np.array_equal(good, want) and not np.array_equal(bad, want)
+
+
+def _fraction_gemm(p, relu):
+    A = _logical(p, "A")
+    B = _logical(p, "B")
+    C = _logical(p, "C") if p.C is not None else None
+    al, be = Fraction(float(np.float32(p.alpha))), Fraction(float(np.float32(p.beta)))
+    sa = Fraction(float(np.float32(p.scale_a or 1.0)))
+    sb = Fraction(float(np.float32(p.scale_b or 1.0)))
+    out = []
+    for i in range(p.M):
+        row = []
+        for j in range(p.N):
+            acc = sum((Fraction(float(A[i, k])) * Fraction(float(B[k, j]))
+                       for k in range(p.K)), Fraction(0))
+            v = al * acc * sa * sb
+            if be != 0:
+                v += be * Fraction(float(C[i, j]))
+            if relu and v <= 0:
+                v = Fraction(0)
+            row.append(v)
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("dtype_ab,dtype_cd", [("f32", "f32"), ("f16", "f16"),
+                                               ("bf16", "bf16"), ("f8e4m3", "bf16")])
+@pytest.mark.parametrize("relu", [False, True])
+def test_brute_force_fraction_tiny(dtype_ab, dtype_cd, relu):
+    rng = np.random.default_rng(8)
+    for trial in range(6):
+        M, N, K = (int(v) for v in rng.integers(1, 7, 3))
+        la, lb, lc = (LAYOUTS[int(v)] for v in rng.integers(0, 2, 3))
+        p = syn.integer_problem(M, N, K, dtype_ab=dtype_ab, dtype_cd=dtype_cd,
+                                la=la, lb=lb, lc=lc, lo=-5, hi=5,
+                                alpha=float(rng.choice([1.0, 0.75, -1.5])),
+                                beta=float(rng.choice([0.0, 1.0, -0.5])),
+                                seed=100 + trial)
+        if dtype_ab == "f8e4m3":
+            p.scale_a, p.scale_b = 0.5, 4.0
+        r = oracle.gemm(p, relu=relu)
+        exact = _fraction_gemm(p, relu)
+        for i in range(M):
+            for j in range(N):
+                assert Fraction(float(r.ref[i, j])) == exact[i][j]
+        want_bits = oracle.encode(dtype_cd, [[float(v) for v in row] for row in exact])
+        assert np.array_equal(r.d_bits, want_bits)
+
+
+@pytest.mark.parametrize("dtype_ab,dtype_cd", [("f32", "f32"), ("f16", "f16"),
+                                               ("bf16", "bf16"), ("f8e4m3", "bf16")])
+def test_matches_numpy_float64_matmul(dtype_ab, dtype_cd):
+    for (M, N, K, la, lb, lc) in [(33, 65, 130, "row", "row", "row"),
+                                  (64, 31, 257, "col", "col", "col"),
+                                  (50, 70, 96, "row", "col", "col")]:
+        p = syn.make_problem(M, N, K, dtype_ab=dtype_ab, dtype_cd=dtype_cd,
+                             la=la, lb=lb, lc=lc, dist_c="normal",
+                             alpha=0.5, beta=-2.0, seed=9)
+        r = oracle.gemm(p)
+        A, B, C = _logical(p, "A"), _logical(p, "B"), _logical(p, "C")
+        sab = (p.scale_a or 1.0) * (p.scale_b or 1.0)
+        want = 0.5 * (A @ B) * sab - 2.0 * C
+        S = 0.5 * sab * (np.abs(A) @ np.abs(B))
+        assert np.all(np.abs(r.ref - want) <= 4 * K * 2.0 ** -52 * (S + 2 * np.abs(C)))
+        assert np.allclose(r.S, S, rtol=1e-12, atol=0)
+
+
+def test_relu_invariant_and_fused_equals_unfused():
+    p = syn.make_problem(40, 52, 77, dtype_ab="f16", dtype_cd="f16",
+                         dist_c="normal", alpha=1.0, beta=1.0, seed=10)
+    lin = oracle.gemm(p, relu=False)
+    fused = oracle.gemm(p, relu=True)
+    assert (fused.ref >= 0).all()
+    assert np.array_equal(fused.ref, np.maximum(lin.ref, 0.0))
+    assert np.array_equal(fused.d_exact, np.maximum(lin.d_exact, 0.0))
+    assert (fused.ref == 0).sum() > 0 and (fused.ref > 0).sum() > 0
+
+
+def test_alpha_power_of_two_doubles_exactly():
+    p = syn.make_problem(20, 30, 40, dtype_ab="bf16", dtype_cd="bf16", seed=11)
+    r1 = oracle.gemm(p)
+    p.alpha = 2.0
+    r2 = oracle.gemm(p)
+    assert np.array_equal(r2.ref, 2 * r1.ref)
+    assert np.array_equal(r2.d_exact, 2 * r1.d_exact)
+
+
+def test_beta_zero_ignores_c():
+    p = syn.make_problem(8, 9, 10, dtype_ab="f16", dtype_cd="f16", dist_c="normal",
+                         beta=0.0, seed=12)
+    r1 = oracle.gemm(p)
+    p.C = torch.full_like(p.C, float("nan"))
+    r2 = oracle.gemm(p)
+    assert np.array_equal(r1.ref, r2.ref) and np.isfinite(r2.ref).all()
+
+
+def test_fp8_scales_multiply_exactly():
+    p = syn.integer_problem(16, 24, 32, dtype_ab="f8e4m3", dtype_cd="bf16",
+                            with_c=False, seed=13)
+    r1 = oracle.gemm(p)
+    p.scale_a, p.scale_b = 0.25, 8.0
+    r2 = oracle.gemm(p)
+    assert np.array_equal(r2.ref, 2.0 * r1.ref)
+
+
+def test_entries_equal_rows():
+    p = syn.make_problem(30, 40, 50, dtype_ab="bf16", dtype_cd="bf16", la="col",
+                         lb="row", lc="col", dist_c="normal", beta=0.5, seed=14)
+    rows = oracle.gemm(p, relu=True)
+    rng = np.random.default_rng(15)
+    ii, jj = rng.integers(0, 30, 100), rng.integers(0, 40, 100)
+    ent = oracle.gemm_entries(p, ii, jj, relu=True)
+    assert np.array_equal(ent.ref, rows.ref[ii, jj])
+    assert np.array_equal(ent.d_bits, rows.d_bits[ii, jj])
+
+
+def test_grouped_equals_loop_of_singles():
+    probs = syn.config3(seed=3, count=4,
+                        shapes=[(32, 128, 128), (64, 256, 128), (96, 128, 256),
+                                (32, 512, 128)])
+    g = oracle.grouped(probs)
+    for p, r in zip(probs, g):
+        s = oracle.gemm(p)
+        assert np.array_equal(r.ref, s.ref) and np.array_equal(r.d_bits, s.d_bits)
+
+
+def test_degenerate_sizes():
+    p = syn.make_problem(5, 6, 0, dtype_ab="f16", dtype_cd="f16", dist_c="normal",
+                         beta=2.0, seed=16)
+    r = oracle.gemm(p, relu=True)           # K = 0: D = relu(beta * C)
+    assert np.array_equal(r.ref, np.maximum(2.0 * _logical(p, "C"), 0))
+    p0 = syn.make_problem(0, 6, 3, dtype_ab="f16", dtype_cd="f16")
+    assert oracle.gemm(p0).ref.shape == (0, 6)
+
+
+def test_acceptance_rules():
+    # ulp: one unit in the last place of the output format
+    assert acceptance.ulp("f16", 1025.0) == 1.0
+    assert acceptance.ulp("bf16", 1.0) == 2.0 ** -7
+    assert acceptance.ulp("f32", 0.0) == 2.0 ** -149
+    assert acceptance.ulp("f16", 2.0 ** -20) == 2.0 ** -24      # subnormal quantum
+    tol = acceptance.tolerance("f16", "f16", np.array([1.0]), np.array([10.0]))
+    assert tol[0] == 2 * 2.0 ** -10 + 2e-3 * 10
+    with pytest.raises(AssertionError):
+        acceptance.check_close([1.1], [1.0], [1.0], "f16", "f16")
+    acceptance.check_exact([0.0, 1.0], [-0.0, 1.0])
