@@ -1,0 +1,303 @@
+"""Python binding of the gfx950 GEMM library (``libmi355_gemm.so``).
+
+Argument marshalling only: every step of D = epi(alpha*A*B + beta*C) runs in
+the library's HIP kernels. The functions keep the C ABI's names
+(``gemm_plan_create``, ``gemm_plan_run``, ``gemm_plan_run_scaled``,
+``grouped_gemm_run``, ...); ``Plan`` and ``gemm``/``grouped_gemm`` are small
+conveniences that take torch tensors, check their sizes against M, N, K on the
+host (so no kernel is launched on a buffer that is too small), and pass their
+device pointers and torch's current HIP stream.
+
+There is no fallback: if the shared library is missing, importing this module
+raises with the command that builds it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from enum import IntEnum
+from typing import Iterable, List, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmi355_gemm.so")
+
+
+class Dtype(IntEnum):
+    F32 = 0
+    F16 = 1
+    BF16 = 2
+    F8_E4M3 = 3
+
+
+class Layout(IntEnum):
+    ROW_MAJOR = 0
+    COL_MAJOR = 1
+
+
+class Epilogue(IntEnum):
+    LINEAR = 0
+    RELU = 1
+
+
+class Status(IntEnum):
+    OK = 0
+    INVALID_ARG = 1
+    UNSUPPORTED = 2
+    HIP_ERROR = 3
+    OUT_OF_MEMORY = 4
+    NOT_INITIALIZED = 5
+
+
+class Schedule(IntEnum):
+    AUTO = 0
+    DATA_PARALLEL = 1
+    STREAM_K = 2
+    HYBRID = 3
+
+
+class Tile(IntEnum):
+    AUTO = 0
+    T256x256 = 1
+    T128x128 = 2
+    T64x256 = 3
+    T32x256 = 4
+    GENERIC = 5
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{Status(status).name}: {message}")
+        self.status = Status(status)
+
+
+class gemm_problem(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("D", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python dense_gemm_epilogue_02_amd/build.py` (needs hipcc for gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, f32, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+    st = ctypes.c_int
+    L.gemm_plan_create.restype = st
+    L.gemm_plan_create.argtypes = [ctypes.POINTER(vp)] + [ctypes.c_int] * 9
+    L.gemm_plan_create_simple.restype = st
+    L.gemm_plan_create_simple.argtypes = [ctypes.POINTER(vp)] + [ctypes.c_int] * 3
+    L.gemm_plan_destroy.restype = st
+    L.gemm_plan_destroy.argtypes = [vp]
+    L.gemm_plan_set_config.restype = st
+    L.gemm_plan_set_config.argtypes = [vp, ctypes.c_int, ctypes.c_int, i32]
+    L.gemm_plan_run.restype = st
+    L.gemm_plan_run.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp]
+    L.gemm_plan_run_scaled.restype = st
+    L.gemm_plan_run_scaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp, vp, vp]
+    L.grouped_gemm_run.restype = st
+    L.grouped_gemm_run.argtypes = [vp, ctypes.POINTER(gemm_problem), i32, f32, f32, vp]
+    L.gemm_plan_describe.restype = st
+    L.gemm_plan_describe.argtypes = [vp, i64, i64, i64, i32, ctypes.c_char_p, i32]
+    L.gemm_last_error.restype = ctypes.c_char_p
+    L.gemm_last_error.argtypes = []
+    L.gemm_status_string.restype = ctypes.c_char_p
+    L.gemm_status_string.argtypes = [ctypes.c_int]
+    L.gemm_supported_count.restype = i32
+    L.gemm_supported_count.argtypes = []
+    L.gemm_supported_get.restype = st
+    L.gemm_supported_get.argtypes = [i32] + [ctypes.POINTER(ctypes.c_int)] * 5
+    L.gemm_version.restype = ctypes.c_char_p
+    L.gemm_version.argtypes = []
+    return L
+
+
+lib = _load()
+
+EXPORTED = ("gemm_plan_create", "gemm_plan_create_simple", "gemm_plan_destroy",
+            "gemm_plan_set_config", "gemm_plan_run", "gemm_plan_run_scaled",
+            "grouped_gemm_run", "gemm_plan_describe", "gemm_last_error",
+            "gemm_status_string", "gemm_supported_count", "gemm_supported_get",
+            "gemm_version")
+
+
+def _check(status: int):
+    if status != 0:
+        raise GemmError(status, lib.gemm_last_error().decode())
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---- same-name wrappers of the C ABI ----------------------------------------
+
+def gemm_plan_create(element_a, element_b, element_c, element_d, element_acc,
+                     layout_a, layout_b, layout_c, epilogue) -> int:
+    h = ctypes.c_void_p()
+    _check(lib.gemm_plan_create(ctypes.byref(h), int(element_a), int(element_b),
+                                int(element_c), int(element_d), int(element_acc),
+                                int(layout_a), int(layout_b), int(layout_c), int(epilogue)))
+    return h.value
+
+
+def gemm_plan_create_simple(element, layout, epilogue) -> int:
+    h = ctypes.c_void_p()
+    _check(lib.gemm_plan_create_simple(ctypes.byref(h), int(element), int(layout), int(epilogue)))
+    return h.value
+
+
+def gemm_plan_destroy(plan: int) -> None:
+    _check(lib.gemm_plan_destroy(plan))
+
+
+def gemm_plan_set_config(plan: int, schedule=Schedule.AUTO, tile=Tile.AUTO, sk_grid: int = 0):
+    _check(lib.gemm_plan_set_config(plan, int(schedule), int(tile), int(sk_grid)))
+
+
+def gemm_plan_run(plan: int, A, B, C, D, M: int, N: int, K: int, alpha: float = 1.0,
+                  beta: float = 0.0, stream=None) -> None:
+    _check(lib.gemm_plan_run(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), M, N, K, alpha, beta,
+                             _stream(stream)))
+
+
+def gemm_plan_run_scaled(plan: int, A, B, C, D, M: int, N: int, K: int, alpha: float,
+                         beta: float, scale_a, scale_b, stream=None) -> None:
+    _check(lib.gemm_plan_run_scaled(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), M, N, K, alpha,
+                                    beta, _ptr(scale_a), _ptr(scale_b), _stream(stream)))
+
+
+def grouped_gemm_run(plan: int, problems: Sequence[tuple], alpha: float = 1.0,
+                     beta: float = 0.0, stream=None) -> None:
+    """problems: sequence of (M, N, K, A, B, C, D) with tensors or raw pointers."""
+    arr = (gemm_problem * max(1, len(problems)))()
+    for i, (M, N, K, A, B, C, D) in enumerate(problems):
+        arr[i] = gemm_problem(M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(D))
+    _check(lib.grouped_gemm_run(plan, arr, len(problems), alpha, beta, _stream(stream)))
+
+
+def gemm_plan_describe(plan: int, M: int, N: int, K: int, num_cus: int = 0) -> dict:
+    import json
+    buf = ctypes.create_string_buffer(512)
+    _check(lib.gemm_plan_describe(plan, M, N, K, num_cus, buf, len(buf)))
+    return json.loads(buf.value.decode())
+
+
+def gemm_last_error() -> str:
+    return lib.gemm_last_error().decode()
+
+
+def gemm_status_string(status: int) -> str:
+    return lib.gemm_status_string(int(status)).decode()
+
+
+def gemm_supported_count() -> int:
+    return lib.gemm_supported_count()
+
+
+def gemm_supported_get(i: int):
+    v = [ctypes.c_int() for _ in range(5)]
+    _check(lib.gemm_supported_get(i, *[ctypes.byref(x) for x in v]))
+    return tuple(Dtype(x.value) for x in v)
+
+
+def gemm_version() -> str:
+    return lib.gemm_version().decode()
+
+
+# ---- tensor conveniences ------------------------------------------------------
+
+_TORCH_DT = {"f32": Dtype.F32, "f16": Dtype.F16, "bf16": Dtype.BF16, "f8e4m3": Dtype.F8_E4M3}
+_LAYOUT = {"row": Layout.ROW_MAJOR, "col": Layout.COL_MAJOR}
+
+
+def _dtype_of(t) -> Dtype:
+    import torch
+    m = {torch.float32: Dtype.F32, torch.float16: Dtype.F16, torch.bfloat16: Dtype.BF16,
+         torch.float8_e4m3fn: Dtype.F8_E4M3}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _need(t, n: int, name: str, dtype: Dtype):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (packed storage)")
+    if _dtype_of(t) != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, plan expects {dtype.name}")
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {n}")
+
+
+class Plan:
+    """A plan bound to element types, layouts and epilogue (reusable across shapes)."""
+
+    def __init__(self, dtype_ab="bf16", dtype_cd=None, la="row", lb="row", lc="row",
+                 relu: bool = False):
+        dtype_cd = dtype_cd or ("bf16" if dtype_ab == "f8e4m3" else dtype_ab)
+        self.dab, self.dcd = _TORCH_DT[dtype_ab], _TORCH_DT[dtype_cd]
+        self.handle = gemm_plan_create(self.dab, self.dab, self.dcd, self.dcd, Dtype.F32,
+                                       _LAYOUT[la], _LAYOUT[lb], _LAYOUT[lc],
+                                       Epilogue.RELU if relu else Epilogue.LINEAR)
+
+    def close(self):
+        if self.handle:
+            gemm_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_config(self, schedule=Schedule.AUTO, tile=Tile.AUTO, sk_grid: int = 0):
+        gemm_plan_set_config(self.handle, schedule, tile, sk_grid)
+        return self
+
+    def describe(self, M, N, K, num_cus=0) -> dict:
+        return gemm_plan_describe(self.handle, M, N, K, num_cus)
+
+    def check(self, A, B, C, D, M, N, K, beta):
+        if min(M, N, K) < 0:
+            return   # the library reports negative sizes itself
+        if M and N:
+            _need(D, M * N, "D", self.dcd)
+            if K:
+                _need(A, M * K, "A", self.dab)
+                _need(B, K * N, "B", self.dab)
+            if beta != 0.0:
+                _need(C, M * N, "C", self.dcd)
+
+    def run(self, A, B, C, D, M, N, K, alpha=1.0, beta=0.0, scale_a=None, scale_b=None,
+            stream=None):
+        self.check(A, B, C, D, M, N, K, beta)
+        if scale_a is None and scale_b is None:
+            gemm_plan_run(self.handle, A, B, C, D, M, N, K, alpha, beta, stream)
+        else:
+            gemm_plan_run_scaled(self.handle, A, B, C, D, M, N, K, alpha, beta, scale_a,
+                                 scale_b, stream)
+
+    def run_grouped(self, problems: Iterable[tuple], alpha=1.0, beta=0.0, stream=None):
+        probs = list(problems)
+        for (M, N, K, A, B, C, D) in probs:
+            self.check(A, B, C, D, M, N, K, beta)
+        grouped_gemm_run(self.handle, probs, alpha, beta, stream)

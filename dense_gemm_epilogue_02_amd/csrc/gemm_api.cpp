@@ -1,0 +1,751 @@
+// gemm_api.cpp -- the C ABI declared in include/gemm.h
+//
+// Host side of the library: plan creation and validation (no device calls),
+// kernel selection from the compiled registry keyed by (element family,
+// operand layouts, tile shape, alignment class) -- the role the pages give to
+// "KernelsForDataType" and default_operation() ("CUTLASS Python 接口全解析"
+// section 3.2) -- the data-parallel / stream-K / hybrid schedule, the
+// plan-owned device workspace, and the launches. Errors are reported as
+// status codes plus a descriptive thread-local message ("Python packages
+// associated with CUTLASS", Overview: descriptive run-time errors).
+#include "gemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "kernels.hpp"
+
+using namespace mg;
+
+namespace {
+
+thread_local std::string g_err;
+
+gemm_status fail(gemm_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+gemm_status ok() {
+    g_err.clear();
+    return GEMM_OK;
+}
+
+gemm_status hip_fail(hipError_t e, const char *what) {
+    return fail(GEMM_HIP_ERROR, "%s failed: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+const char *dtype_name(int d) {
+    switch (d) {
+    case GEMM_F32: return "F32";
+    case GEMM_F16: return "F16";
+    case GEMM_BF16: return "BF16";
+    case GEMM_F8_E4M3: return "F8_E4M3";
+    }
+    return "?";
+}
+
+struct Tuple {
+    gemm_dtype a, b, c, d, acc;
+    int fam;
+};
+const Tuple kSupported[] = {
+    {GEMM_F32, GEMM_F32, GEMM_F32, GEMM_F32, GEMM_F32, FAM_F32},
+    {GEMM_F16, GEMM_F16, GEMM_F16, GEMM_F16, GEMM_F32, FAM_F16},
+    {GEMM_BF16, GEMM_BF16, GEMM_BF16, GEMM_BF16, GEMM_F32, FAM_BF16},
+    {GEMM_F8_E4M3, GEMM_F8_E4M3, GEMM_BF16, GEMM_BF16, GEMM_F32, FAM_F8},
+};
+constexpr int kNumSupported = (int)(sizeof(kSupported) / sizeof(kSupported[0]));
+
+int elem_bytes(int fam) { return fam == FAM_F32 ? 4 : fam == FAM_F8 ? 1 : 2; }
+int out_bytes(int fam) { return fam == FAM_F32 ? 4 : 2; }
+
+// ------------------------------------------------------------------ registry
+
+struct Registry {
+    std::vector<KernelEntry> all;
+    Registry() {
+        const KernelEntry *(*tables[])(int *) = {entries_f32, entries_f16, entries_bf16, entries_f8};
+        for (auto t : tables) {
+            int n = 0;
+            const KernelEntry *e = t(&n);
+            all.insert(all.end(), e, e + n);
+        }
+    }
+    const KernelEntry *find(int fam, bool a_kc, bool b_kc, int tile) const {
+        for (const auto &e : all)
+            if (e.fam == fam && e.a_kc == (int)a_kc && e.b_kc == (int)b_kc && e.tile == tile) return &e;
+        return nullptr;
+    }
+};
+
+const Registry &registry() {
+    static Registry r;
+    return r;
+}
+
+// Per-device facts, and occupancy per kernel (queried once).
+struct DeviceInfo {
+    int num_cus = 0;
+    std::unordered_map<const void *, int> occ;
+};
+std::mutex g_dev_mu;
+std::unordered_map<int, DeviceInfo> g_dev;
+
+gemm_status device_cus(int dev, int *cus) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DeviceInfo &di = g_dev[dev];
+    if (di.num_cus == 0) {
+        int v = 0;
+        hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+        di.num_cus = v > 0 ? v : 1;
+    }
+    *cus = di.num_cus;
+    return GEMM_OK;
+}
+
+gemm_status kernel_occupancy(int dev, const void *fn, int nt, int *occ) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DeviceInfo &di = g_dev[dev];
+    auto it = di.occ.find(fn);
+    if (it == di.occ.end()) {
+        int v = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, nt, 0);
+        if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+        it = di.occ.emplace(fn, v > 0 ? v : 1).first;
+    }
+    *occ = it->second;
+    return GEMM_OK;
+}
+
+int static_occupancy(const KernelEntry *e) {
+    int occ = (160 * 1024) / e->lds_bytes;
+    const int by_waves = 32 / (e->nt / 64);   // 8 waves per SIMD x 4 SIMDs
+    if (occ > by_waves) occ = by_waves;
+    return occ > 0 ? occ : 1;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ plan
+
+struct gemm_plan_s {
+    uint32_t magic;
+    gemm_dtype a, b, c, d, acc;
+    gemm_layout la, lb, lc;
+    gemm_epilogue epi;
+    int fam;
+    gemm_schedule sched;
+    gemm_tile tile;
+    int sk_grid;
+    int device;
+    float *partials;
+    size_t partial_bytes;
+    int *counters;
+    size_t counter_count;
+    GroupDesc *gdesc;
+    size_t gdesc_cap;
+    GroupDesc *ghost;
+    hipEvent_t gevent;
+    bool gevent_pending;
+    hipStream_t last_stream;
+    bool used;
+};
+
+namespace {
+
+constexpr uint32_t kMagic = 0x6D473535u;
+
+bool plan_ok(gemm_plan_t p) { return p && p->magic == kMagic; }
+
+// What a run of (M, N, K) will launch.
+struct Decision {
+    const KernelEntry *e = nullptr;   // null: scalar-load kernel
+    gemm_schedule sched = GEMM_SCHED_DATA_PARALLEL;
+    int tiles_m = 0, tiles_n = 0, ipt = 0, total = 0, grid = 0, sk_tiles = 0;
+    int64_t sk_iters = 0;
+    int group_m = 4;
+    int vec_cd = 0;
+    const char *why_generic = "";
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Vector (16-byte buffer-load) eligibility of one operand for a tile kernel.
+const char *operand_vec_problem(const void *ptr, bool kc, int64_t contig, int64_t rows, int esz) {
+    const int vec = 16 / esz;
+    if (reinterpret_cast<uintptr_t>(ptr) % 16) return "operand base not 16-byte aligned";
+    if (contig % vec) return "contiguous extent not a multiple of 16 bytes";
+    // largest in-tile byte offset must stay below the 31-bit buffer range
+    const int64_t span = kc ? rows * contig * esz : (int64_t)KTILE_BYTES * contig;
+    if (span + 16 > 0x7FFFFFFFLL) return "operand row stride too large for 32-bit offsets";
+    (void)rows;
+    return nullptr;
+}
+
+gemm_tile pick_tile(int fam, int64_t M, int64_t N, int cus) {
+    if (fam == FAM_F32) return GEMM_TILE_128x128;
+    if (M <= 32) return GEMM_TILE_32x256;
+    if (M <= 64) return GEMM_TILE_64x256;
+    const int64_t big = cdiv(M, 256) * cdiv(N, 256);
+    return big >= cus ? GEMM_TILE_256x256 : GEMM_TILE_128x128;
+}
+
+int tile_id(gemm_tile t) {
+    switch (t) {
+    case GEMM_TILE_256x256: return TILE_256x256;
+    case GEMM_TILE_128x128: return TILE_128x128;
+    case GEMM_TILE_64x256: return TILE_64x256;
+    case GEMM_TILE_32x256: return TILE_32x256;
+    default: return 0;
+    }
+}
+
+const char *tile_name(const KernelEntry *e) {
+    if (!e) return "generic64x64";
+    switch (e->tile) {
+    case TILE_256x256: return "256x256";
+    case TILE_128x128: return "128x128";
+    case TILE_64x256: return "64x256";
+    case TILE_32x256: return "32x256";
+    }
+    return "?";
+}
+
+const char *sched_name(gemm_schedule s) {
+    switch (s) {
+    case GEMM_SCHED_DATA_PARALLEL: return "data_parallel";
+    case GEMM_SCHED_STREAM_K: return "stream_k";
+    case GEMM_SCHED_HYBRID: return "hybrid";
+    default: return "auto";
+    }
+}
+
+// `occ_of` gives workgroups per CU for an entry (live query or estimate).
+template <class OccFn>
+gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const void *C, const void *D,
+                   int64_t M, int64_t N, int64_t K, float beta, int cus, OccFn occ_of, Decision &d) {
+    const int fam = pl->fam;
+    const int esz = elem_bytes(fam), osz = out_bytes(fam);
+    const bool a_kc = pl->la == GEMM_ROW_MAJOR, b_kc = pl->lb == GEMM_COL_MAJOR;
+    d.vec_cd = (pl->lc == GEMM_ROW_MAJOR && N % 4 == 0 &&
+                reinterpret_cast<uintptr_t>(D) % (4 * osz) == 0 &&
+                (beta == 0.0f || reinterpret_cast<uintptr_t>(C) % (4 * osz) == 0))
+                   ? 1 : 0;
+    if (pl->tile != GEMM_TILE_GENERIC) {
+        gemm_tile t = pl->tile == GEMM_TILE_AUTO ? pick_tile(fam, M, N, cus) : pl->tile;
+        const KernelEntry *e = registry().find(fam, a_kc, b_kc, tile_id(t));
+        if (!e) e = registry().find(fam, a_kc, b_kc, TILE_128x128);
+        const char *why = nullptr;
+        if (K > 0) {
+            why = operand_vec_problem(A, a_kc, a_kc ? K : M, e ? e->bm : 0, esz);
+            if (!why) why = operand_vec_problem(B, b_kc, b_kc ? K : N, e ? e->bn : 0, esz);
+        }
+        if (e && !why) d.e = e;
+        else d.why_generic = why ? why : "no tile kernel for this layout";
+    } else {
+        d.why_generic = "scalar-load kernel requested";
+    }
+    if (!d.e) {
+        d.sched = GEMM_SCHED_DATA_PARALLEL;
+        d.tiles_m = (int)cdiv(M, 64);
+        d.tiles_n = (int)cdiv(N, 64);
+        d.total = d.tiles_m * d.tiles_n;
+        d.grid = d.total;
+        return GEMM_OK;
+    }
+    const KernelEntry *e = d.e;
+    const int64_t tm = cdiv(M, e->bm), tn = cdiv(N, e->bn), ipt = cdiv(K, e->bk);
+    if (tm * tn > 0x7FFFFFFFLL || ipt > 0x7FFFFFFFLL || tm * tn * ipt > (1LL << 52))
+        return fail(GEMM_UNSUPPORTED, "problem %lldx%lldx%lld has too many tiles", (long long)M,
+                    (long long)N, (long long)K);
+    d.tiles_m = (int)tm;
+    d.tiles_n = (int)tn;
+    d.ipt = (int)ipt;
+    d.total = (int)(tm * tn);
+    int occ = 1;
+    gemm_status st = occ_of(e, &occ);
+    if (st != GEMM_OK) return st;
+    int G = cus * occ;
+    if (pl->sk_grid > 0 && pl->sk_grid < G) G = pl->sk_grid;
+    gemm_schedule s = pl->sched;
+    if (d.ipt == 0) s = GEMM_SCHED_DATA_PARALLEL;
+    if (s == GEMM_SCHED_AUTO) {
+        if (d.total >= G) {
+            const int rem = d.total % G;
+            const double eff = (double)d.total / (double)(cdiv(d.total, G) * G);
+            s = (rem == 0 || eff >= 0.9 || d.ipt < 4) ? GEMM_SCHED_DATA_PARALLEL : GEMM_SCHED_HYBRID;
+        } else {
+            s = d.ipt >= 4 ? GEMM_SCHED_STREAM_K : GEMM_SCHED_DATA_PARALLEL;
+        }
+    }
+    if (s == GEMM_SCHED_HYBRID && (d.total < G || d.total % G == 0))
+        s = d.total < G ? GEMM_SCHED_STREAM_K : GEMM_SCHED_DATA_PARALLEL;
+    d.sched = s;
+    switch (s) {
+    case GEMM_SCHED_DATA_PARALLEL:
+        d.sk_tiles = 0;
+        d.grid = d.total < G ? d.total : G;
+        break;
+    case GEMM_SCHED_STREAM_K: {
+        d.sk_tiles = d.total;
+        d.sk_iters = (int64_t)d.total * d.ipt;
+        const int64_t g = d.sk_iters < G ? d.sk_iters : G;
+        d.grid = (int)(g > 0 ? g : 1);
+        break;
+    }
+    default:   // hybrid: whole waves data-parallel, the remainder stream-K
+        d.sk_tiles = d.total % G;
+        d.sk_iters = (int64_t)d.sk_tiles * d.ipt;
+        d.grid = G;
+        break;
+    }
+    return GEMM_OK;
+}
+
+gemm_status check_device(gemm_plan_s *pl, int *dev) {
+    hipError_t e = hipGetDevice(dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (pl->device >= 0 && pl->device != *dev)
+        return fail(GEMM_UNSUPPORTED, "plan is bound to device %d (first run) but device %d is current",
+                    pl->device, *dev);
+    pl->device = *dev;
+    return GEMM_OK;
+}
+
+void note_stream(gemm_plan_s *pl, hipStream_t s) {
+    pl->last_stream = s;
+    pl->used = true;
+}
+
+// Make sure the stream-K workspace covers `slots` partial tiles and `ctr`
+// counters; new counters are zeroed on `st` before any kernel that uses them.
+gemm_status ensure_workspace(gemm_plan_s *pl, size_t partial_bytes, size_t ctr, hipStream_t st) {
+    if (partial_bytes <= pl->partial_bytes && ctr <= pl->counter_count) return GEMM_OK;
+    if (pl->used) {
+        hipError_t e = hipStreamSynchronize(pl->last_stream);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize (workspace growth)");
+    }
+    if (partial_bytes > pl->partial_bytes) {
+        if (pl->partials) (void)hipFree(pl->partials);
+        pl->partials = nullptr;
+        pl->partial_bytes = 0;
+        hipError_t e = hipMalloc(reinterpret_cast<void **>(&pl->partials), partial_bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(GEMM_OUT_OF_MEMORY, "stream-K workspace of %zu bytes: %s", partial_bytes,
+                        hipGetErrorString(e));
+        }
+        pl->partial_bytes = partial_bytes;
+    }
+    if (ctr > pl->counter_count) {
+        if (pl->counters) (void)hipFree(pl->counters);
+        pl->counters = nullptr;
+        pl->counter_count = 0;
+        const size_t n = ctr < 1024 ? 1024 : ctr;
+        hipError_t e = hipMalloc(reinterpret_cast<void **>(&pl->counters), n * sizeof(int));
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(GEMM_OUT_OF_MEMORY, "stream-K counters: %s", hipGetErrorString(e));
+        }
+        e = launch_zero_u32(reinterpret_cast<uint32_t *>(pl->counters), n, st);
+        if (e != hipSuccess) return hip_fail(e, "counter initialisation");
+        pl->counter_count = n;
+    }
+    return GEMM_OK;
+}
+
+gemm_status validate_problem(const gemm_plan_s *pl, const void *A, const void *B, const void *C,
+                             const void *D, int64_t M, int64_t N, int64_t K, float beta,
+                             const char *where) {
+    (void)pl;
+    if (M < 0 || N < 0 || K < 0)
+        return fail(GEMM_INVALID_ARG, "%s: negative size M=%lld N=%lld K=%lld", where, (long long)M,
+                    (long long)N, (long long)K);
+    if (M == 0 || N == 0) return GEMM_OK;
+    if (!D) return fail(GEMM_INVALID_ARG, "%s: D is NULL", where);
+    if (K > 0 && (!A || !B)) return fail(GEMM_INVALID_ARG, "%s: A or B is NULL with K > 0", where);
+    if (beta != 0.0f && !C) return fail(GEMM_INVALID_ARG, "%s: C is NULL but beta != 0", where);
+    if (M > (1LL << 40) || N > (1LL << 40) || K > (1LL << 40))
+        return fail(GEMM_UNSUPPORTED, "%s: dimension beyond 2^40", where);
+    return GEMM_OK;
+}
+
+Prob make_prob(const void *A, const void *B, const void *C, void *D, int64_t M, int64_t N, int64_t K,
+               const Decision &d) {
+    Prob p;
+    p.A = static_cast<const char *>(A);
+    p.B = static_cast<const char *>(B);
+    p.C = static_cast<const char *>(C);
+    p.D = static_cast<char *>(D);
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.tiles_m = d.tiles_m;
+    p.tiles_n = d.tiles_n;
+    p.ipt = d.ipt;
+    p.vec_cd = d.vec_cd;
+    return p;
+}
+
+EpiArgs make_epi(const gemm_plan_s *pl, float alpha, float beta, const float *sa, const float *sb) {
+    EpiArgs e;
+    e.alpha = alpha;
+    e.beta = beta;
+    e.scale_a = sa;
+    e.scale_b = sb;
+    e.relu = pl->epi == GEMM_EPI_RELU ? 1 : 0;
+    e.lc_row = pl->lc == GEMM_ROW_MAJOR ? 1 : 0;
+    return e;
+}
+
+gemm_status run_generic(const gemm_plan_s *pl, const Prob &p, const EpiArgs &ep, hipStream_t st) {
+    GenericArgs g;
+    g.p = p;
+    g.e = ep;
+    g.la_row = pl->la == GEMM_ROW_MAJOR;
+    g.lb_row = pl->lb == GEMM_ROW_MAJOR;
+    hipError_t e = launch_generic(pl->fam, g, st);
+    if (e != hipSuccess) return hip_fail(e, "generic kernel launch");
+    return GEMM_OK;
+}
+
+gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C, void *D, int64_t M,
+                    int64_t N, int64_t K, float alpha, float beta, const float *sa, const float *sb,
+                    void *stream) {
+    if (!plan_ok(pl)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_run: invalid plan handle");
+    gemm_status st = validate_problem(pl, A, B, C, D, M, N, K, beta, "gemm_plan_run");
+    if (st != GEMM_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    if (beta == 0.0f) C = nullptr;
+    int dev = 0;
+    if ((st = check_device(pl, &dev)) != GEMM_OK) return st;
+    int cus = 0;
+    if ((st = device_cus(dev, &cus)) != GEMM_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    Decision d;
+    st = decide(pl, A, B, C, D, M, N, K, beta, cus,
+                [&](const KernelEntry *e, int *occ) {
+                    return kernel_occupancy(dev, e->fn_persistent, e->nt, occ);
+                },
+                d);
+    if (st != GEMM_OK) return st;
+    const Prob p = make_prob(A, B, C, D, M, N, K, d);
+    const EpiArgs ep = make_epi(pl, alpha, beta, sa, sb);
+    if (!d.e) {
+        st = run_generic(pl, p, ep, hs);
+        if (st == GEMM_OK) note_stream(pl, hs);
+        return st == GEMM_OK ? ok() : st;
+    }
+    KArgs a;
+    a.p = p;
+    a.e = ep;
+    a.s.grid = d.grid;
+    a.s.total_tiles = d.total;
+    a.s.sk_tiles = d.sk_tiles;
+    a.s.sk_iters = d.sk_iters;
+    a.s.group_m = d.group_m;
+    a.s.xcd_remap = 1;
+    a.s.partials = nullptr;
+    a.s.counters = nullptr;
+    if (d.sk_tiles > 0) {
+        const size_t pbytes = (size_t)2 * d.grid * d.e->bm * d.e->bn * sizeof(float);
+        if ((st = ensure_workspace(pl, pbytes, (size_t)d.sk_tiles, hs)) != GEMM_OK) return st;
+        a.s.partials = pl->partials;
+        a.s.counters = pl->counters;
+    }
+    hipError_t e = d.e->run(a, d.grid, hs);
+    if (e != hipSuccess) return hip_fail(e, "tile kernel launch");
+    note_stream(pl, hs);
+    return ok();
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ C ABI
+
+extern "C" {
+
+gemm_status gemm_plan_create(gemm_plan_t *out, gemm_dtype a, gemm_dtype b, gemm_dtype c, gemm_dtype d,
+                             gemm_dtype acc, gemm_layout la, gemm_layout lb, gemm_layout lc,
+                             gemm_epilogue epi) {
+    if (!out) return fail(GEMM_INVALID_ARG, "gemm_plan_create: out is NULL");
+    *out = nullptr;
+    auto bad_layout = [](gemm_layout l) { return l != GEMM_ROW_MAJOR && l != GEMM_COL_MAJOR; };
+    if (bad_layout(la) || bad_layout(lb) || bad_layout(lc))
+        return fail(GEMM_INVALID_ARG, "gemm_plan_create: layout must be ROW_MAJOR or COL_MAJOR");
+    if (epi != GEMM_EPI_LINEAR && epi != GEMM_EPI_RELU)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_create: epilogue must be LINEAR or RELU");
+    int fam = -1;
+    for (const Tuple &t : kSupported)
+        if (t.a == a && t.b == b && t.c == c && t.d == d && t.acc == acc) fam = t.fam;
+    if (fam < 0)
+        return fail(GEMM_UNSUPPORTED,
+                    "gemm_plan_create: element tuple (A=%s, B=%s, C=%s, D=%s, accumulator=%s) is not "
+                    "supported; supported: (F32,F32,F32,F32,F32), (F16,F16,F16,F16,F32), "
+                    "(BF16,BF16,BF16,BF16,F32), (F8_E4M3,F8_E4M3,BF16,BF16,F32)",
+                    dtype_name(a), dtype_name(b), dtype_name(c), dtype_name(d), dtype_name(acc));
+    gemm_plan_s *p = new (std::nothrow) gemm_plan_s();
+    if (!p) return fail(GEMM_OUT_OF_MEMORY, "gemm_plan_create: host allocation failed");
+    p->magic = kMagic;
+    p->a = a;
+    p->b = b;
+    p->c = c;
+    p->d = d;
+    p->acc = acc;
+    p->la = la;
+    p->lb = lb;
+    p->lc = lc;
+    p->epi = epi;
+    p->fam = fam;
+    p->sched = GEMM_SCHED_AUTO;
+    p->tile = GEMM_TILE_AUTO;
+    p->sk_grid = 0;
+    p->device = -1;
+    *out = p;
+    return ok();
+}
+
+gemm_status gemm_plan_create_simple(gemm_plan_t *out, gemm_dtype element, gemm_layout layout,
+                                    gemm_epilogue epi) {
+    if (element == GEMM_F8_E4M3)
+        return fail(GEMM_UNSUPPORTED,
+                    "gemm_plan_create_simple: F8_E4M3 needs BF16 C/D; use gemm_plan_create");
+    return gemm_plan_create(out, element, element, element, element, GEMM_F32, layout, layout, layout,
+                            epi);
+}
+
+gemm_status gemm_plan_destroy(gemm_plan_t p) {
+    if (!p) return ok();
+    if (!plan_ok(p)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_destroy: invalid plan handle");
+    gemm_status st = GEMM_OK;
+    if (p->used || p->gevent_pending) {
+        hipError_t e = hipStreamSynchronize(p->last_stream);
+        if (e != hipSuccess) st = hip_fail(e, "gemm_plan_destroy: hipStreamSynchronize");
+    }
+    if (p->partials) (void)hipFree(p->partials);
+    if (p->counters) (void)hipFree(p->counters);
+    if (p->gdesc) (void)hipFree(p->gdesc);
+    if (p->gevent) (void)hipEventDestroy(p->gevent);
+    if (p->ghost) (void)hipHostFree(p->ghost);
+    p->magic = 0;
+    delete p;
+    return st == GEMM_OK ? ok() : st;
+}
+
+gemm_status gemm_plan_set_config(gemm_plan_t p, gemm_schedule s, gemm_tile t, int32_t sk_grid) {
+    if (!plan_ok(p)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_set_config: invalid plan handle");
+    if (s < GEMM_SCHED_AUTO || s > GEMM_SCHED_HYBRID)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_set_config: unknown schedule %d", (int)s);
+    if (t < GEMM_TILE_AUTO || t > GEMM_TILE_GENERIC)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_set_config: unknown tile %d", (int)t);
+    if (sk_grid < 0) return fail(GEMM_INVALID_ARG, "gemm_plan_set_config: sk_grid < 0");
+    p->sched = s;
+    p->tile = t;
+    p->sk_grid = sk_grid;
+    return ok();
+}
+
+gemm_status gemm_plan_run(gemm_plan_t p, const void *A, const void *B, const void *C, void *D, int64_t M,
+                          int64_t N, int64_t K, float alpha, float beta, void *stream) {
+    return run_one(p, A, B, C, D, M, N, K, alpha, beta, nullptr, nullptr, stream);
+}
+
+gemm_status gemm_plan_run_scaled(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,
+                                 int64_t M, int64_t N, int64_t K, float alpha, float beta,
+                                 const float *scale_a, const float *scale_b, void *stream) {
+    return run_one(p, A, B, C, D, M, N, K, alpha, beta, scale_a, scale_b, stream);
+}
+
+gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32_t count, float alpha,
+                             float beta, void *stream) {
+    if (!plan_ok(pl)) return fail(GEMM_NOT_INITIALIZED, "grouped_gemm_run: invalid plan handle");
+    if (count < 0) return fail(GEMM_INVALID_ARG, "grouped_gemm_run: count < 0");
+    if (count > 0 && !problems) return fail(GEMM_INVALID_ARG, "grouped_gemm_run: problems is NULL");
+    for (int32_t i = 0; i < count; ++i) {
+        const gemm_problem &q = problems[i];
+        char where[64];
+        snprintf(where, sizeof(where), "grouped_gemm_run problem %d", (int)i);
+        gemm_status st = validate_problem(pl, q.A, q.B, q.C, q.D, q.M, q.N, q.K, beta, where);
+        if (st != GEMM_OK) return st;
+    }
+    bool any = false;
+    for (int32_t i = 0; i < count && !any; ++i) any = problems[i].M > 0 && problems[i].N > 0;
+    if (!any) return ok();
+    int dev = 0, cus = 0;
+    gemm_status st = check_device(pl, &dev);
+    if (st != GEMM_OK) return st;
+    if ((st = device_cus(dev, &cus)) != GEMM_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool a_kc = pl->la == GEMM_ROW_MAJOR, b_kc = pl->lb == GEMM_COL_MAJOR;
+    const KernelEntry *e = registry().find(pl->fam, a_kc, b_kc, TILE_128x128);
+    const int esz = elem_bytes(pl->fam), osz = out_bytes(pl->fam);
+    const EpiArgs ep = make_epi(pl, alpha, beta, nullptr, nullptr);
+
+    std::vector<GroupDesc> table;
+    std::vector<int32_t> scalar_path;
+    int64_t total = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const gemm_problem &q = problems[i];
+        if (q.M == 0 || q.N == 0) continue;
+        const void *C = beta == 0.0f ? nullptr : q.C;
+        const char *why = (e && e->fn_grouped && pl->tile != GEMM_TILE_GENERIC) ? nullptr : "no grouped kernel";
+        if (!why && q.K > 0) {
+            why = operand_vec_problem(q.A, a_kc, a_kc ? q.K : q.M, e->bm, esz);
+            if (!why) why = operand_vec_problem(q.B, b_kc, b_kc ? q.K : q.N, e->bn, esz);
+        }
+        if (why) {
+            scalar_path.push_back(i);
+            continue;
+        }
+        GroupDesc g;
+        std::memset(&g, 0, sizeof(g));
+        Decision d;
+        d.tiles_m = (int)cdiv(q.M, e->bm);
+        d.tiles_n = (int)cdiv(q.N, e->bn);
+        d.ipt = (int)cdiv(q.K, e->bk);
+        d.vec_cd = (pl->lc == GEMM_ROW_MAJOR && q.N % 4 == 0 &&
+                    reinterpret_cast<uintptr_t>(q.D) % (4 * osz) == 0 &&
+                    (!C || reinterpret_cast<uintptr_t>(C) % (4 * osz) == 0))
+                       ? 1 : 0;
+        g.p = make_prob(q.A, q.B, C, q.D, q.M, q.N, q.K, d);
+        g.tile_start = (int)total;
+        total += (int64_t)d.tiles_m * d.tiles_n;
+        if (total > 0x7FFFFFFFLL) return fail(GEMM_UNSUPPORTED, "grouped_gemm_run: more than 2^31 tiles");
+        table.push_back(g);
+    }
+    if (!table.empty()) {
+        const size_t bytes = table.size() * sizeof(GroupDesc);
+        if (table.size() > pl->gdesc_cap) {
+            if (pl->used || pl->gevent_pending) {
+                hipError_t he = hipStreamSynchronize(pl->last_stream);
+                if (he != hipSuccess) return hip_fail(he, "hipStreamSynchronize (descriptor growth)");
+                pl->gevent_pending = false;
+            }
+            if (pl->gdesc) (void)hipFree(pl->gdesc);
+            if (pl->ghost) (void)hipHostFree(pl->ghost);
+            pl->gdesc = nullptr;
+            pl->ghost = nullptr;
+            pl->gdesc_cap = 0;
+            const size_t cap = table.size() < 64 ? 64 : table.size();
+            hipError_t he = hipMalloc(reinterpret_cast<void **>(&pl->gdesc), cap * sizeof(GroupDesc));
+            if (he != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(GEMM_OUT_OF_MEMORY, "grouped descriptor table: %s", hipGetErrorString(he));
+            }
+            he = hipHostMalloc(reinterpret_cast<void **>(&pl->ghost), cap * sizeof(GroupDesc),
+                               hipHostMallocDefault);
+            if (he != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(GEMM_OUT_OF_MEMORY, "grouped pinned staging: %s", hipGetErrorString(he));
+            }
+            pl->gdesc_cap = cap;
+        }
+        if (!pl->gevent) {
+            hipError_t he = hipEventCreateWithFlags(&pl->gevent, hipEventDisableTiming);
+            if (he != hipSuccess) return hip_fail(he, "hipEventCreate");
+        }
+        if (pl->gevent_pending) {   // the previous upload must finish before reuse
+            hipError_t he = hipEventSynchronize(pl->gevent);
+            if (he != hipSuccess) return hip_fail(he, "hipEventSynchronize (descriptor staging)");
+            pl->gevent_pending = false;
+        }
+        std::memcpy(pl->ghost, table.data(), bytes);
+        hipError_t he = hipMemcpyAsync(pl->gdesc, pl->ghost, bytes, hipMemcpyHostToDevice, hs);
+        if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync (descriptor table)");
+        he = hipEventRecord(pl->gevent, hs);
+        if (he != hipSuccess) return hip_fail(he, "hipEventRecord");
+        pl->gevent_pending = true;
+        int occ = 1;
+        if ((st = kernel_occupancy(dev, e->fn_grouped, e->nt, &occ)) != GEMM_OK) return st;
+        GroupArgs ga;
+        ga.desc = pl->gdesc;
+        ga.count = (int)table.size();
+        ga.total_tiles = (int)total;
+        const int64_t G = (int64_t)cus * occ;
+        ga.grid = (int)(total < G ? total : G);
+        ga.group_m = 4;
+        ga.xcd_remap = 1;
+        ga.e = ep;
+        he = e->run_grouped(ga, ga.grid, hs);
+        if (he != hipSuccess) return hip_fail(he, "grouped kernel launch");
+        note_stream(pl, hs);
+    }
+    for (int32_t i : scalar_path) {
+        const gemm_problem &q = problems[i];
+        Decision d;
+        d.vec_cd = 0;
+        const Prob p = make_prob(q.A, q.B, beta == 0.0f ? nullptr : q.C, q.D, q.M, q.N, q.K, d);
+        if ((st = run_generic(pl, p, ep, hs)) != GEMM_OK) return st;
+        note_stream(pl, hs);
+    }
+    return ok();
+}
+
+gemm_status gemm_plan_describe(gemm_plan_t pl, int64_t M, int64_t N, int64_t K, int32_t num_cus, char *buf,
+                               int32_t len) {
+    if (!plan_ok(pl)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_describe: invalid plan handle");
+    if (!buf || len <= 0) return fail(GEMM_INVALID_ARG, "gemm_plan_describe: empty buffer");
+    if (M < 0 || N < 0 || K < 0) return fail(GEMM_INVALID_ARG, "gemm_plan_describe: negative size");
+    const int cus = num_cus > 0 ? num_cus : 256;
+    // aligned stand-in pointers: describes the vector-load path
+    const void *fake = reinterpret_cast<const void *>(uintptr_t(1) << 20);
+    Decision d;
+    gemm_status st = decide(pl, fake, fake, fake, fake, M, N, K, 1.0f, cus,
+                            [](const KernelEntry *e, int *occ) {
+                                *occ = static_occupancy(e);
+                                return GEMM_OK;
+                            },
+                            d);
+    if (st != GEMM_OK) return st;
+    snprintf(buf, (size_t)len,
+             "{\"kernel\": \"%s\", \"tile\": \"%s\", \"bk\": %d, \"waves\": %d, \"schedule\": \"%s\", "
+             "\"tiles\": %d, \"ipt\": %d, \"sk_tiles\": %d, \"grid\": %d, \"generic_reason\": \"%s\"}",
+             d.e ? "tile" : "generic", tile_name(d.e), d.e ? d.e->bk : 16, d.e ? d.e->nt / 64 : 4,
+             sched_name(d.sched), d.total, d.ipt, d.sk_tiles, d.grid, d.why_generic);
+    return ok();
+}
+
+const char *gemm_last_error(void) { return g_err.c_str(); }
+
+const char *gemm_status_string(gemm_status s) {
+    switch (s) {
+    case GEMM_OK: return "GEMM_OK";
+    case GEMM_INVALID_ARG: return "GEMM_INVALID_ARG";
+    case GEMM_UNSUPPORTED: return "GEMM_UNSUPPORTED";
+    case GEMM_HIP_ERROR: return "GEMM_HIP_ERROR";
+    case GEMM_OUT_OF_MEMORY: return "GEMM_OUT_OF_MEMORY";
+    case GEMM_NOT_INITIALIZED: return "GEMM_NOT_INITIALIZED";
+    }
+    return "GEMM_UNKNOWN_STATUS";
+}
+
+int32_t gemm_supported_count(void) { return kNumSupported; }
+
+gemm_status gemm_supported_get(int32_t i, gemm_dtype *a, gemm_dtype *b, gemm_dtype *c, gemm_dtype *d,
+                               gemm_dtype *acc) {
+    if (i < 0 || i >= kNumSupported) return fail(GEMM_INVALID_ARG, "gemm_supported_get: index %d", (int)i);
+    if (a) *a = kSupported[i].a;
+    if (b) *b = kSupported[i].b;
+    if (c) *c = kSupported[i].c;
+    if (d) *d = kSupported[i].d;
+    if (acc) *acc = kSupported[i].acc;
+    return ok();
+}
+
+const char *gemm_version(void) { return "mi355-gemm 0.1.0 (gfx950)"; }
+
+}  // extern "C"

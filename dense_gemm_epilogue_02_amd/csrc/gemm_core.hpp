@@ -1,0 +1,729 @@
+// gemm_core.hpp -- device building blocks of the gfx950 GEMM
+//
+//   D = epilogue(alpha * s_A * s_B * (A * B) + beta * C),  fp32 accumulation
+//
+// The operation is the one stated in "CUTLASS Python接口" section 3.3 and
+// "CUTLASS Python 接口全解析" section 2 (D = A*B + C, with alpha/beta and an
+// fp32 accumulator); the ReLU epilogue follows "CUTLASS Python接口" section
+// 5.2 (activation applied after the linear combination).
+//
+// Design (CDNA4 / gfx950):
+//   * A workgroup owns a BM x BN output tile. K is walked in k-tiles of 128
+//     bytes per row (64 bf16/f16, 128 fp8, 32 fp32 elements).
+//   * Both operand tiles live in LDS "K-contiguous": row r (an m of A or an n
+//     of B) holds the k-tile's 128 bytes as eight 16-byte chunks. Chunk c of
+//     row r is stored at chunk slot c ^ swz(r), swz(r) = (r ^ (r >> 3)) & 7,
+//     which keeps 16-byte MFMA fragment reads, row-wise staging writes and
+//     transposed staging writes free of bank conflicts.
+//   * Global -> LDS staging uses 16-byte buffer loads (out-of-range lanes get
+//     an offset past num_records and read zeros). An operand whose contiguous
+//     dimension is K is copied chunk by chunk; one whose contiguous dimension
+//     is M (A ColumnMajor) or N (B RowMajor) is loaded as VEC x VEC element
+//     blocks and transposed in registers before the LDS write.
+//   * Two LDS stages: the k-tile t+1 is fetched into registers while tile t is
+//     multiplied out of LDS, then written to the other stage (one barrier per
+//     k-tile).
+//   * MFMA 32x32 blocks with src0 = B rows (n) and src1 = A rows (m), so each
+//     lane ends up with four consecutive n of one m: RowMajor D gets 8- or
+//     16-byte vector stores straight from the accumulators.
+//   * The k index inside one MFMA is assigned identically for both operands
+//     (lane group g, element e -> k = chunk(g) * VEC + e), so the hardware's
+//     sum over its K slots is exactly the sum over this k-tile's k.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mg {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+enum Family { FAM_F32 = 0, FAM_F16 = 1, FAM_BF16 = 2, FAM_F8 = 3 };
+
+constexpr int KTILE_BYTES = 128;      // bytes of K per LDS row per k-tile
+constexpr uint32_t OOB_OFFSET = 0x80000000u;
+constexpr int NUM_RECORDS = 0x7FFFFFFF;
+constexpr int RSRC_FLAGS = 0x00020000;   // gfx9 raw buffer, 32-bit data format
+
+// ---------------------------------------------------------------- per-family
+
+template <int FAM> struct Fam;
+
+template <> struct Fam<FAM_BF16> {
+    static constexpr int ESZ = 2, CPL = 1;
+    using Out = __bf16;
+    static __device__ __forceinline__ void mma(f32x16 &c, const u32x4 *x, const u32x4 *y) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[0]),
+                                                     __builtin_bit_cast(bf16x8, y[0]), c, 0, 0, 0);
+    }
+};
+template <> struct Fam<FAM_F16> {
+    static constexpr int ESZ = 2, CPL = 1;
+    using Out = _Float16;
+    static __device__ __forceinline__ void mma(f32x16 &c, const u32x4 *x, const u32x4 *y) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x[0]),
+                                                    __builtin_bit_cast(f16x8, y[0]), c, 0, 0, 0);
+    }
+};
+template <> struct Fam<FAM_F32> {
+    static constexpr int ESZ = 4, CPL = 1;
+    using Out = float;
+    static __device__ __forceinline__ void mma(f32x16 &c, const u32x4 *x, const u32x4 *y) {
+        const f32x4 xv = __builtin_bit_cast(f32x4, x[0]);
+        const f32x4 yv = __builtin_bit_cast(f32x4, y[0]);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(xv.x, yv.x, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(xv.y, yv.y, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(xv.z, yv.z, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(xv.w, yv.w, c, 0, 0, 0);
+    }
+};
+template <> struct Fam<FAM_F8> {
+    static constexpr int ESZ = 1, CPL = 2;
+    using Out = __bf16;
+    static __device__ __forceinline__ void mma(f32x16 &c, const u32x4 *x, const u32x4 *y) {
+        i32x8 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = (int)x[0][e]; a[e + 4] = (int)x[1][e];
+            b[e] = (int)y[0][e]; b[e + 4] = (int)y[1][e];
+        }
+        // format 0 = FP8 E4M3 for both operands; E8M0 scale 127 = 1.0
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    }
+};
+
+// ---------------------------------------------------------------- arguments
+
+// One GEMM problem as the tile engine sees it (uniform per workgroup).
+struct Prob {
+    const char *A;
+    const char *B;
+    const char *C;
+    char *D;
+    int64_t M, N, K;
+    int tiles_m, tiles_n, ipt;   // tile grid and k-tiles per output tile
+    int vec_cd;                  // C/D allow 4-element vector access
+};
+
+struct EpiArgs {
+    float alpha, beta;
+    const float *scale_a, *scale_b;   // device pointers or null (1.0)
+    int relu;
+    int lc_row;                       // C/D RowMajor
+};
+
+// Persistent schedule: schedule indices [0, sk_tiles) are split stream-K
+// style over `grid` workgroups; [sk_tiles, total) are whole tiles dealt out
+// round robin.
+struct Sched {
+    int grid;
+    int total_tiles;
+    int sk_tiles;
+    int64_t sk_iters;       // sk_tiles * ipt
+    int group_m;            // raster: tile rows per swizzle group
+    int xcd_remap;          // map consecutive virtual ids onto one XCD
+    float *partials;        // stream-K workspace: 2 * grid slots of BM*BN fp32
+    int *counters;          // one arrival counter per stream-K tile (self-resetting)
+};
+
+struct KArgs {
+    Prob p;
+    EpiArgs e;
+    Sched s;
+};
+
+// Grouped GEMM: per-problem descriptors in device memory.
+struct GroupDesc {
+    Prob p;
+    int tile_start;   // prefix sum of tiles of the problems before this one
+    int pad[3];
+};
+
+struct GroupArgs {
+    const GroupDesc *desc;
+    int count;
+    int total_tiles;
+    int grid;
+    int group_m;
+    int xcd_remap;
+    EpiArgs e;
+};
+
+// ---------------------------------------------------------------- helpers
+
+// Wave-uniform copies (the compiler cannot always prove uniformity; buffer
+// descriptors and M0 must live in scalar registers).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(uniform_ptr(base)), (short)0,
+                                             NUM_RECORDS, RSRC_FLAGS);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+__device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
+    return (uint32_t)(row * KTILE_BYTES + ((chunk ^ swz(row)) << 4));
+}
+
+// In-register transpose of a VEC x VEC block of ESZ-byte elements held as
+// VEC rows of 16 bytes: out[j] element i = in[i] element j.
+template <int ESZ> struct Transpose;
+template <> struct Transpose<4> {
+    static __device__ __forceinline__ void run(const u32x4 *in, u32x4 *out) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[j][i] = in[i][j];
+    }
+};
+template <> struct Transpose<2> {
+    static __device__ __forceinline__ void run(const u32x4 *in, u32x4 *out) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t lo = in[2 * d][j >> 1], hi = in[2 * d + 1][j >> 1];
+                out[j][d] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u))
+                                    : ((lo & 0xFFFFu) | (hi << 16));
+            }
+    }
+};
+template <> struct Transpose<1> {
+    static __device__ __forceinline__ void run(const u32x4 *in, u32x4 *out) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int sh = 8 * (j & 3);
+                uint32_t v = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    v |= ((in[4 * d + b][j >> 2] >> sh) & 0xFFu) << (8 * b);
+                out[j][d] = v;
+            }
+    }
+};
+
+// ---------------------------------------------------------------- staging
+
+// Global -> register -> LDS copy of one operand k-tile with R rows.
+// KC: the operand's contiguous dimension is K (A RowMajor, B ColumnMajor).
+template <int R, int ESZ, bool KC, int NT> struct Stager {
+    static constexpr int VEC = 16 / ESZ;
+    static constexpr int UNITS = KC ? R * 8 : (R / VEC) * 8;
+    static constexpr int LPU = KC ? 1 : VEC;           // loads per unit
+    static constexpr int UPT = (UNITS + NT - 1) / NT;  // units per thread
+    static constexpr bool FULL = (UNITS % NT) == 0;
+    u32x4 r[UPT * LPU];
+
+    // base: operand element (row r0, k0) for KC, (k0, r0) otherwise.
+    // ld_bytes: byte distance between consecutive rows of the storage.
+    // r_left: valid rows from r0; k_left: valid k from k0.
+    __device__ __forceinline__ void load(const char *base, uint32_t ld_bytes, int r_left,
+                                         int k_left, int tid) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+#pragma unroll
+        for (int u = 0; u < UPT; ++u) {
+            const int unit = tid + u * NT;
+            const bool act = FULL || unit < UNITS;
+            if constexpr (KC) {
+                const int row = unit >> 3, c = unit & 7;
+                const bool ok = act && row < r_left && c * VEC < k_left;
+                r[u] = buf_load16(rs, ok ? row * ld_bytes + (uint32_t)(c << 4) : OOB_OFFSET);
+            } else {
+                constexpr int RB = R / VEC;
+                const int rb = unit % RB, kb = unit / RB;
+                const bool okr = act && rb * VEC < r_left;
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    const int k = kb * VEC + i;
+                    const bool ok = okr && k < k_left;
+                    r[u * VEC + i] =
+                        buf_load16(rs, ok ? (uint32_t)k * ld_bytes + (uint32_t)(rb << 4) : OOB_OFFSET);
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(char *lds, int tid) const {
+#pragma unroll
+        for (int u = 0; u < UPT; ++u) {
+            const int unit = tid + u * NT;
+            if (!FULL && unit >= UNITS) continue;
+            if constexpr (KC) {
+                *reinterpret_cast<u32x4 *>(lds + lds_off(unit >> 3, unit & 7)) = r[u];
+            } else {
+                constexpr int RB = R / VEC;
+                const int rb = unit % RB, kb = unit / RB;
+                u32x4 t[VEC];
+                Transpose<ESZ>::run(&r[u * VEC], t);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j)
+                    *reinterpret_cast<u32x4 *>(lds + lds_off(rb * VEC + j, kb)) = t[j];
+            }
+        }
+    }
+};
+
+// Direct global -> LDS copy (buffer_load_dwordx4 ... lds) of a K-contiguous
+// operand k-tile with R rows: no staging registers. One instruction moves 64
+// lanes x 16 bytes into 1 KiB of consecutive LDS, lane i landing at slot
+// base + i; lane i therefore fetches the logical chunk that the swizzle puts
+// in that slot. Out-of-range lanes use an offset past num_records and write
+// zeros.
+template <int R, int ESZ, int NT> struct DirectStager {
+    static constexpr int VEC = 16 / ESZ;
+    static constexpr int WAVES = NT / 64;
+    static constexpr int INSTR = R / 8;            // 8 rows x 8 chunks each
+    static constexpr int IPW = INSTR / WAVES;      // instructions per wave
+    static_assert(INSTR % WAVES == 0, "rows per tile must cover all waves");
+
+    static __device__ __forceinline__ void issue(const char *base, uint32_t ld_bytes, int r_left,
+                                                 int k_left, char *lds, int tid) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+        const int lane = tid & 63, wave = uniform(tid >> 6);
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int instr = wave * IPW + i;
+            const int row = instr * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ swz(row);
+            const bool ok = row < r_left && c * VEC < k_left;
+            const uint32_t off = ok ? row * ld_bytes + (uint32_t)(c << 4) : OOB_OFFSET;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void *)(lds + instr * 1024), 16, off, 0, 0, 0);
+        }
+    }
+};
+
+// ---------------------------------------------------------------- tile engine
+
+template <int FAM_, bool A_KC, bool B_KC, int BM_, int BN_, int WM_, int WN_>
+struct Tile {
+    static constexpr int FAM = FAM_, BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    using F = Fam<FAM>;
+    using Out = typename F::Out;
+    static constexpr int ESZ = F::ESZ, CPL = F::CPL;
+    static constexpr int NT = 64 * WM * WN;
+    static constexpr int VEC = 16 / ESZ;            // elements per 16-byte chunk
+    static constexpr int BK = KTILE_BYTES / ESZ;    // elements of K per k-tile
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int FM = WTM / 32, FN = WTN / 32;
+    static constexpr int SUBSTEPS = 8 / (2 * CPL);
+    static constexpr int A_BYTES = BM * KTILE_BYTES, B_BYTES = BN * KTILE_BYTES;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+
+    // K-contiguous operands go straight to LDS; the others are staged through
+    // registers and transposed.
+    using SA = Stager<BM, ESZ, false, NT>;
+    using SB = Stager<BN, ESZ, false, NT>;
+    using DA = DirectStager<BM, ESZ, NT>;
+    using DB = DirectStager<BN, ESZ, NT>;
+
+    struct Acc {
+        f32x16 v[FN][FM];
+    };
+
+    static __device__ __forceinline__ void zero(Acc &a) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) a.v[i][j][e] = 0.0f;
+    }
+
+    // Element pointers of the operand k-tile origins, and row strides.
+    static __device__ __forceinline__ void a_tile(const Prob &p, int tm, int kt, const char *&base,
+                                                  uint32_t &ld, int &r_left, int &k_left) {
+        const int64_t m0 = (int64_t)tm * BM, k0 = (int64_t)kt * BK;
+        if constexpr (A_KC) {   // RowMajor A: [M][K]
+            base = p.A + (m0 * p.K + k0) * ESZ;
+            ld = (uint32_t)(p.K * ESZ);
+        } else {                // ColumnMajor A: [K][M]
+            base = p.A + (k0 * p.M + m0) * ESZ;
+            ld = (uint32_t)(p.M * ESZ);
+        }
+        r_left = (int)imin64(p.M - m0, BM);
+        k_left = (int)imin64(p.K - k0, BK);
+    }
+    static __device__ __forceinline__ void b_tile(const Prob &p, int tn, int kt, const char *&base,
+                                                  uint32_t &ld, int &r_left, int &k_left) {
+        const int64_t n0 = (int64_t)tn * BN, k0 = (int64_t)kt * BK;
+        if constexpr (B_KC) {   // ColumnMajor B: [N][K]
+            base = p.B + (n0 * p.K + k0) * ESZ;
+            ld = (uint32_t)(p.K * ESZ);
+        } else {                // RowMajor B: [K][N]
+            base = p.B + (k0 * p.N + n0) * ESZ;
+            ld = (uint32_t)(p.N * ESZ);
+        }
+        r_left = (int)imin64(p.N - n0, BN);
+        k_left = (int)imin64(p.K - k0, BK);
+    }
+
+    // Start the copy of k-tile kt: direct operands are issued into `stage`,
+    // transposed operands are fetched into registers (stored by store_regs).
+    static __device__ __forceinline__ void issue_stage(const Prob &p, int tm, int tn, int kt,
+                                                       char *stage, SA &sa, SB &sb, int tid) {
+        const char *base;
+        uint32_t ld;
+        int rl, kl;
+        a_tile(p, tm, kt, base, ld, rl, kl);
+        if constexpr (A_KC) DA::issue(base, ld, rl, kl, stage, tid);
+        else sa.load(base, ld, rl, kl, tid);
+        b_tile(p, tn, kt, base, ld, rl, kl);
+        if constexpr (B_KC) DB::issue(base, ld, rl, kl, stage + A_BYTES, tid);
+        else sb.load(base, ld, rl, kl, tid);
+    }
+
+    static __device__ __forceinline__ void store_regs(char *stage, const SA &sa, const SB &sb,
+                                                      int tid) {
+        if constexpr (!A_KC) sa.store(stage, tid);
+        if constexpr (!B_KC) sb.store(stage + A_BYTES, tid);
+    }
+
+    // Multiply one LDS stage into the accumulators.
+    static __device__ __forceinline__ void compute(const char *sA, const char *sB, Acc &acc,
+                                                   int lane, int wm, int wn) {
+        const int g = lane >> 5, r = lane & 31;
+#pragma unroll
+        for (int s = 0; s < SUBSTEPS; ++s) {
+            u32x4 xf[FN][CPL], yf[FM][CPL];
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+                const int row = wn * WTN + i * 32 + r;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    xf[i][c] = *reinterpret_cast<const u32x4 *>(
+                        sB + lds_off(row, s * 2 * CPL + g * CPL + c));
+            }
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                const int row = wm * WTM + j * 32 + r;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    yf[j][c] = *reinterpret_cast<const u32x4 *>(
+                        sA + lds_off(row, s * 2 * CPL + g * CPL + c));
+            }
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) F::mma(acc.v[i][j], xf[i], yf[j]);
+        }
+    }
+
+    // acc = sum over k-tiles [kt0, kt1) of the tile (tm, tn). Ends with a
+    // barrier, so LDS may be reused immediately afterwards.
+    //
+    // Per k-tile: wait for this wave's copies of tile kt, barrier (every
+    // wave's copies of kt are in LDS and every wave has finished reading the
+    // other stage), start the copy of kt+1 into the other stage, multiply kt.
+    static __device__ __forceinline__ void mainloop(const Prob &p, int tm, int tn, int kt0, int kt1,
+                                                    Acc &acc, char *lds) {
+        const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+        const int wm = wave / WN, wn = wave % WN;
+        zero(acc);
+        if (kt0 >= kt1) return;
+        SA sa;
+        SB sb;
+        issue_stage(p, tm, tn, kt0, lds, sa, sb, tid);
+        store_regs(lds, sa, sb, tid);
+        for (int kt = kt0; kt < kt1; ++kt) {
+            char *cur = lds + ((kt - kt0) & 1) * STAGE_BYTES;
+            char *nxt = lds + (((kt - kt0) & 1) ^ 1) * STAGE_BYTES;
+            const bool more = kt + 1 < kt1;
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of kt landed
+            __syncthreads();
+            if (more) issue_stage(p, tm, tn, kt + 1, nxt, sa, sb, tid);
+            compute(cur, cur + A_BYTES, acc, lane, wm, wn);
+            if (more) store_regs(nxt, sa, sb, tid);
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue ------------------------------------------------------------
+    //
+    // v = alpha' * acc + beta * C (C not read when beta == 0), alpha' = alpha
+    // times the per-tensor scales; ReLU maps v to max(v, +0) (NaN -> +0); one
+    // round-to-nearest-even conversion into the output type.
+
+    static __device__ __forceinline__ float act(float v, int relu) {
+        return relu ? (v > 0.0f ? v : 0.0f) : v;
+    }
+
+    static __device__ __forceinline__ float eff_alpha(const EpiArgs &e) {
+        float a = e.alpha;
+        if (e.scale_a) a *= *e.scale_a;
+        if (e.scale_b) a *= *e.scale_b;
+        return a;
+    }
+
+    // Interior tile, RowMajor C/D with 4-element vector access: every lane
+    // owns four consecutive n of one m for each (i, j, q).
+    template <bool BETA>
+    static __device__ __forceinline__ void epi_fast(const Prob &p, const EpiArgs &e, float alpha,
+                                                    int64_t m_base, int64_t n_base, const Acc &acc) {
+        Out *D = reinterpret_cast<Out *>(p.D);
+        const Out *C = reinterpret_cast<const Out *>(p.C);
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int64_t row = (m_base + j * 32) * p.N;
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t idx = row + n_base + i * 32 + q * 8;
+                    float v[4];
+                    if constexpr (BETA) {
+                        float c[4];
+                        if constexpr (sizeof(Out) == 4) {
+                            const f32x4 t = *reinterpret_cast<const f32x4 *>(C + idx);
+#pragma unroll
+                            for (int t4 = 0; t4 < 4; ++t4) c[t4] = t[t4];
+                        } else {
+                            const u32x2 t = *reinterpret_cast<const u32x2 *>(C + idx);
+#pragma unroll
+                            for (int t4 = 0; t4 < 4; ++t4)
+                                c[t4] = (float)__builtin_bit_cast(
+                                    Out, (uint16_t)(t[t4 >> 1] >> (16 * (t4 & 1))));
+                        }
+#pragma unroll
+                        for (int t4 = 0; t4 < 4; ++t4)
+                            v[t4] = act(__builtin_fmaf(alpha, acc.v[i][j][q * 4 + t4], e.beta * c[t4]),
+                                        e.relu);
+                    } else {
+#pragma unroll
+                        for (int t4 = 0; t4 < 4; ++t4) v[t4] = act(alpha * acc.v[i][j][q * 4 + t4], e.relu);
+                    }
+                    if constexpr (sizeof(Out) == 4) {
+                        *reinterpret_cast<f32x4 *>(D + idx) = f32x4{v[0], v[1], v[2], v[3]};
+                    } else {
+                        u32x2 t;
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            t[h] = (uint32_t)__builtin_bit_cast(uint16_t, (Out)v[2 * h]) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, (Out)v[2 * h + 1]) << 16);
+                        *reinterpret_cast<u32x2 *>(D + idx) = t;
+                    }
+                }
+        }
+    }
+
+    // Edge tiles, ColumnMajor C/D or unaligned C/D: element by element.
+    static __device__ __noinline__ void epi_slow(const Prob &p, const EpiArgs &e, float alpha,
+                                                 int64_t m_base, int64_t n_base, const float *vals) {
+        Out *D = reinterpret_cast<Out *>(p.D);
+        const Out *C = reinterpret_cast<const Out *>(p.C);
+        for (int j = 0; j < FM; ++j) {
+            const int64_t m = m_base + j * 32;
+            if (m >= p.M) continue;
+            for (int i = 0; i < FN; ++i)
+                for (int q = 0; q < 4; ++q)
+                    for (int t4 = 0; t4 < 4; ++t4) {
+                        const int64_t n = n_base + i * 32 + q * 8 + t4;
+                        if (n >= p.N) continue;
+                        const int64_t idx = e.lc_row ? m * p.N + n : m + n * p.M;
+                        const float a = vals[((i * FM + j) * 4 + q) * 4 + t4];
+                        float v = alpha * a;
+                        if (e.beta != 0.0f) v = __builtin_fmaf(alpha, a, e.beta * (float)C[idx]);
+                        D[idx] = (Out)act(v, e.relu);
+                    }
+        }
+    }
+
+    static __device__ __forceinline__ void epilogue(const Prob &p, const EpiArgs &e, int tm, int tn,
+                                                    const Acc &acc) {
+        const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+        const int wm = wave / WN, wn = wave % WN;
+        const float alpha = eff_alpha(e);
+        const int64_t m_base = (int64_t)tm * BM + wm * WTM + (lane & 31);
+        const int64_t n_base = (int64_t)tn * BN + wn * WTN + (lane >> 5) * 4;
+        const bool interior = e.lc_row && p.vec_cd && (int64_t)(tm + 1) * BM <= p.M &&
+                              (int64_t)(tn + 1) * BN <= p.N;
+        if (interior) {
+            if (e.beta != 0.0f) epi_fast<true>(p, e, alpha, m_base, n_base, acc);
+            else epi_fast<false>(p, e, alpha, m_base, n_base, acc);
+        } else {
+            float vals[FN * FM * 16];
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+#pragma unroll
+                    for (int x = 0; x < 16; ++x) vals[(i * FM + j) * 16 + x] = acc.v[i][j][x];
+            epi_slow(p, e, alpha, m_base, n_base, vals);
+        }
+    }
+
+    // ---- stream-K partial tiles ---------------------------------------------
+
+    static __device__ __forceinline__ void store_partial(float *slot, const Acc &acc) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int grp = (i * FM + j) * 4 + q;
+                    f32x4 t{acc.v[i][j][q * 4], acc.v[i][j][q * 4 + 1], acc.v[i][j][q * 4 + 2],
+                            acc.v[i][j][q * 4 + 3]};
+                    *reinterpret_cast<f32x4 *>(slot + ((size_t)grp * NT + tid) * 4) = t;
+                }
+    }
+
+    static __device__ __forceinline__ void add_partial(const float *slot, Acc &acc, bool first) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int grp = (i * FM + j) * 4 + q;
+                    const f32x4 t = *reinterpret_cast<const f32x4 *>(slot + ((size_t)grp * NT + tid) * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc.v[i][j][q * 4 + e] = first ? t[e] : acc.v[i][j][q * 4 + e] + t[e];
+                }
+    }
+};
+
+// ---------------------------------------------------------------- schedules
+
+// Raster order of output tiles: groups of `group_m` tile rows, column-major
+// inside a group, so consecutive schedule indices form compact 2-D blocks
+// that share A and B panels in L2.
+__device__ __forceinline__ void tile_coords(int s, int tiles_m, int tiles_n, int group_m, int &tm,
+                                            int &tn) {
+    const int per_group = group_m * tiles_n;
+    const int grp = s / per_group;
+    const int first_m = grp * group_m;
+    const int gm = min(group_m, tiles_m - first_m);
+    const int local = s - grp * per_group;
+    tm = first_m + local % gm;
+    tn = local / gm;
+}
+
+// Workgroups are dealt to the 8 XCDs round robin; give the 32 (or G/8)
+// workgroups of one XCD consecutive virtual ids so they work on neighbouring
+// tiles and share that XCD's L2.
+__device__ __forceinline__ int virtual_id(int w, int grid, int remap) {
+    if (!remap || (grid & 7)) return w;
+    return (w & 7) * (grid >> 3) + (w >> 3);
+}
+
+// Virtual workgroup whose stream-K range holds iteration x:
+// ranges are [floor(v T / G), floor((v+1) T / G)).
+__device__ __forceinline__ int sk_owner(int64_t x, int64_t T, int G) {
+    return (int)(((x + 1) * G + T - 1) / T) - 1;
+}
+
+template <class TL>
+__global__ void __launch_bounds__(TL::NT) gemm_persistent(KArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[TL::LDS_BYTES];
+    __shared__ int last_flag;
+    const Prob &p = a.p;
+    const Sched &s = a.s;
+    const int v = uniform(virtual_id(blockIdx.x, s.grid, s.xcd_remap));
+    typename TL::Acc acc;
+    int tm, tn;
+
+    if (s.sk_tiles > 0 && p.ipt > 0) {
+        const int64_t T = s.sk_iters;
+        const int G = s.grid;
+        int64_t it = (int64_t)v * T / G;
+        const int64_t end = (int64_t)(v + 1) * T / G;
+        const int first_tile = (int)(it / p.ipt);
+        while (it < end) {
+            const int t = (int)(it / p.ipt);
+            const int64_t tile_it0 = (int64_t)t * p.ipt;
+            const int k0 = (int)(it - tile_it0);
+            const int k1 = (int)(imin64(end, tile_it0 + p.ipt) - tile_it0);
+            tile_coords(t, p.tiles_m, p.tiles_n, s.group_m, tm, tn);
+            TL::mainloop(p, tm, tn, k0, k1, acc, lds);
+            if (k0 == 0 && k1 == p.ipt) {
+                TL::epilogue(p, a.e, tm, tn, acc);
+            } else {
+                // every contributor publishes its partial, the last to arrive
+                // sums all partials in contributor order (deterministic)
+                const size_t slot_elems = (size_t)TL::BM * TL::BN;
+                const int my_slot = 2 * v + (t == first_tile ? 0 : 1);
+                TL::store_partial(s.partials + my_slot * slot_elems, acc);
+                __threadfence();
+                __syncthreads();
+                const int v0 = sk_owner(tile_it0, T, G);
+                const int v1 = sk_owner(tile_it0 + p.ipt - 1, T, G);
+                if (threadIdx.x == 0) {
+                    const int old = __hip_atomic_fetch_add(&s.counters[t], 1, __ATOMIC_ACQ_REL,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+                    last_flag = (old == v1 - v0);
+                }
+                __syncthreads();
+                if (last_flag) {
+                    __threadfence();
+                    for (int u = v0; u <= v1; ++u) {
+                        const int ft = (int)(((int64_t)u * T / G) / p.ipt);
+                        const int slot = 2 * u + (t == ft ? 0 : 1);
+                        TL::add_partial(s.partials + slot * slot_elems, acc, u == v0);
+                    }
+                    TL::epilogue(p, a.e, tm, tn, acc);
+                    if (threadIdx.x == 0)
+                        __hip_atomic_store(&s.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                __syncthreads();
+            }
+            it = tile_it0 + k1;
+        }
+    }
+    for (int t = s.sk_tiles + v; t < s.total_tiles; t += s.grid) {
+        tile_coords(t, p.tiles_m, p.tiles_n, s.group_m, tm, tn);
+        TL::mainloop(p, tm, tn, 0, p.ipt, acc, lds);
+        TL::epilogue(p, a.e, tm, tn, acc);
+    }
+}
+
+template <class TL>
+__global__ void __launch_bounds__(TL::NT) gemm_grouped(GroupArgs g) {
+    __shared__ __attribute__((aligned(16))) char lds[TL::LDS_BYTES];
+    const int v = uniform(virtual_id(blockIdx.x, g.grid, g.xcd_remap));
+    typename TL::Acc acc;
+    for (int t = v; t < g.total_tiles; t += g.grid) {
+        // last problem whose first tile is <= t
+        int lo = 0, hi = g.count - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (g.desc[mid].tile_start <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        const Prob p = g.desc[lo].p;
+        int tm, tn;
+        tile_coords(t - g.desc[lo].tile_start, p.tiles_m, p.tiles_n, g.group_m, tm, tn);
+        TL::mainloop(p, tm, tn, 0, p.ipt, acc, lds);
+        TL::epilogue(p, g.e, tm, tn, acc);
+    }
+}
+
+}  // namespace mg

@@ -1,0 +1,18 @@
+// kernels_f16.hip -- f16 tile kernels for every operand layout and tile shape
+#include "kernels_inst.hpp"
+
+namespace mg {
+
+static const KernelEntry kTable[] = {
+    MG_LAYOUTS(FAM_F16, TILE_256x256, 256, 256, 2, 4, false),
+    MG_LAYOUTS(FAM_F16, TILE_128x128, 128, 128, 2, 2, true),
+    MG_LAYOUTS(FAM_F16, TILE_64x256, 64, 256, 1, 4, false),
+    MG_LAYOUTS(FAM_F16, TILE_32x256, 32, 256, 1, 4, false),
+};
+
+const KernelEntry *entries_f16(int *count) {
+    *count = (int)(sizeof(kTable) / sizeof(kTable[0]));
+    return kTable;
+}
+
+}  // namespace mg

@@ -1,0 +1,136 @@
+// kernels_generic.hip -- scalar-load GEMM for operands that vector loads cannot
+// serve (unaligned base addresses, contiguous extents that are not a multiple
+// of 16 bytes, or offsets beyond 32 bits), plus a small zero-fill kernel.
+//
+// Same contract as the tile kernels ("CUTLASS Python接口" section 3.3:
+// D = alpha*A*B + beta*C with an fp32 accumulator; section 7.2: misaligned
+// data still works, only slower): each element is loaded on its own (64-bit
+// addressing), decoded to fp32, staged in LDS, and accumulated with fp32 FMA
+// in increasing k.
+#include "kernels.hpp"
+
+namespace mg {
+
+namespace {
+
+constexpr int GT = 64;    // output tile edge
+constexpr int GK = 16;    // k per step
+
+template <int FAM> __device__ __forceinline__ float ld_elem(const char *base, int64_t idx);
+
+template <> __device__ __forceinline__ float ld_elem<FAM_F32>(const char *base, int64_t idx) {
+    return reinterpret_cast<const float *>(base)[idx];
+}
+template <> __device__ __forceinline__ float ld_elem<FAM_F16>(const char *base, int64_t idx) {
+    return (float)reinterpret_cast<const _Float16 *>(base)[idx];
+}
+template <> __device__ __forceinline__ float ld_elem<FAM_BF16>(const char *base, int64_t idx) {
+    return (float)reinterpret_cast<const __bf16 *>(base)[idx];
+}
+// OCP E4M3: sign, 4-bit exponent (bias 7), 3-bit fraction, S.1111.111 = NaN.
+template <> __device__ __forceinline__ float ld_elem<FAM_F8>(const char *base, int64_t idx) {
+    const uint32_t u = reinterpret_cast<const uint8_t *>(base)[idx];
+    const uint32_t s = (u & 0x80u) << 24, e = (u >> 3) & 15u, m = u & 7u;
+    if (e == 15u && m == 7u) return __builtin_nanf("");
+    float v;
+    if (e == 0u) v = (float)m * 0.001953125f;   // m * 2^-9
+    else v = __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
+    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) | s);
+}
+
+template <int FAM> struct OutT;
+template <> struct OutT<FAM_F32> { using T = float; };
+template <> struct OutT<FAM_F16> { using T = _Float16; };
+template <> struct OutT<FAM_BF16> { using T = __bf16; };
+template <> struct OutT<FAM_F8> { using T = __bf16; };
+
+template <int FAM>
+__global__ void __launch_bounds__(256) gemm_generic(GenericArgs a) {
+    using Out = typename OutT<FAM>::T;
+    __shared__ float As[GK][GT + 1];
+    __shared__ float Bs[GK][GT + 1];
+    const Prob &p = a.p;
+    const int tiles_n = (int)((p.N + GT - 1) / GT);
+    const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * GT;
+    const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * GT;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    float acc[4][4] = {};
+    for (int64_t k0 = 0; k0 < p.K; k0 += GK) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = tid + u * 256;      // 0 .. 1023
+            const int kk = e / GT, rr = e % GT;
+            const int64_t k = k0 + kk;
+            const int64_t m = m0 + rr, n = n0 + rr;
+            float av = 0.0f, bv = 0.0f;
+            if (k < p.K && m < p.M) av = ld_elem<FAM>(p.A, a.la_row ? m * p.K + k : m + k * p.M);
+            if (k < p.K && n < p.N) bv = ld_elem<FAM>(p.B, a.lb_row ? k * p.N + n : k + n * p.K);
+            As[kk][rr] = av;
+            Bs[kk][rr] = bv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < GK; ++kk) {
+            float x[4], y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = As[kk][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(x[i], y[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+    float alpha = a.e.alpha;
+    if (a.e.scale_a) alpha *= *a.e.scale_a;
+    if (a.e.scale_b) alpha *= *a.e.scale_b;
+    Out *D = reinterpret_cast<Out *>(p.D);
+    const Out *C = reinterpret_cast<const Out *>(p.C);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
+            if (m >= p.M || n >= p.N) continue;
+            const int64_t idx = a.e.lc_row ? m * p.N + n : m + n * p.M;
+            float v = alpha * acc[i][j];
+            if (a.e.beta != 0.0f) v = __builtin_fmaf(alpha, acc[i][j], a.e.beta * (float)C[idx]);
+            if (a.e.relu) v = v > 0.0f ? v : 0.0f;
+            D[idx] = (Out)v;
+        }
+}
+
+__global__ void zero_u32(uint32_t *p, size_t n) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_generic(int fam, const GenericArgs &a, hipStream_t st) {
+    const int64_t tiles = ((a.p.M + GT - 1) / GT) * ((a.p.N + GT - 1) / GT);
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)tiles), block(256);
+    switch (fam) {
+    case FAM_F32: hipLaunchKernelGGL(gemm_generic<FAM_F32>, grid, block, 0, st, a); break;
+    case FAM_F16: hipLaunchKernelGGL(gemm_generic<FAM_F16>, grid, block, 0, st, a); break;
+    case FAM_BF16: hipLaunchKernelGGL(gemm_generic<FAM_BF16>, grid, block, 0, st, a); break;
+    case FAM_F8: hipLaunchKernelGGL(gemm_generic<FAM_F8>, grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_u32(uint32_t *p, size_t n, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(zero_u32, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace mg

@@ -1,0 +1,16 @@
+// kernels_inst.hpp -- instantiation helper: one table row per tile kernel
+#pragma once
+
+#include "kernels.hpp"
+
+#define MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN) mg::Tile<FAM, AKC, BKC, BM, BN, WM, WN>
+
+#define MG_ROW(FAM, AKC, BKC, TILEID, BM, BN, WM, WN, GROUPED) \
+    mg::make_entry<MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN), GROUPED>(TILEID, AKC, BKC)
+
+// The four operand-layout combinations of one tile shape.
+#define MG_LAYOUTS(FAM, TILEID, BM, BN, WM, WN, GROUPED)          \
+    MG_ROW(FAM, true, true, TILEID, BM, BN, WM, WN, GROUPED),     \
+    MG_ROW(FAM, true, false, TILEID, BM, BN, WM, WN, GROUPED),    \
+    MG_ROW(FAM, false, true, TILEID, BM, BN, WM, WN, GROUPED),    \
+    MG_ROW(FAM, false, false, TILEID, BM, BN, WM, WN, GROUPED)

@@ -1,0 +1,191 @@
+/*
+ * gemm.h -- C ABI of an MI355X (gfx950) GEMM library:  D = alpha * A * B + beta * C
+ *
+ * The operation and the shape of the interface follow the pages this library
+ * is built from:
+ *   - "CUTLASS Python 接口全解析", section 2: a GEMM plan computes D = A*B + C;
+ *     section 2.1: the plan binds element_A/B/C/D/accumulator and the layout at
+ *     construction, and one plan runs problems of different shapes with the
+ *     same types; section 2.2: compilation is separate from running;
+ *     section 2.3: an elementwise activation (ReLU) fuses into the epilogue,
+ *     and run() is asynchronous with an explicit synchronisation afterwards.
+ *   - "CUTLASS Python接口", section 3.3: D = alpha * A * B + beta * C with an
+ *     fp32 accumulator; section 4.3: automatic, persistent and grouped kernel
+ *     schedules; section 7.1: descriptive errors instead of crashes.
+ *   - "Python packages associated with CUTLASS", Overview: descriptive
+ *     run-time errors and an enumeration of the configurations known to work;
+ *     Current functionality: GEMM, fused elementwise epilogue (ReLU),
+ *     stream-K work splitting, grouped GEMM.
+ *   - "Generating State-of-the-Art GEMMs with TorchInductor's CuteDSL
+ *     backend", section 5.1: FP8 matrix multiply as a scaled mm.
+ *
+ * Conventions shared by every call
+ *   - Matrices are dense and packed. A is M x K, B is K x N, C and D are
+ *     M x N. RowMajor means the last index is contiguous (X[r][c] at
+ *     base[r * cols + c]); ColumnMajor means X[r][c] at base[r + c * rows].
+ *     C and D share the plan's layout_C.
+ *   - All data pointers are device pointers (hipMalloc'd memory or torch CUDA
+ *     tensors on ROCm). The caller owns them and keeps them alive until the
+ *     enqueued work has completed on `stream`.
+ *   - `stream` is a hipStream_t passed as void*; NULL selects the null stream.
+ *     Runs are asynchronous: they enqueue kernels and return. Synchronise the
+ *     stream before reading D on the host.
+ *   - Every call returns a gemm_status; on failure gemm_last_error() gives a
+ *     descriptive, thread-local message. Arguments are validated before
+ *     anything is enqueued, so a failed call has enqueued nothing. Faults in
+ *     enqueued work surface at the caller's stream synchronisation.
+ *   - Accumulation is always fp32 (element_accumulator must be GEMM_F32).
+ *   - D may be the same pointer as C (in-place update). Any other overlap
+ *     between D and A, B or C is undefined.
+ *   - beta == 0: C is not read and may be NULL (NaN/Inf in C do not
+ *     propagate). M == 0 or N == 0: nothing is enqueued, GEMM_OK.
+ *     K == 0: D = epilogue(beta * C). Negative sizes: GEMM_INVALID_ARG.
+ *   - Any pointer alignment and any size are accepted; operands whose base
+ *     address or contiguous extent do not allow 16-byte vector loads run on a
+ *     slower, scalar-load kernel with the same arithmetic contract.
+ */
+#ifndef MI355_GEMM_H
+#define MI355_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMM_F32 = 0,
+    GEMM_F16 = 1,
+    GEMM_BF16 = 2,
+    GEMM_F8_E4M3 = 3 /* OCP FP8 E4M3 (e4m3fn: bias 7, max 448, no Inf) */
+} gemm_dtype;
+
+typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout;
+
+/* Epilogue: LINEAR gives v = alpha*acc + beta*C; RELU gives max(v, +0)
+ * (NaN maps to +0), both rounded once, to nearest even, into element_D. */
+typedef enum { GEMM_EPI_LINEAR = 0, GEMM_EPI_RELU = 1 } gemm_epilogue;
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_INVALID_ARG = 1,     /* NULL/negative/inconsistent arguments */
+    GEMM_UNSUPPORTED = 2,     /* type tuple or option not provided */
+    GEMM_HIP_ERROR = 3,       /* a HIP runtime call failed */
+    GEMM_OUT_OF_MEMORY = 4,   /* workspace allocation failed */
+    GEMM_NOT_INITIALIZED = 5  /* NULL or destroyed plan */
+} gemm_status;
+
+/* Work schedule ("CUTLASS Python接口" section 4.3: auto / persistent /
+ * grouped schedules; "Python packages associated with CUTLASS": stream-K). */
+typedef enum {
+    GEMM_SCHED_AUTO = 0,          /* heuristic: data-parallel, stream-K or hybrid */
+    GEMM_SCHED_DATA_PARALLEL = 1, /* one work unit per output tile */
+    GEMM_SCHED_STREAM_K = 2,      /* every tile's MAC iterations split evenly */
+    GEMM_SCHED_HYBRID = 3         /* whole waves data-parallel, the rest stream-K */
+} gemm_schedule;
+
+/* Output tile shape (rows of D x columns of D per workgroup). */
+typedef enum {
+    GEMM_TILE_AUTO = 0,
+    GEMM_TILE_256x256 = 1,
+    GEMM_TILE_128x128 = 2,
+    GEMM_TILE_64x256 = 3,
+    GEMM_TILE_32x256 = 4,
+    GEMM_TILE_GENERIC = 5   /* the scalar-load kernel, for any alignment */
+} gemm_tile;
+
+typedef struct gemm_plan_s *gemm_plan_t;
+
+/* Create a plan binding the element types, layouts and epilogue.
+ * Supported (element_A, element_B, element_C, element_D, element_accumulator):
+ *   (F32, F32, F32, F32, F32), (F16, F16, F16, F16, F32),
+ *   (BF16, BF16, BF16, BF16, F32), (F8_E4M3, F8_E4M3, BF16, BF16, F32).
+ * Others return GEMM_UNSUPPORTED naming the tuple. Makes no device call.
+ * On success *out owns host memory until gemm_plan_destroy. */
+gemm_status gemm_plan_create(gemm_plan_t *out, gemm_dtype element_a,
+                             gemm_dtype element_b, gemm_dtype element_c,
+                             gemm_dtype element_d, gemm_dtype element_acc,
+                             gemm_layout layout_a, gemm_layout layout_b,
+                             gemm_layout layout_c, gemm_epilogue epilogue);
+
+/* Shorthand ("CUTLASS Python 接口全解析" section 2.1: one `element` and one
+ * `layout` for every operand): element for A, B, C, D; F8_E4M3 is not
+ * accepted here (its output type differs). Accumulator fp32. */
+gemm_status gemm_plan_create_simple(gemm_plan_t *out, gemm_dtype element,
+                                    gemm_layout layout, gemm_epilogue epilogue);
+
+/* Release the plan and its device workspace. Waits for the last stream the
+ * plan ran on before freeing device memory. NULL is a no-op. */
+gemm_status gemm_plan_destroy(gemm_plan_t plan);
+
+/* Override the heuristic choice of schedule and tile (for tuning and tests).
+ * sk_grid > 0 caps the number of persistent workgroups (0 = automatic).
+ * Host-only; no device call. */
+gemm_status gemm_plan_set_config(gemm_plan_t plan, gemm_schedule schedule,
+                                 gemm_tile tile, int32_t sk_grid);
+
+/* Enqueue D = epilogue(alpha * A * B + beta * C) on `stream`.
+ * For an F8 plan this is gemm_plan_run_scaled with unit scales. */
+gemm_status gemm_plan_run(gemm_plan_t plan, const void *A, const void *B,
+                          const void *C, void *D, int64_t M, int64_t N,
+                          int64_t K, float alpha, float beta, void *stream);
+
+/* FP8 with per-tensor scales ("Generating State-of-the-Art GEMMs ...",
+ * section 5.1, scaled mm): D = epi(alpha * s_A * s_B * (A_q B_q) + beta * C).
+ * scale_a / scale_b point to one fp32 each in device memory (NULL = 1.0);
+ * they are read by the kernel, so they may be produced on the same stream.
+ * Accepted by every plan; for non-F8 plans the scales multiply alpha too. */
+gemm_status gemm_plan_run_scaled(gemm_plan_t plan, const void *A,
+                                 const void *B, const void *C, void *D,
+                                 int64_t M, int64_t N, int64_t K, float alpha,
+                                 float beta, const float *scale_a,
+                                 const float *scale_b, void *stream);
+
+/* One problem of a grouped call; pointers follow the conventions above. */
+typedef struct {
+    int64_t M, N, K;
+    const void *A;
+    const void *B;
+    const void *C; /* may be NULL when beta == 0 */
+    void *D;
+} gemm_problem;
+
+/* Grouped GEMM ("Python packages associated with CUTLASS", Current
+ * functionality): `count` independent problems with the plan's types,
+ * layouts and epilogue, and shared alpha/beta, in one persistent launch.
+ * `problems` is a host array, copied before the call returns (the caller may
+ * free it at once). Problems with M, N or K == 0 follow the single-GEMM
+ * rules. The plan keeps a device copy of the descriptor table: one plan must
+ * not run grouped calls on two streams at once. */
+gemm_status grouped_gemm_run(gemm_plan_t plan, const gemm_problem *problems,
+                             int32_t count, float alpha, float beta,
+                             void *stream);
+
+/* Describe, without any device call, the kernel and schedule a run of
+ * M x N x K would use, as a short JSON object written into buf (NUL
+ * terminated, truncated to len). num_cus = 0 assumes 256 compute units. */
+gemm_status gemm_plan_describe(gemm_plan_t plan, int64_t M, int64_t N,
+                               int64_t K, int32_t num_cus, char *buf,
+                               int32_t len);
+
+/* Thread-local description of the last failure in this thread ("" if none). */
+const char *gemm_last_error(void);
+
+/* Static name of a status code. */
+const char *gemm_status_string(gemm_status status);
+
+/* Enumerate the supported type tuples ("Python packages associated with
+ * CUTLASS", Overview: configurations known to work). */
+int32_t gemm_supported_count(void);
+gemm_status gemm_supported_get(int32_t index, gemm_dtype *element_a,
+                               gemm_dtype *element_b, gemm_dtype *element_c,
+                               gemm_dtype *element_d, gemm_dtype *element_acc);
+
+/* Library version string. */
+const char *gemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355_GEMM_H */

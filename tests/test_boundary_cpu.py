@@ -1,0 +1,169 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function include/gemm.h declares, and its host-side logic (plan creation,
+validation, error reporting, kernel/schedule selection) behaves as documented.
+No call here enqueues device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_epilogue_02_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "gemm.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:gemm|grouped)_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert "gemm_plan_create" in names and "grouped_gemm_run" in names
+    for n in names:
+        assert hasattr(g.lib, n), n           # ctypes resolves the symbol
+        assert n in g.EXPORTED, n             # and the binding wraps it
+
+
+def test_version_and_supported_tuples():
+    assert "gfx950" in g.gemm_version()
+    tuples = [g.gemm_supported_get(i) for i in range(g.gemm_supported_count())]
+    D = g.Dtype
+    assert (D.F32, D.F32, D.F32, D.F32, D.F32) in tuples
+    assert (D.F16, D.F16, D.F16, D.F16, D.F32) in tuples
+    assert (D.BF16, D.BF16, D.BF16, D.BF16, D.F32) in tuples
+    assert (D.F8_E4M3, D.F8_E4M3, D.BF16, D.BF16, D.F32) in tuples
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_supported_get(99)
+    assert e.value.status == g.Status.INVALID_ARG
+
+
+def test_status_strings():
+    for s in g.Status:
+        assert g.gemm_status_string(s) == "GEMM_" + s.name
+
+
+def test_unsupported_tuple_is_named():
+    D, L = g.Dtype, g.Layout
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_plan_create(D.F16, D.BF16, D.F16, D.F16, D.F32, L.ROW_MAJOR, L.ROW_MAJOR,
+                           L.ROW_MAJOR, g.Epilogue.LINEAR)
+    assert e.value.status == g.Status.UNSUPPORTED
+    assert "A=F16, B=BF16" in str(e.value)
+    with pytest.raises(g.GemmError) as e:   # fp16 accumulator is not offered
+        g.gemm_plan_create(D.F16, D.F16, D.F16, D.F16, D.F16, L.ROW_MAJOR, L.ROW_MAJOR,
+                           L.ROW_MAJOR, g.Epilogue.LINEAR)
+    assert e.value.status == g.Status.UNSUPPORTED
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_plan_create_simple(D.F8_E4M3, L.ROW_MAJOR, g.Epilogue.LINEAR)
+    assert e.value.status == g.Status.UNSUPPORTED
+
+
+def test_bad_enums_and_handles():
+    D, L = g.Dtype, g.Layout
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_plan_create(D.F16, D.F16, D.F16, D.F16, D.F32, 7, L.ROW_MAJOR, L.ROW_MAJOR, 0)
+    assert e.value.status == g.Status.INVALID_ARG
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_plan_create(D.F16, D.F16, D.F16, D.F16, D.F32, 0, 0, 0, 5)
+    assert e.value.status == g.Status.INVALID_ARG
+    assert g.lib.gemm_plan_create(None, 0, 0, 0, 0, 0, 0, 0, 0, 0) == g.Status.INVALID_ARG
+    assert g.lib.gemm_plan_run(None, None, None, None, None, 1, 1, 1, 1.0, 0.0, None) == \
+        g.Status.NOT_INITIALIZED
+    assert "invalid plan" in g.gemm_last_error()
+    assert g.lib.gemm_plan_destroy(None) == g.Status.OK
+
+
+def test_create_simple_and_destroy_without_device():
+    for dt in (g.Dtype.F32, g.Dtype.F16, g.Dtype.BF16):
+        h = g.gemm_plan_create_simple(dt, g.Layout.ROW_MAJOR, g.Epilogue.RELU)
+        assert h
+        g.gemm_plan_destroy(h)
+
+
+def test_run_argument_validation_before_any_device_call():
+    h = g.gemm_plan_create_simple(g.Dtype.F16, g.Layout.ROW_MAJOR, g.Epilogue.LINEAR)
+    try:
+        run = g.lib.gemm_plan_run
+        assert run(h, 16, 16, 16, 16, -1, 4, 4, 1.0, 0.0, None) == g.Status.INVALID_ARG
+        assert "negative size" in g.gemm_last_error()
+        assert run(h, 16, 16, None, None, 4, 4, 4, 1.0, 0.0, None) == g.Status.INVALID_ARG
+        assert "D is NULL" in g.gemm_last_error()
+        assert run(h, None, 16, None, 16, 4, 4, 4, 1.0, 0.0, None) == g.Status.INVALID_ARG
+        assert run(h, 16, 16, None, 16, 4, 4, 4, 1.0, 0.5, None) == g.Status.INVALID_ARG
+        assert "C is NULL" in g.gemm_last_error()
+        # empty output: a no-op that succeeds without touching the device
+        assert run(h, None, None, None, None, 0, 8, 8, 1.0, 1.0, None) == g.Status.OK
+        assert run(h, None, None, None, None, 8, 0, 8, 1.0, 1.0, None) == g.Status.OK
+        assert g.gemm_last_error() == ""
+        # grouped: count < 0, NULL array, empty problems
+        assert g.lib.grouped_gemm_run(h, None, -1, 1.0, 0.0, None) == g.Status.INVALID_ARG
+        assert g.lib.grouped_gemm_run(h, None, 2, 1.0, 0.0, None) == g.Status.INVALID_ARG
+        assert g.lib.grouped_gemm_run(h, None, 0, 1.0, 0.0, None) == g.Status.OK
+        g.grouped_gemm_run(h, [(0, 8, 8, None, None, None, None)], 1.0, 0.0, stream=0)
+        with pytest.raises(g.GemmError) as e:
+            g.grouped_gemm_run(h, [(4, 4, 4, 16, 16, None, None)], 1.0, 0.0, stream=0)
+        assert "problem 0" in str(e.value)
+    finally:
+        g.gemm_plan_destroy(h)
+
+
+def test_set_config_validation():
+    h = g.gemm_plan_create_simple(g.Dtype.BF16, g.Layout.ROW_MAJOR, g.Epilogue.LINEAR)
+    try:
+        g.gemm_plan_set_config(h, g.Schedule.STREAM_K, g.Tile.T128x128, 64)
+        for bad in ((9, 0, 0), (0, 9, 0), (0, 0, -1)):
+            assert g.lib.gemm_plan_set_config(h, *bad) == g.Status.INVALID_ARG
+    finally:
+        g.gemm_plan_destroy(h)
+
+
+def _plan(dtype_ab, la="row", lb="col", lc="row"):
+    return g.Plan(dtype_ab, la=la, lb=lb, lc=lc)
+
+
+def test_describe_transformer_layer_schedules():
+    p = _plan("bf16")
+    # hidden 8192 / FFN 28672 layer GEMMs at 4096 tokens on 256 CUs
+    down = p.describe(4096, 8192, 28672)
+    assert down["tile"] == "256x256" and down["schedule"] == "data_parallel"
+    assert down["tiles"] == 512 and down["ipt"] == 448
+    qkv = p.describe(4096, 10240, 8192)
+    assert qkv["schedule"] == "hybrid" and qkv["tiles"] == 640 and qkv["sk_tiles"] == 128
+    gate = p.describe(4096, 57344, 8192)
+    assert gate["schedule"] == "data_parallel" and gate["tiles"] == 3584
+    p.close()
+
+
+def test_describe_small_and_skinny_use_stream_k():
+    p = g.Plan("f16", la="row", lb="row", lc="row", relu=True)
+    d = p.describe(1024, 1024, 1024)
+    assert d["tile"] == "128x128" and d["schedule"] == "stream_k" and d["ipt"] == 16
+    p.close()
+    q = _plan("f8e4m3")
+    for M, tile in ((16, "32x256"), (64, "64x256"), (128, "128x128")):
+        d = q.describe(M, 8192, 28672)
+        assert d["tile"] == tile and d["schedule"] == "stream_k", d
+        assert d["bk"] == 128
+    q.close()
+
+
+def test_describe_generic_for_unaligned_extent():
+    p = _plan("bf16")
+    d = p.describe(100, 100, 13)        # K * 2 bytes not a multiple of 16
+    assert d["kernel"] == "generic" and "multiple of 16" in d["generic_reason"]
+    d = p.describe(100, 100, 0)         # K = 0: nothing to load, tile kernel
+    assert d["kernel"] == "tile" and d["ipt"] == 0 and d["schedule"] == "data_parallel"
+    p.close()
+
+
+def test_describe_forced_configs():
+    p = _plan("bf16")
+    p.set_config(g.Schedule.STREAM_K, g.Tile.T256x256, 0)
+    d = p.describe(4096, 8192, 8192)
+    assert d["schedule"] == "stream_k" and d["tile"] == "256x256"
+    p.set_config(g.Schedule.DATA_PARALLEL, g.Tile.GENERIC, 0)
+    assert p.describe(64, 64, 64)["kernel"] == "generic"
+    p.close()

@@ -1,0 +1,340 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: bit-exact on integer-valued data; otherwise the tolerances of
+oracle.acceptance (fp32: 1e-5 S + 1e-6; fp16/bf16: 2 ulp + 2e-3 S; fp8 inputs:
+2 ulp + 1.5e-2 S). Full-size workloads are checked on sampled outputs that the
+oracle computes one by one, in the launch configuration the benchmark uses.
+"""
+import itertools
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_epilogue_02_amd as g
+import oracle
+from oracle import acceptance
+import synthetic as syn
+from gpu_util import DEV, device_operands, logical, make_out, run, scales
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+LAYOUTS = list(itertools.product(("row", "col"), repeat=3))
+S, T = g.Schedule, g.Tile
+
+
+def close(got, p, relu=False, what=""):
+    r = oracle.gemm(p, relu=relu)
+    return acceptance.check_close(got, r.ref, r.S, p.dtype_ab, p.dtype_cd, what)
+
+
+def exact(got, p, relu=False, what=""):
+    r = oracle.gemm(p, relu=relu)
+    acceptance.check_exact(got, r.d_exact, what)
+
+
+# ------------------------------------------------------------ worked examples
+
+def _golden(name):
+    kv = {}
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    return kv
+
+
+@pytest.mark.parametrize("name", ["ones_fp16_128.txt", "ones_fp16_1024.txt"])
+def test_golden_ones(name):
+    kv = _golden(name)
+    M, N, K = int(kv["M"]), int(kv["N"]), int(kv["K"])
+    p = syn.make_problem(M, N, K, dtype_ab=kv["dtype"], dtype_cd=kv["dtype"], dist_a="ones",
+                         dist_b="ones", dist_c="ones", alpha=float(kv["alpha"]),
+                         beta=float(kv["beta"]))
+    got = run(p)
+    assert (got == float(kv["expect_all"])).all()
+
+
+# ------------------------------------------------------------ the workloads
+
+@pytest.mark.parametrize("sched", [S.AUTO, S.DATA_PARALLEL, S.STREAM_K])
+def test_config1_fp32_small(sched):
+    p = syn.config1()
+    close(run(p, schedule=sched), p, what=f"fp32 128x64x256 {sched.name}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_config1_ones_closed_form(dtype):
+    p = syn.config1_ones(1024, dtype)
+    got = run(p)
+    want = oracle.decode(dtype, oracle.encode(dtype, [1025.0]))[0]   # bf16: 1024
+    assert (got == want).all()
+
+
+def test_config2_fp16_relu_full():
+    p = syn.config2()
+    got = run(p, relu=True)
+    assert (got >= 0).all()
+    close(got, p, relu=True, what="fp16 1024^3 relu")
+
+
+@pytest.mark.parametrize("sched", [S.AUTO, S.DATA_PARALLEL, S.STREAM_K])
+def test_config2_schedules(sched):
+    p = syn.config2(n=512)
+    close(run(p, relu=True, schedule=sched), p, relu=True, what=f"fp16 512^3 {sched.name}")
+
+
+def _sample(M, N, n, seed):
+    rng = np.random.default_rng(seed)
+    ii = rng.integers(0, M, n)
+    jj = rng.integers(0, N, n)
+    # always include the four corners (first/last tiles, ragged edges)
+    ii = np.concatenate([ii, [0, 0, M - 1, M - 1]])
+    jj = np.concatenate([jj, [0, N - 1, 0, N - 1]])
+    return ii, jj
+
+
+@pytest.mark.parametrize("name", ["qkv", "o", "down", "gate_up"])
+def test_config4_layer_gemm_sampled(name):
+    p = syn.config4(name)
+    got = run(p)
+    assert np.isfinite(got).all()
+    ii, jj = _sample(p.M, p.N, 256, 1)
+    r = oracle.gemm_entries(p, ii, jj)
+    acceptance.check_close(got[ii, jj], r.ref, r.S, "bf16", "bf16", f"layer {name}")
+
+
+def test_config4_row_major_b_sampled():
+    p = syn.config4("o", lb="row")
+    got = run(p)
+    ii, jj = _sample(p.M, p.N, 256, 2)
+    r = oracle.gemm_entries(p, ii, jj)
+    acceptance.check_close(got[ii, jj], r.ref, r.S, "bf16", "bf16", "layer o, RowMajor B")
+
+
+@pytest.mark.parametrize("M", syn.DECODE_MS)
+@pytest.mark.parametrize("NK", syn.DECODE_NK)
+def test_config5_fp8_sampled(M, NK):
+    N, K = NK
+    p = syn.config5(M, N, K)
+    got = run(p)
+    assert np.isfinite(got).all()
+    ii, jj = _sample(M, N, 256, 3)
+    r = oracle.gemm_entries(p, ii, jj)
+    acceptance.check_close(got[ii, jj], r.ref, r.S, "f8e4m3", "bf16", f"fp8 {M}x{N}x{K}")
+
+
+def test_config5_fp8_small_full():
+    p = syn.config5(64, 1024, 2048, seed=4)
+    close(run(p), p, what="fp8 64x1024x2048")
+
+
+# ------------------------------------------------------------ bit-exact sweeps
+
+FAMS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("f8e4m3", "bf16")]
+TILES = [T.T256x256, T.T128x128, T.T64x256, T.T32x256, T.GENERIC]
+
+
+def _int_problem(dab, dcd, la, lb, lc, M=304, N=272, K=208, seed=0, beta=1.0):
+    # |sum| must stay exact in the output type: bf16 holds integers to 256
+    lo, hi = (-1, 1) if dcd == "bf16" else (-2, 2)
+    return syn.integer_problem(M, N, K, dtype_ab=dab, dtype_cd=dcd, la=la, lb=lb, lc=lc,
+                               lo=lo, hi=hi, beta=beta, seed=seed)
+
+
+@pytest.mark.parametrize("dab,dcd", FAMS)
+@pytest.mark.parametrize("la,lb,lc", LAYOUTS)
+@pytest.mark.parametrize("tile", TILES)
+def test_integer_exact_all_layouts_tiles(dab, dcd, la, lb, lc, tile):
+    p = _int_problem(dab, dcd, la, lb, lc)
+    exact(run(p, tile=tile, schedule=S.DATA_PARALLEL), p,
+          what=f"{dab} {la}{lb}{lc} {tile.name}")
+
+
+@pytest.mark.parametrize("dab,dcd", FAMS)
+@pytest.mark.parametrize("sched", [S.STREAM_K, S.HYBRID])
+@pytest.mark.parametrize("tile", [T.T256x256, T.T128x128, T.T32x256])
+@pytest.mark.parametrize("relu", [False, True])
+def test_integer_exact_stream_k(dab, dcd, sched, tile, relu):
+    p = _int_problem(dab, dcd, "row", "col", "row", M=544, N=528, K=1024, seed=5)
+    got = run(p, relu=relu, tile=tile, schedule=sched, sk_grid=37 if sched == S.STREAM_K else 16)
+    exact(got, p, relu=relu, what=f"{dab} {sched.name} {tile.name}")
+
+
+@pytest.mark.parametrize("dab,dcd", FAMS)
+@pytest.mark.parametrize("la,lb,lc", [("row", "row", "row"), ("col", "col", "col"),
+                                      ("row", "col", "row"), ("col", "row", "col")])
+def test_random_tolerance(dab, dcd, la, lb, lc):
+    p = syn.make_problem(336, 400, 520, dtype_ab=dab, dtype_cd=dcd, la=la, lb=lb, lc=lc,
+                         dist_c="normal", alpha=0.75, beta=-0.5, seed=7)
+    for sched in (S.DATA_PARALLEL, S.STREAM_K):
+        close(run(p, relu=True, schedule=sched), p, relu=True, what=f"{dab} {la}{lb}{lc}")
+
+
+# ------------------------------------------------------------ stream-K
+
+def test_stream_k_deterministic_and_equivalent():
+    p = syn.make_problem(512, 512, 4096, dtype_ab="bf16", dtype_cd="bf16", lb="col", seed=8)
+    dp = run(p, schedule=S.DATA_PARALLEL, tile=T.T128x128)
+    for grid in (7, 64, 256):
+        a = run(p, schedule=S.STREAM_K, tile=T.T128x128, sk_grid=grid)
+        b = run(p, schedule=S.STREAM_K, tile=T.T128x128, sk_grid=grid)
+        assert np.array_equal(a, b), f"stream-K grid {grid} not bitwise repeatable"
+        close(a, p, what=f"stream-K grid {grid}")
+    close(dp, p, what="data-parallel")
+
+
+def test_stream_k_matches_dp_on_integers():
+    p = _int_problem("bf16", "bf16", "row", "col", "row", M=256, N=256, K=2048, seed=9)
+    dp = run(p, schedule=S.DATA_PARALLEL, tile=T.T128x128)
+    sk = run(p, schedule=S.STREAM_K, tile=T.T128x128, sk_grid=100)
+    assert np.array_equal(dp, sk)
+    exact(sk, p)
+
+
+def test_plan_reuse_across_shapes_and_workspace_growth():
+    plan = g.Plan("bf16", la="row", lb="col", lc="row")
+    for (M, N, K) in ((64, 64, 256), (512, 512, 2048), (1000, 776, 1032), (128, 256, 64)):
+        p = syn.make_problem(M, N, K, dtype_ab="bf16", dtype_cd="bf16", lb="col", seed=M)
+        close(run(p, plan=plan, schedule=S.STREAM_K), p, what=f"reuse {M}x{N}x{K}")
+    plan.close()
+
+
+# ------------------------------------------------------------ grouped
+
+def _grouped_run(plan, probs, alpha=1.0, beta=0.0):
+    ops, outs, problems = [], [], []
+    for p in probs:
+        A, B, C = device_operands(p)
+        buf, D = make_out(p)
+        ops.append((A, B, C, buf))
+        outs.append(D)
+        problems.append((p.M, p.N, p.K, A, B, C, D))
+    print(f"[gpu] grouped {len(probs)} problems", flush=True)
+    plan.run_grouped(problems, alpha, beta)
+    torch.cuda.synchronize()
+    return [logical(D, p) for D, p in zip(outs, probs)]
+
+
+def test_grouped_small_full_oracle():
+    shapes = [(32, 128, 128), (96, 256, 512), (160, 512, 256), (544, 128, 1024),
+              (64, 1024, 128), (2048, 256, 256), (0, 128, 128), (224, 128, 0)]
+    probs = syn.config3(seed=11, shapes=shapes)
+    plan = g.Plan("f16", la="row", lb="row", lc="row")
+    outs = _grouped_run(plan, probs)
+    for p, got in zip(probs, outs):
+        close(got, p, what=f"grouped {p.M}x{p.N}x{p.K}")
+    plan.close()
+
+
+def test_grouped_config3_sampled_rows():
+    probs = syn.config3()
+    plan = g.Plan("f16", la="row", lb="row", lc="row")
+    outs = _grouped_run(plan, probs)
+    for p, got in zip(probs, outs):
+        rows = [0, p.M // 2, p.M - 1]
+        r = oracle.gemm(p, rows=rows)
+        acceptance.check_close(got[rows], r.ref, r.S, "f16", "f16", f"grouped {p.M}x{p.N}x{p.K}")
+    plan.close()
+
+
+def test_grouped_equals_loop_of_singles_bitwise():
+    probs = syn.config3(seed=12, count=10)
+    plan = g.Plan("f16", la="row", lb="row", lc="row", relu=True)
+    outs = _grouped_run(plan, probs)
+    for p, got in zip(probs, outs):
+        single = run(p, relu=True, schedule=S.DATA_PARALLEL, tile=T.T128x128)
+        assert np.array_equal(got, single), f"grouped != single for {p.M}x{p.N}x{p.K}"
+    plan.close()
+
+
+def test_grouped_integer_exact_mixed_alignment():
+    shapes = [(128, 128, 64), (40, 72, 24), (256, 136, 96), (33, 17, 9)]
+    probs = [_int_problem("bf16", "bf16", "row", "row", "row", M=m, N=n, K=k, seed=i)
+             for i, (m, n, k) in enumerate(shapes)]
+    plan = g.Plan("bf16", la="row", lb="row", lc="row")
+    outs = _grouped_run(plan, probs, beta=1.0)
+    for p, got in zip(probs, outs):
+        exact(got, p, what=f"grouped int {p.M}x{p.N}x{p.K}")
+    plan.close()
+
+
+# ------------------------------------------------------------ edge cases
+
+def test_k_zero_gives_beta_c():
+    p = syn.make_problem(100, 60, 0, dtype_ab="bf16", dtype_cd="bf16", dist_c="normal",
+                         beta=2.0, seed=13)
+    exact(run(p, relu=True), p, relu=True)
+
+
+def test_empty_outputs_are_no_ops():
+    for (M, N) in ((0, 16), (16, 0)):
+        plan = g.Plan("f16")
+        plan.run(None, None, None, None, M, N, 8)
+        plan.close()
+
+
+def test_in_place_d_equals_c():
+    p = syn.make_problem(200, 152, 96, dtype_ab="f16", dtype_cd="f16", dist_c="normal",
+                         beta=1.0, seed=14)
+    close(run(p, in_place=True), p, what="in place")
+
+
+def test_beta_zero_ignores_nan_c():
+    p = syn.make_problem(128, 128, 64, dtype_ab="bf16", dtype_cd="bf16", dist_c="normal",
+                         beta=0.0, seed=15)
+    p.C = torch.full_like(p.C, float("nan"))
+    got = run(p)
+    assert np.isfinite(got).all()
+    close(got, p)
+
+
+def test_misaligned_operand_uses_generic_and_matches():
+    p = syn.make_problem(96, 80, 64, dtype_ab="bf16", dtype_cd="bf16", dist_c="normal",
+                         beta=1.0, seed=16)
+    A, B, C = device_operands(p)
+    A2 = torch.empty(p.M * p.K + 1, dtype=A.dtype, device=DEV)
+    A2[1:] = A.reshape(-1)
+    Ash = A2[1:]                         # 2-byte aligned base
+    plan = g.Plan("bf16")
+    assert plan.describe(p.M, p.N, p.K)["kernel"] == "tile"
+    got = run(p, plan=plan, operands=(Ash, B, C))
+    close(got, p, what="misaligned A")
+    plan.close()
+
+
+@pytest.mark.parametrize("dab,dcd", FAMS)
+def test_odd_sizes_generic(dab, dcd):
+    p = _int_problem(dab, dcd, "row", "row", "row", M=37, N=29, K=13, seed=17)
+    exact(run(p), p)
+
+
+def test_alpha_two_doubles_bitwise_and_relu_fusion():
+    p = syn.make_problem(256, 256, 512, dtype_ab="bf16", dtype_cd="bf16", dist_c="normal",
+                         beta=1.0, seed=18)
+    lin = run(p, schedule=S.DATA_PARALLEL, tile=T.T128x128)
+    fused = run(p, relu=True, schedule=S.DATA_PARALLEL, tile=T.T128x128)
+    assert np.array_equal(fused, np.maximum(lin, 0.0))
+    p.alpha, p.beta = 2.0, 2.0
+    dbl = run(p, schedule=S.DATA_PARALLEL, tile=T.T128x128)
+    assert np.array_equal(dbl, 2.0 * lin)
+
+
+def test_large_k_beyond_32bit_tile_span_uses_generic():
+    K = (1 << 25) + 64
+    p = syn.make_problem(2, 8, K, dtype_ab="bf16", dtype_cd="bf16", lb="col", seed=19)
+    plan = g.Plan("bf16", lb="col")
+    d = plan.describe(p.M, p.N, p.K)
+    assert d["kernel"] == "generic" and "32-bit" in d["generic_reason"]
+    close(run(p, plan=plan), p, what="K = 2^25 + 64")
+    plan.close()
+
+
+def test_fp8_scales_read_on_device():
+    p = syn.integer_problem(64, 256, 256, dtype_ab="f8e4m3", dtype_cd="bf16", with_c=False,
+                            lo=-1, hi=1, seed=20)
+    p.scale_a, p.scale_b = 0.5, 0.25
+    exact(run(p), p)
