@@ -290,7 +290,8 @@ template <int R, int ESZ, bool KC, int NT> struct Stager {
 // lanes x 16 bytes into 1 KiB of consecutive LDS, lane i landing at slot
 // base + i; lane i therefore fetches the logical chunk that the swizzle puts
 // in that slot. Out-of-range lanes use an offset past num_records and write
-// zeros.
+// zeros. The per-lane byte offsets do not depend on k: they are computed once
+// per output tile, and each k-tile only advances the (scalar) base address.
 template <int R, int ESZ, int NT> struct DirectStager {
     static constexpr int VEC = 16 / ESZ;
     static constexpr int WAVES = NT / 64;
@@ -298,19 +299,43 @@ template <int R, int ESZ, int NT> struct DirectStager {
     static constexpr int IPW = INSTR / WAVES;      // instructions per wave
     static_assert(INSTR % WAVES == 0, "rows per tile must cover all waves");
 
-    static __device__ __forceinline__ void issue(const char *base, uint32_t ld_bytes, int r_left,
-                                                 int k_left, char *lds, int tid) {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+    const char *base;        // operand element (r0, k = 0), wave-uniform
+    uint32_t ld;             // bytes between rows
+    uint32_t voff[IPW];      // per-lane offsets (OOB_OFFSET for rows past the edge)
+
+    __device__ __forceinline__ void init(const char *tile_base, uint32_t ld_bytes, int r_left,
+                                         int tid) {
+        base = static_cast<const char *>(uniform_ptr(tile_base));
+        ld = ld_bytes;
         const int lane = tid & 63, wave = uniform(tid >> 6);
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
-            const int instr = wave * IPW + i;
-            const int row = instr * 8 + (lane >> 3);
+            const int row = (wave * IPW + i) * 8 + (lane >> 3);
             const int c = (lane & 7) ^ swz(row);
-            const bool ok = row < r_left && c * VEC < k_left;
-            const uint32_t off = ok ? row * ld_bytes + (uint32_t)(c << 4) : OOB_OFFSET;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (__attribute__((address_space(3))) void *)(lds + instr * 1024), 16, off, 0, 0, 0);
+            voff[i] = row < r_left ? row * ld_bytes + (uint32_t)(c << 4) : OOB_OFFSET;
+        }
+    }
+
+    // Copy k-tile kt (k_left valid elements from its start) into `lds`.
+    __device__ __forceinline__ void issue(int kt, int k_left, char *lds, int tid) const {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (size_t)kt * KTILE_BYTES);
+        const int wave = uniform(tid >> 6);
+        if (k_left >= 8 * VEC) {
+#pragma unroll
+            for (int i = 0; i < IPW; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void *)(lds + (wave * IPW + i) * 1024), 16,
+                    voff[i], 0, 0, 0);
+        } else {   // ragged K tail: drop the chunks past K
+            const int lane = tid & 63;
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                const int row = (wave * IPW + i) * 8 + (lane >> 3);
+                const int c = (lane & 7) ^ swz(row);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void *)(lds + (wave * IPW + i) * 1024), 16,
+                    c * VEC < k_left ? voff[i] : OOB_OFFSET, 0, 0, 0);
+            }
         }
     }
 };
@@ -383,25 +408,54 @@ struct Tile {
         k_left = (int)imin64(p.K - k0, BK);
     }
 
-    // Start the copy of k-tile kt: direct operands are issued into `stage`,
-    // transposed operands are fetched into registers (stored by store_regs).
-    static __device__ __forceinline__ void issue_stage(const Prob &p, int tm, int tn, int kt,
-                                                       char *stage, SA &sa, SB &sb, int tid) {
+    // Per-work-unit copy state: direct stagers for K-contiguous operands,
+    // register stagers (with in-register transpose) for the others.
+    struct Loader {
+        DA da;
+        DB db;
+        SA sa;
+        SB sb;
+    };
+
+    static __device__ __forceinline__ void loader_init(const Prob &p, int tm, int tn, Loader &L,
+                                                       int tid) {
         const char *base;
         uint32_t ld;
         int rl, kl;
-        a_tile(p, tm, kt, base, ld, rl, kl);
-        if constexpr (A_KC) DA::issue(base, ld, rl, kl, stage, tid);
-        else sa.load(base, ld, rl, kl, tid);
-        b_tile(p, tn, kt, base, ld, rl, kl);
-        if constexpr (B_KC) DB::issue(base, ld, rl, kl, stage + A_BYTES, tid);
-        else sb.load(base, ld, rl, kl, tid);
+        if constexpr (A_KC) {
+            a_tile(p, tm, 0, base, ld, rl, kl);
+            L.da.init(base, ld, rl, tid);
+        }
+        if constexpr (B_KC) {
+            b_tile(p, tn, 0, base, ld, rl, kl);
+            L.db.init(base, ld, rl, tid);
+        }
     }
 
-    static __device__ __forceinline__ void store_regs(char *stage, const SA &sa, const SB &sb,
-                                                      int tid) {
-        if constexpr (!A_KC) sa.store(stage, tid);
-        if constexpr (!B_KC) sb.store(stage + A_BYTES, tid);
+    // Start the copy of k-tile kt: direct operands are issued into `stage`,
+    // transposed operands are fetched into registers (stored by store_regs).
+    static __device__ __forceinline__ void issue_stage(const Prob &p, int tm, int tn, int kt,
+                                                       int k_left, char *stage, Loader &L, int tid) {
+        const char *base;
+        uint32_t ld;
+        int rl, kl;
+        if constexpr (A_KC) {
+            L.da.issue(kt, k_left, stage, tid);
+        } else {
+            a_tile(p, tm, kt, base, ld, rl, kl);
+            L.sa.load(base, ld, rl, kl, tid);
+        }
+        if constexpr (B_KC) {
+            L.db.issue(kt, k_left, stage + A_BYTES, tid);
+        } else {
+            b_tile(p, tn, kt, base, ld, rl, kl);
+            L.sb.load(base, ld, rl, kl, tid);
+        }
+    }
+
+    static __device__ __forceinline__ void store_regs(char *stage, const Loader &L, int tid) {
+        if constexpr (!A_KC) L.sa.store(stage, tid);
+        if constexpr (!B_KC) L.sb.store(stage + A_BYTES, tid);
     }
 
     // Multiply one LDS stage into the accumulators.
@@ -440,25 +494,29 @@ struct Tile {
     // Per k-tile: wait for this wave's copies of tile kt, barrier (every
     // wave's copies of kt are in LDS and every wave has finished reading the
     // other stage), start the copy of kt+1 into the other stage, multiply kt.
-    static __device__ __forceinline__ void mainloop(const Prob &p, int tm, int tn, int kt0, int kt1,
+    static __device__ __forceinline__ void mainloop(const Prob &p, int tm, int tn, int kt0_, int kt1_,
                                                     Acc &acc, char *lds) {
         const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
         const int wm = wave / WN, wn = wave % WN;
+        const int kt0 = uniform(kt0_), kt1 = uniform(kt1_);
         zero(acc);
         if (kt0 >= kt1) return;
-        SA sa;
-        SB sb;
-        issue_stage(p, tm, tn, kt0, lds, sa, sb, tid);
-        store_regs(lds, sa, sb, tid);
+        // valid k of the last k-tile of K (the only one that can be partial)
+        const int last = uniform(p.ipt) - 1;
+        const int k_tail = uniform((int)(p.K - (int64_t)last * BK));
+        Loader L;
+        loader_init(p, tm, tn, L, tid);
+        issue_stage(p, tm, tn, kt0, kt0 == last ? k_tail : BK, lds, L, tid);
+        store_regs(lds, L, tid);
         for (int kt = kt0; kt < kt1; ++kt) {
-            char *cur = lds + ((kt - kt0) & 1) * STAGE_BYTES;
-            char *nxt = lds + (((kt - kt0) & 1) ^ 1) * STAGE_BYTES;
-            const bool more = kt + 1 < kt1;
+            const int par = (kt - kt0) & 1;
+            char *cur = lds + par * STAGE_BYTES;
+            char *nxt = lds + (par ^ 1) * STAGE_BYTES;
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of kt landed
             __syncthreads();
-            if (more) issue_stage(p, tm, tn, kt + 1, nxt, sa, sb, tid);
+            if (kt + 1 < kt1) issue_stage(p, tm, tn, kt + 1, kt + 1 == last ? k_tail : BK, nxt, L, tid);
             compute(cur, cur + A_BYTES, acc, lane, wm, wn);
-            if (more) store_regs(nxt, sa, sb, tid);
+            if (kt + 1 < kt1) store_regs(nxt, L, tid);
         }
         __syncthreads();
     }
