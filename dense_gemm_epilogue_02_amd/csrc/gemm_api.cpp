@@ -185,14 +185,15 @@ struct Decision {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Vector (16-byte buffer-load) eligibility of one operand for a tile kernel.
-const char *operand_vec_problem(const void *ptr, bool kc, int64_t contig, int64_t rows, int esz) {
+// rows: tile rows of this operand; kbytes: bytes of K per k-tile row.
+const char *operand_vec_problem(const void *ptr, bool kc, int64_t contig, int64_t rows, int esz,
+                                int kbytes) {
     const int vec = 16 / esz;
     if (reinterpret_cast<uintptr_t>(ptr) % 16) return "operand base not 16-byte aligned";
     if (contig % vec) return "contiguous extent not a multiple of 16 bytes";
     // largest in-tile byte offset must stay below the 31-bit buffer range
-    const int64_t span = kc ? rows * contig * esz : (int64_t)KTILE_BYTES * contig;
+    const int64_t span = kc ? rows * contig * esz : (int64_t)kbytes * contig;
     if (span + 16 > 0x7FFFFFFFLL) return "operand row stride too large for 32-bit offsets";
-    (void)rows;
     return nullptr;
 }
 
@@ -251,8 +252,9 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
         if (!e) e = registry().find(fam, a_kc, b_kc, TILE_128x128);
         const char *why = nullptr;
         if (K > 0) {
-            why = operand_vec_problem(A, a_kc, a_kc ? K : M, e ? e->bm : 0, esz);
-            if (!why) why = operand_vec_problem(B, b_kc, b_kc ? K : N, e ? e->bn : 0, esz);
+            const int kb = e ? e->bk * esz : 128;
+            why = operand_vec_problem(A, a_kc, a_kc ? K : M, e ? e->bm : 0, esz, kb);
+            if (!why) why = operand_vec_problem(B, b_kc, b_kc ? K : N, e ? e->bn : 0, esz, kb);
         }
         if (e && !why) d.e = e;
         else d.why_generic = why ? why : "no tile kernel for this layout";
@@ -604,8 +606,8 @@ gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32
         const void *C = beta == 0.0f ? nullptr : q.C;
         const char *why = (e && e->fn_grouped && pl->tile != GEMM_TILE_GENERIC) ? nullptr : "no grouped kernel";
         if (!why && q.K > 0) {
-            why = operand_vec_problem(q.A, a_kc, a_kc ? q.K : q.M, e->bm, esz);
-            if (!why) why = operand_vec_problem(q.B, b_kc, b_kc ? q.K : q.N, e->bn, esz);
+            why = operand_vec_problem(q.A, a_kc, a_kc ? q.K : q.M, e->bm, esz, e->bk * esz);
+            if (!why) why = operand_vec_problem(q.B, b_kc, b_kc ? q.K : q.N, e->bn, esz, e->bk * esz);
         }
         if (why) {
             scalar_path.push_back(i);

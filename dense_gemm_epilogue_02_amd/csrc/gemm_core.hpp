@@ -8,8 +8,8 @@
 // 5.2 (activation applied after the linear combination).
 //
 // Design (CDNA4 / gfx950):
-//   * A workgroup owns a BM x BN output tile. K is walked in k-tiles of 128
-//     bytes per row (64 bf16/f16, 128 fp8, 32 fp32 elements).
+//   * A workgroup owns a BM x BN output tile. K is walked in k-tiles of KB
+//     bytes per row (KB = 128: 64 bf16/f16, 128 fp8, 32 fp32 elements).
 //   * Both operand tiles live in LDS "K-contiguous": row r (an m of A or an n
 //     of B) holds the k-tile's 128 bytes as eight 16-byte chunks. Chunk c of
 //     row r is stored at chunk slot c ^ swz(r), swz(r) = (r ^ (r >> 3)) & 7,
@@ -46,7 +46,6 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 enum Family { FAM_F32 = 0, FAM_F16 = 1, FAM_BF16 = 2, FAM_F8 = 3 };
 
-constexpr int KTILE_BYTES = 128;      // bytes of K per LDS row per k-tile
 constexpr uint32_t OOB_OFFSET = 0x80000000u;
 constexpr int NUM_RECORDS = 0x7FFFFFFF;
 constexpr int RSRC_FLAGS = 0x00020000;   // gfx9 raw buffer, 32-bit data format
@@ -179,10 +178,29 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// LDS rows hold CH 16-byte chunks (CH = 8: 128-byte rows, CH = 4: 64-byte
+// rows). Chunk c of row r lives at slot c ^ swz<CH>(r); the XOR keeps the
+// 16 lanes that read rows r..r+15 at one chunk index on distinct banks.
+template <int CH> __device__ __forceinline__ int swz(int row);
+template <> __device__ __forceinline__ int swz<8>(int row) { return (row ^ (row >> 3)) & 7; }
+template <> __device__ __forceinline__ int swz<4>(int row) { return ((row >> 2) ^ (row >> 4)) & 3; }
 
-__device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
-    return (uint32_t)(row * KTILE_BYTES + ((chunk ^ swz(row)) << 4));
+template <int CH> __device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
+    return (uint32_t)(row * CH * 16 + ((chunk ^ swz<CH>(row)) << 4));
+}
+
+// Workgroup barrier without the release fence of __syncthreads(): the fence
+// would wait for every outstanding vector load (vmcnt(0)), draining the
+// LDS-DMA copies that a deep pipeline keeps in flight. Callers wait for the
+// copies they need with wait_vmcnt<n>() first (LDS-DMA completion is counted
+// by vmcnt); the memory clobber keeps the compiler from moving LDS accesses
+// across the barrier.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
 // In-register transpose of a VEC x VEC block of ESZ-byte elements held as
@@ -228,9 +246,9 @@ template <> struct Transpose<1> {
 
 // Global -> register -> LDS copy of one operand k-tile with R rows.
 // KC: the operand's contiguous dimension is K (A RowMajor, B ColumnMajor).
-template <int R, int ESZ, bool KC, int NT> struct Stager {
+template <int R, int ESZ, bool KC, int NT, int CH> struct Stager {
     static constexpr int VEC = 16 / ESZ;
-    static constexpr int UNITS = KC ? R * 8 : (R / VEC) * 8;
+    static constexpr int UNITS = KC ? R * CH : (R / VEC) * CH;
     static constexpr int LPU = KC ? 1 : VEC;           // loads per unit
     static constexpr int UPT = (UNITS + NT - 1) / NT;  // units per thread
     static constexpr bool FULL = (UNITS % NT) == 0;
@@ -247,7 +265,7 @@ template <int R, int ESZ, bool KC, int NT> struct Stager {
             const int unit = tid + u * NT;
             const bool act = FULL || unit < UNITS;
             if constexpr (KC) {
-                const int row = unit >> 3, c = unit & 7;
+                const int row = unit / CH, c = unit % CH;
                 const bool ok = act && row < r_left && c * VEC < k_left;
                 r[u] = buf_load16(rs, ok ? row * ld_bytes + (uint32_t)(c << 4) : OOB_OFFSET);
             } else {
@@ -271,7 +289,7 @@ template <int R, int ESZ, bool KC, int NT> struct Stager {
             const int unit = tid + u * NT;
             if (!FULL && unit >= UNITS) continue;
             if constexpr (KC) {
-                *reinterpret_cast<u32x4 *>(lds + lds_off(unit >> 3, unit & 7)) = r[u];
+                *reinterpret_cast<u32x4 *>(lds + lds_off<CH>(unit / CH, unit % CH)) = r[u];
             } else {
                 constexpr int RB = R / VEC;
                 const int rb = unit % RB, kb = unit / RB;
@@ -279,7 +297,7 @@ template <int R, int ESZ, bool KC, int NT> struct Stager {
                 Transpose<ESZ>::run(&r[u * VEC], t);
 #pragma unroll
                 for (int j = 0; j < VEC; ++j)
-                    *reinterpret_cast<u32x4 *>(lds + lds_off(rb * VEC + j, kb)) = t[j];
+                    *reinterpret_cast<u32x4 *>(lds + lds_off<CH>(rb * VEC + j, kb)) = t[j];
             }
         }
     }
@@ -292,10 +310,11 @@ template <int R, int ESZ, bool KC, int NT> struct Stager {
 // in that slot. Out-of-range lanes use an offset past num_records and write
 // zeros. The per-lane byte offsets do not depend on k: they are computed once
 // per output tile, and each k-tile only advances the (scalar) base address.
-template <int R, int ESZ, int NT> struct DirectStager {
+template <int R, int ESZ, int NT, int CH> struct DirectStager {
     static constexpr int VEC = 16 / ESZ;
     static constexpr int WAVES = NT / 64;
-    static constexpr int INSTR = R / 8;            // 8 rows x 8 chunks each
+    static constexpr int RPI = 64 / CH;            // rows per instruction
+    static constexpr int INSTR = R / RPI;
     static constexpr int IPW = INSTR / WAVES;      // instructions per wave
     static_assert(INSTR % WAVES == 0, "rows per tile must cover all waves");
 
@@ -310,17 +329,29 @@ template <int R, int ESZ, int NT> struct DirectStager {
         const int lane = tid & 63, wave = uniform(tid >> 6);
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
-            const int row = (wave * IPW + i) * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ swz(row);
+            const int row = (wave * IPW + i) * RPI + lane / CH;
+            const int c = (lane % CH) ^ swz<CH>(row);
             voff[i] = row < r_left ? row * ld_bytes + (uint32_t)(c << 4) : OOB_OFFSET;
         }
     }
 
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int kt) const {
+        return make_rsrc(base + (size_t)kt * (CH * 16));
+    }
+
+    // Instruction i of this wave for a full k-tile (no K tail).
+    __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int i, char *lds,
+                                              int wave) const {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void *)(lds + (wave * IPW + i) * 1024), 16, voff[i],
+            0, 0, 0);
+    }
+
     // Copy k-tile kt (k_left valid elements from its start) into `lds`.
     __device__ __forceinline__ void issue(int kt, int k_left, char *lds, int tid) const {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (size_t)kt * KTILE_BYTES);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (size_t)kt * (CH * 16));
         const int wave = uniform(tid >> 6);
-        if (k_left >= 8 * VEC) {
+        if (k_left >= CH * VEC) {
 #pragma unroll
             for (int i = 0; i < IPW; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -330,8 +361,8 @@ template <int R, int ESZ, int NT> struct DirectStager {
             const int lane = tid & 63;
 #pragma unroll
             for (int i = 0; i < IPW; ++i) {
-                const int row = (wave * IPW + i) * 8 + (lane >> 3);
-                const int c = (lane & 7) ^ swz(row);
+                const int row = (wave * IPW + i) * RPI + lane / CH;
+                const int c = (lane % CH) ^ swz<CH>(row);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rs, (__attribute__((address_space(3))) void *)(lds + (wave * IPW + i) * 1024), 16,
                     c * VEC < k_left ? voff[i] : OOB_OFFSET, 0, 0, 0);
@@ -342,30 +373,49 @@ template <int R, int ESZ, int NT> struct DirectStager {
 
 // ---------------------------------------------------------------- tile engine
 
-template <int FAM_, bool A_KC, bool B_KC, int BM_, int BN_, int WM_, int WN_>
+// KB: bytes of K per LDS row per k-tile (128 or 64); STAGES: LDS stages
+// (more than 2 only when both operands are K-contiguous).
+// PIPE: 0 = fragment reads scheduled by the compiler; 3 = the fragments of
+// substep s+1 are read (as one burst) before the MFMAs of substep s, with
+// scheduling fences; 4 = as 3, with the k-loop unrolled over the LDS stages
+// (all LDS offsets become immediates) and the barrier placed before the last
+// substep of each k-tile, so the next k-tile's first fragments are read while
+// that substep's MFMAs run (needs STAGES >= 3 and direct loads); 5 = as 3,
+// with the next k-tile's LDS-DMA instructions spread through the MFMA
+// stream (one after every few MFMAs) instead of issued as one burst, which
+// would stall every wave's MFMA issue behind the CU's memory queue.
+template <int FAM_, bool A_KC, bool B_KC, int BM_, int BN_, int WM_, int WN_, int KB = 128,
+          int STAGES = 2, int PIPE = 0>
 struct Tile {
     static constexpr int FAM = FAM_, BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int CH = KB / 16;
     using F = Fam<FAM>;
     using Out = typename F::Out;
     static constexpr int ESZ = F::ESZ, CPL = F::CPL;
     static constexpr int NT = 64 * WM * WN;
     static constexpr int VEC = 16 / ESZ;            // elements per 16-byte chunk
-    static constexpr int BK = KTILE_BYTES / ESZ;    // elements of K per k-tile
+    static constexpr int BK = KB / ESZ;             // elements of K per k-tile
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
-    static constexpr int SUBSTEPS = 8 / (2 * CPL);
-    static constexpr int A_BYTES = BM * KTILE_BYTES, B_BYTES = BN * KTILE_BYTES;
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static constexpr int SUBSTEPS = CH / (2 * CPL);
+    // LDS: [A stage 0 .. A stage S-1 | B stage 0 .. B stage S-1]
+    static constexpr int A_BYTES = BM * KB, B_BYTES = BN * KB;
+    static constexpr int B_OFF = STAGES * A_BYTES;
+    static constexpr int LDS_BYTES = STAGES * (A_BYTES + B_BYTES);
+    static_assert(CH == 8 || CH == 4, "64- or 128-byte LDS rows");
+    static_assert(STAGES == 2 || (A_KC && B_KC), "deep pipelines need direct loads");
+    static_assert(PIPE != 4 || (STAGES >= 3 && SUBSTEPS % 2 == 0 && A_KC && B_KC),
+                  "cross-tile fragment prefetch");
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
     // K-contiguous operands go straight to LDS; the others are staged through
     // registers and transposed.
-    using SA = Stager<BM, ESZ, false, NT>;
-    using SB = Stager<BN, ESZ, false, NT>;
-    using DA = DirectStager<BM, ESZ, NT>;
-    using DB = DirectStager<BN, ESZ, NT>;
+    using SA = Stager<BM, ESZ, false, NT, CH>;
+    using SB = Stager<BN, ESZ, false, NT, CH>;
+    using DA = DirectStager<BM, ESZ, NT, CH>;
+    using DB = DirectStager<BN, ESZ, NT, CH>;
+    static constexpr int LPS = DA::IPW + DB::IPW;   // direct loads per stage per wave
 
     struct Acc {
         f32x16 v[FN][FM];
@@ -435,7 +485,9 @@ struct Tile {
     // Start the copy of k-tile kt: direct operands are issued into `stage`,
     // transposed operands are fetched into registers (stored by store_regs).
     static __device__ __forceinline__ void issue_stage(const Prob &p, int tm, int tn, int kt,
-                                                       int k_left, char *stage, Loader &L, int tid) {
+                                                       int k_left, char *lds, int st, Loader &L,
+                                                       int tid) {
+        char *stage = lds + st * A_BYTES;   // A of stage st; B of stage st at B_OFF + st * B_BYTES
         const char *base;
         uint32_t ld;
         int rl, kl;
@@ -446,16 +498,124 @@ struct Tile {
             L.sa.load(base, ld, rl, kl, tid);
         }
         if constexpr (B_KC) {
-            L.db.issue(kt, k_left, stage + A_BYTES, tid);
+            L.db.issue(kt, k_left, lds + B_OFF + st * B_BYTES, tid);
         } else {
             b_tile(p, tn, kt, base, ld, rl, kl);
             L.sb.load(base, ld, rl, kl, tid);
         }
     }
 
-    static __device__ __forceinline__ void store_regs(char *stage, const Loader &L, int tid) {
-        if constexpr (!A_KC) L.sa.store(stage, tid);
-        if constexpr (!B_KC) L.sb.store(stage + A_BYTES, tid);
+    static __device__ __forceinline__ void store_regs(char *lds, int st, const Loader &L, int tid) {
+        if constexpr (!A_KC) L.sa.store(lds + st * A_BYTES, tid);
+        if constexpr (!B_KC) L.sb.store(lds + B_OFF + st * B_BYTES, tid);
+    }
+
+    struct Frags {
+        u32x4 x[FN][CPL], y[FM][CPL];
+    };
+
+    static __device__ __forceinline__ void load_frags(const char *sA, const char *sB, int s, Frags &f,
+                                                      int lane, int wm, int wn) {
+        const int g = lane >> 5, r = lane & 31;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                f.x[i][c] = *reinterpret_cast<const u32x4 *>(
+                    sB + lds_off<CH>(wn * WTN + i * 32 + r, s * 2 * CPL + g * CPL + c));
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                f.y[j][c] = *reinterpret_cast<const u32x4 *>(
+                    sA + lds_off<CH>(wm * WTM + j * 32 + r, s * 2 * CPL + g * CPL + c));
+    }
+
+    static __device__ __forceinline__ void mma_frags(const Frags &f, Acc &acc) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) F::mma(acc.v[i][j], f.x[i], f.y[j]);
+    }
+
+    // Pipelined multiply with scheduling fences: the reads of substep s+1 are
+    // issued as one burst, then the MFMAs of substep s; the fence keeps the
+    // scheduler from interleaving them back into read -> wait -> MFMA pairs.
+    static __device__ __forceinline__ void compute_p3(const char *sA, const char *sB, Acc &acc,
+                                                      int lane, int wm, int wn) {
+        Frags f[2];
+        load_frags(sA, sB, 0, f[0], lane, wm, wn);
+#pragma unroll
+        for (int s = 0; s < SUBSTEPS; ++s) {
+            if (s + 1 < SUBSTEPS) load_frags(sA, sB, s + 1, f[(s + 1) & 1], lane, wm, wn);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_frags(f[s & 1], acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // Copy plan of the next k-tile for PIPE 5.
+    struct Dma {
+        __amdgpu_buffer_rsrc_t ra, rb;
+        char *la, *lb;
+        int on;   // 0: nothing to copy
+    };
+
+    // Copy J goes right after MFMA call floor(J * NMT / NL) of the k-tile.
+    template <int M, int J = 0>
+    static __device__ __forceinline__ void dma_slot(const Loader &L, const Dma &d, int wave) {
+        constexpr int NMT = SUBSTEPS * FN * FM;     // MFMA calls per k-tile
+        constexpr int NL = DA::IPW + DB::IPW;       // copies per k-tile
+        if constexpr (J < NL) {
+            if constexpr ((J * NMT) / NL == M) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (d.on) {
+                    if constexpr (J < DA::IPW) L.da.issue_one(d.ra, J, d.la, wave);
+                    else L.db.issue_one(d.rb, J - DA::IPW, d.lb, wave);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            dma_slot<M, J + 1>(L, d, wave);
+        }
+    }
+
+    template <int S, int K = 0>
+    static __device__ __forceinline__ void mma_dma(const Frags &f, Acc &acc, const Loader &L,
+                                                   const Dma &d, int wave) {
+        if constexpr (K < FN * FM) {
+            constexpr int i = K / FM, j = K % FM;
+            F::mma(acc.v[i][j], f.x[i], f.y[j]);
+            dma_slot<S * FN * FM + K>(L, d, wave);
+            mma_dma<S, K + 1>(f, acc, L, d, wave);
+        }
+    }
+
+    template <int S>
+    static __device__ __forceinline__ void p5_substeps(const char *sA, const char *sB, Frags (&f)[2],
+                                                       Acc &acc, const Loader &L, const Dma &d,
+                                                       int lane, int wm, int wn, int wave) {
+        if constexpr (S < SUBSTEPS) {
+            if constexpr (S + 1 < SUBSTEPS) load_frags(sA, sB, S + 1, f[(S + 1) & 1], lane, wm, wn);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_dma<S>(f[S & 1], acc, L, d, wave);
+            __builtin_amdgcn_sched_barrier(0);
+            p5_substeps<S + 1>(sA, sB, f, acc, L, d, lane, wm, wn, wave);
+        }
+    }
+
+    static __device__ __forceinline__ void compute_p5(const char *sA, const char *sB, Acc &acc,
+                                                      const Loader &L, const Dma &d, int lane,
+                                                      int wm, int wn, int wave) {
+        Frags f[2];
+        load_frags(sA, sB, 0, f[0], lane, wm, wn);
+        p5_substeps<0>(sA, sB, f, acc, L, d, lane, wm, wn, wave);
+    }
+
+    template <int P>
+    static __device__ __forceinline__ void compute_any(const char *sA, const char *sB, Acc &acc,
+                                                       int lane, int wm, int wn) {
+        if constexpr (P == 3) compute_p3(sA, sB, acc, lane, wm, wn);
+        else compute(sA, sB, acc, lane, wm, wn);
     }
 
     // Multiply one LDS stage into the accumulators.
@@ -471,7 +631,7 @@ struct Tile {
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
                     xf[i][c] = *reinterpret_cast<const u32x4 *>(
-                        sB + lds_off(row, s * 2 * CPL + g * CPL + c));
+                        sB + lds_off<CH>(row, s * 2 * CPL + g * CPL + c));
             }
 #pragma unroll
             for (int j = 0; j < FM; ++j) {
@@ -479,7 +639,7 @@ struct Tile {
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
                     yf[j][c] = *reinterpret_cast<const u32x4 *>(
-                        sA + lds_off(row, s * 2 * CPL + g * CPL + c));
+                        sA + lds_off<CH>(row, s * 2 * CPL + g * CPL + c));
             }
 #pragma unroll
             for (int i = 0; i < FN; ++i)
@@ -488,12 +648,66 @@ struct Tile {
         }
     }
 
+    // Wait until at most n k-tiles issued after the one needed are in flight
+    // (vmcnt counts this wave's direct loads; LPS per k-tile).
+    static __device__ __forceinline__ void wait_tiles_after(int n) {
+        if constexpr (STAGES >= 5) {
+            if (n >= 3) { wait_vmcnt<3 * LPS>(); return; }
+        }
+        if constexpr (STAGES >= 4) {
+            if (n >= 2) { wait_vmcnt<2 * LPS>(); return; }
+        }
+        if constexpr (STAGES >= 3) {
+            if (n >= 1) { wait_vmcnt<LPS>(); return; }
+        }
+        wait_vmcnt<0>();
+    }
+
+    // PIPE 4: one k-tile at compile-time stage U (see the PIPE notes above).
+    template <int U>
+    static __device__ __forceinline__ void step4(const Prob &p, int tm, int tn, int kt, int kt1,
+                                                 int last, int k_tail, Loader &L, Frags (&f)[2],
+                                                 Acc &acc, char *lds, int tid, int lane, int wm,
+                                                 int wn) {
+        const char *sA = lds + U * A_BYTES;
+        const char *sB = lds + B_OFF + U * B_BYTES;
+#pragma unroll
+        for (int s = 0; s + 1 < SUBSTEPS; ++s) {
+            load_frags(sA, sB, s + 1, f[(s + 1) & 1], lane, wm, wn);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_frags(f[s & 1], acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // k-tile kt+1 must be in LDS; later ones may stay in flight
+        wait_tiles_after(imin64(STAGES - 3, kt1 - 2 - kt));
+        barrier_no_fence();
+        constexpr int UN = (U + 1) % STAGES;        // stage of kt+1
+        constexpr int UD = (U + STAGES - 1) % STAGES;  // stage of kt-1, refilled with kt+S-1
+        if (kt + STAGES - 1 < kt1)
+            issue_stage(p, tm, tn, kt + STAGES - 1, kt + STAGES - 1 == last ? k_tail : BK, lds, UD,
+                        L, tid);
+        if (kt + 1 < kt1)
+            load_frags(lds + UN * A_BYTES, lds + B_OFF + UN * B_BYTES, 0, f[0], lane, wm, wn);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_frags(f[(SUBSTEPS - 1) & 1], acc);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    template <int U>
+    static __device__ __forceinline__ void steps4(const Prob &p, int tm, int tn, int kg, int kt1,
+                                                  int last, int k_tail, Loader &L, Frags (&f)[2],
+                                                  Acc &acc, char *lds, int tid, int lane, int wm,
+                                                  int wn) {
+        if constexpr (U < STAGES) {
+            if (kg + U < kt1) {
+                step4<U>(p, tm, tn, kg + U, kt1, last, k_tail, L, f, acc, lds, tid, lane, wm, wn);
+                steps4<U + 1>(p, tm, tn, kg, kt1, last, k_tail, L, f, acc, lds, tid, lane, wm, wn);
+            }
+        }
+    }
+
     // acc = sum over k-tiles [kt0, kt1) of the tile (tm, tn). Ends with a
     // barrier, so LDS may be reused immediately afterwards.
-    //
-    // Per k-tile: wait for this wave's copies of tile kt, barrier (every
-    // wave's copies of kt are in LDS and every wave has finished reading the
-    // other stage), start the copy of kt+1 into the other stage, multiply kt.
     static __device__ __forceinline__ void mainloop(const Prob &p, int tm, int tn, int kt0_, int kt1_,
                                                     Acc &acc, char *lds) {
         const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
@@ -506,17 +720,74 @@ struct Tile {
         const int k_tail = uniform((int)(p.K - (int64_t)last * BK));
         Loader L;
         loader_init(p, tm, tn, L, tid);
-        issue_stage(p, tm, tn, kt0, kt0 == last ? k_tail : BK, lds, L, tid);
-        store_regs(lds, L, tid);
-        for (int kt = kt0; kt < kt1; ++kt) {
-            const int par = (kt - kt0) & 1;
-            char *cur = lds + par * STAGE_BYTES;
-            char *nxt = lds + (par ^ 1) * STAGE_BYTES;
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of kt landed
-            __syncthreads();
-            if (kt + 1 < kt1) issue_stage(p, tm, tn, kt + 1, kt + 1 == last ? k_tail : BK, nxt, L, tid);
-            compute(cur, cur + A_BYTES, acc, lane, wm, wn);
-            if (kt + 1 < kt1) store_regs(nxt, L, tid);
+        if constexpr (PIPE == 4) {
+            // k-tile kt lives in stage (kt - kt0) % STAGES
+#pragma unroll
+            for (int j = 0; j < STAGES - 1; ++j)
+                if (kt0 + j < kt1)
+                    issue_stage(p, tm, tn, kt0 + j, kt0 + j == last ? k_tail : BK, lds, j, L, tid);
+            wait_tiles_after(imin64(STAGES - 2, kt1 - 1 - kt0));
+            barrier_no_fence();
+            Frags f[2];
+            load_frags(lds, lds + B_OFF, 0, f[0], lane, wm, wn);
+            for (int kg = kt0; kg < kt1; kg += STAGES)
+                steps4<0>(p, tm, tn, kg, kt1, last, k_tail, L, f, acc, lds, tid, lane, wm, wn);
+        } else if constexpr (STAGES > 2) {
+            // Deep pipeline: k-tiles kt+1 .. kt+STAGES-2 stay in flight while
+            // kt is multiplied; the stage refilled at iteration kt held kt-1.
+#pragma unroll
+            for (int j = 0; j < STAGES - 1; ++j)
+                if (kt0 + j < kt1)
+                    issue_stage(p, tm, tn, kt0 + j, kt0 + j == last ? k_tail : BK, lds, j, L, tid);
+            int stage = 0;
+            for (int kt = kt0; kt < kt1; ++kt) {
+                wait_tiles_after(imin64(STAGES - 2, kt1 - 1 - kt));
+                barrier_no_fence();
+                if (kt + STAGES - 1 < kt1) {
+                    const int st = stage == 0 ? STAGES - 1 : stage - 1;
+                    issue_stage(p, tm, tn, kt + STAGES - 1, kt + STAGES - 1 == last ? k_tail : BK,
+                                lds, st, L, tid);
+                }
+                compute_any<PIPE>(lds + stage * A_BYTES, lds + B_OFF + stage * B_BYTES, acc, lane,
+                                  wm, wn);
+                stage = stage + 1 == STAGES ? 0 : stage + 1;
+            }
+        } else if constexpr (PIPE == 5) {
+            static_assert(A_KC && B_KC && STAGES == 2, "PIPE 5: direct loads, two stages");
+            issue_stage(p, tm, tn, kt0, kt0 == last ? k_tail : BK, lds, 0, L, tid);
+            for (int kt = kt0; kt < kt1; ++kt) {
+                const int par = (kt - kt0) & 1;
+                wait_vmcnt<0>();   // this wave's copies of kt landed
+                __syncthreads();
+                Dma d;
+                d.on = 0;
+                if (kt + 1 < kt1) {
+                    if (kt + 1 == last && k_tail < BK) {   // ragged K tail: plain copy
+                        issue_stage(p, tm, tn, kt + 1, k_tail, lds, par ^ 1, L, tid);
+                    } else {
+                        d.on = 1;
+                        d.ra = L.da.rsrc(kt + 1);
+                        d.rb = L.db.rsrc(kt + 1);
+                        d.la = lds + (par ^ 1) * A_BYTES;
+                        d.lb = lds + B_OFF + (par ^ 1) * B_BYTES;
+                    }
+                }
+                compute_p5(lds + par * A_BYTES, lds + B_OFF + par * B_BYTES, acc, L, d, lane, wm, wn,
+                           wave);
+            }
+        } else {
+            issue_stage(p, tm, tn, kt0, kt0 == last ? k_tail : BK, lds, 0, L, tid);
+            store_regs(lds, 0, L, tid);
+            for (int kt = kt0; kt < kt1; ++kt) {
+                const int par = (kt - kt0) & 1;
+                wait_vmcnt<0>();   // this wave's copies of kt landed
+                __syncthreads();
+                if (kt + 1 < kt1)
+                    issue_stage(p, tm, tn, kt + 1, kt + 1 == last ? k_tail : BK, lds, par ^ 1, L, tid);
+                compute_any<PIPE>(lds + par * A_BYTES, lds + B_OFF + par * B_BYTES, acc, lane, wm,
+                                  wn);
+                if (kt + 1 < kt1) store_regs(lds, par ^ 1, L, tid);
+            }
         }
         __syncthreads();
     }

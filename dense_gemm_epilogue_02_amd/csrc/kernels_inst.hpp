@@ -3,7 +3,10 @@
 
 #include "kernels.hpp"
 
-#define MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN) mg::Tile<FAM, AKC, BKC, BM, BN, WM, WN>
+// K-contiguous operands on both sides (TN): LDS-DMA copies interleaved with
+// the MFMAs (PIPE 5); otherwise register-staged copies (PIPE 0).
+#define MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN) \
+    mg::Tile<FAM, AKC, BKC, BM, BN, WM, WN, 128, 2, ((AKC) && (BKC)) ? 5 : 0>
 
 #define MG_ROW(FAM, AKC, BKC, TILEID, BM, BN, WM, WN, GROUPED) \
     mg::make_entry<MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN), GROUPED>(TILEID, AKC, BKC)
