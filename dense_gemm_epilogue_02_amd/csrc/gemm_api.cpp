@@ -303,9 +303,14 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
         d.grid = d.total < G ? d.total : G;
         break;
     case GEMM_SCHED_STREAM_K: {
+        // at least kMinSkIters MAC iterations per workgroup, so the partial-tile
+        // fixups stay small next to the work (an explicit sk_grid overrides)
+        constexpr int64_t kMinSkIters = 8;
         d.sk_tiles = d.total;
         d.sk_iters = (int64_t)d.total * d.ipt;
-        const int64_t g = d.sk_iters < G ? d.sk_iters : G;
+        int64_t g = pl->sk_grid > 0 ? d.sk_iters : d.sk_iters / kMinSkIters;
+        if (g > G) g = G;
+        if (g < d.total && pl->sk_grid <= 0) g = d.total < G ? d.total : G;
         d.grid = (int)(g > 0 ? g : 1);
         break;
     }

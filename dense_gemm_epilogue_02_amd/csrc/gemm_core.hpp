@@ -907,9 +907,16 @@ struct Tile {
     }
 
     // ---- stream-K partial tiles ---------------------------------------------
+    //
+    // Partials are written and read with device-scope (sc1) buffer accesses,
+    // which stay coherent across the XCDs' private L2s; no L2 write-back or
+    // invalidate (what a __threadfence() costs) is needed.
+
+    static constexpr int SC1 = 16;   // cache-policy bit: device scope
 
     static __device__ __forceinline__ void store_partial(float *slot, const Acc &acc) {
         const int tid = threadIdx.x;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot);
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -917,14 +924,16 @@ struct Tile {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int grp = (i * FM + j) * 4 + q;
-                    f32x4 t{acc.v[i][j][q * 4], acc.v[i][j][q * 4 + 1], acc.v[i][j][q * 4 + 2],
-                            acc.v[i][j][q * 4 + 3]};
-                    *reinterpret_cast<f32x4 *>(slot + ((size_t)grp * NT + tid) * 4) = t;
+                    const f32x4 t{acc.v[i][j][q * 4], acc.v[i][j][q * 4 + 1], acc.v[i][j][q * 4 + 2],
+                                  acc.v[i][j][q * 4 + 3]};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t), rs,
+                                                           (uint32_t)((grp * NT + tid) * 16), 0, SC1);
                 }
     }
 
     static __device__ __forceinline__ void add_partial(const float *slot, Acc &acc, bool first) {
         const int tid = threadIdx.x;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot);
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -932,7 +941,9 @@ struct Tile {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int grp = (i * FM + j) * 4 + q;
-                    const f32x4 t = *reinterpret_cast<const f32x4 *>(slot + ((size_t)grp * NT + tid) * 4);
+                    const f32x4 t = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   rs, (uint32_t)((grp * NT + tid) * 16), 0, SC1));
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         acc.v[i][j][q * 4 + e] = first ? t[e] : acc.v[i][j][q * 4 + e] + t[e];
@@ -1001,18 +1012,18 @@ __global__ void __launch_bounds__(TL::NT) gemm_persistent(KArgs a) {
                 const size_t slot_elems = (size_t)TL::BM * TL::BN;
                 const int my_slot = 2 * v + (t == first_tile ? 0 : 1);
                 TL::store_partial(s.partials + my_slot * slot_elems, acc);
-                __threadfence();
-                __syncthreads();
+                wait_vmcnt<0>();   // this thread's device-scope stores are complete
+                __syncthreads();   // ... and every thread's, before the arrival is counted
                 const int v0 = sk_owner(tile_it0, T, G);
                 const int v1 = sk_owner(tile_it0 + p.ipt - 1, T, G);
                 if (threadIdx.x == 0) {
-                    const int old = __hip_atomic_fetch_add(&s.counters[t], 1, __ATOMIC_ACQ_REL,
+                    const int old = __hip_atomic_fetch_add(&s.counters[t], 1, __ATOMIC_RELAXED,
                                                            __HIP_MEMORY_SCOPE_AGENT);
                     last_flag = (old == v1 - v0);
                 }
                 __syncthreads();
                 if (last_flag) {
-                    __threadfence();
+                    // every contributor's partial is complete at device scope
                     for (int u = v0; u <= v1; ++u) {
                         const int ft = (int)(((int64_t)u * T / G) / p.ipt);
                         const int slot = 2 * u + (t == ft ? 0 : 1);

@@ -3,10 +3,10 @@
 
 #include "kernels.hpp"
 
-// K-contiguous operands on both sides (TN): LDS-DMA copies interleaved with
-// the MFMAs (PIPE 5); otherwise register-staged copies (PIPE 0).
-#define MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN) \
-    mg::Tile<FAM, AKC, BKC, BM, BN, WM, WN, 128, 2, ((AKC) && (BKC)) ? 5 : 0>
+// 128-byte LDS rows, two stages, compiler-scheduled fragment reads (PIPE 0):
+// in interleaved same-box measurements this matched or beat the hand-ordered
+// pipelines (PIPE 3 / 5) on the layer GEMMs.
+#define MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN) mg::Tile<FAM, AKC, BKC, BM, BN, WM, WN, 128, 2, 0>
 
 #define MG_ROW(FAM, AKC, BKC, TILEID, BM, BN, WM, WN, GROUPED) \
     mg::make_entry<MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN), GROUPED>(TILEID, AKC, BKC)
