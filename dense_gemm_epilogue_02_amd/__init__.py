@@ -53,6 +53,7 @@ class Schedule(IntEnum):
     DATA_PARALLEL = 1
     STREAM_K = 2
     HYBRID = 3
+    SPLIT_K = 4
 
 
 class Tile(IntEnum):
@@ -81,6 +82,12 @@ def _load():
         raise ImportError(
             f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
             "or `python dense_gemm_epilogue_02_amd/build.py` (needs hipcc for gfx950)")
+    # One HIP runtime per process: torch ships its own libamdhip64 and asks for
+    # it by its unversioned file name, so if this library were loaded first its
+    # libamdhip64.so.7 from ROCm would stay beside torch's as a second runtime
+    # with its own device state. Loading torch first makes the soname resolve to
+    # the copy torch already holds.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     i32, i64, f32, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
     st = ctypes.c_int

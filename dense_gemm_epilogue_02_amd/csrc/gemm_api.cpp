@@ -12,6 +12,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -175,7 +176,7 @@ bool plan_ok(gemm_plan_t p) { return p && p->magic == kMagic; }
 struct Decision {
     const KernelEntry *e = nullptr;   // null: scalar-load kernel
     gemm_schedule sched = GEMM_SCHED_DATA_PARALLEL;
-    int tiles_m = 0, tiles_n = 0, ipt = 0, total = 0, grid = 0, sk_tiles = 0;
+    int tiles_m = 0, tiles_n = 0, ipt = 0, total = 0, grid = 0, sk_tiles = 0, split = 0;
     int64_t sk_iters = 0;
     int group_m = 4;
     int vec_cd = 0;
@@ -199,7 +200,8 @@ const char *operand_vec_problem(const void *ptr, bool kc, int64_t contig, int64_
 
 gemm_tile pick_tile(int fam, int64_t M, int64_t N, int cus) {
     if (fam == FAM_F32) return GEMM_TILE_128x128;
-    if (M <= 32) return GEMM_TILE_32x256;
+    // skinny M streams B once: 64-row tiles matched or beat 32-row ones for
+    // every measured M <= 64 (fewer, longer B panels per workgroup)
     if (M <= 64) return GEMM_TILE_64x256;
     const int64_t big = cdiv(M, 256) * cdiv(N, 256);
     return big >= cus ? GEMM_TILE_256x256 : GEMM_TILE_128x128;
@@ -231,9 +233,13 @@ const char *sched_name(gemm_schedule s) {
     case GEMM_SCHED_DATA_PARALLEL: return "data_parallel";
     case GEMM_SCHED_STREAM_K: return "stream_k";
     case GEMM_SCHED_HYBRID: return "hybrid";
+    case GEMM_SCHED_SPLIT_K: return "split_k";
     default: return "auto";
     }
 }
+
+// fewest k-tiles one split-K unit takes
+constexpr int kMinSplitIters = 8;
 
 // `occ_of` gives workgroups per CU for an entry (live query or estimate).
 template <class OccFn>
@@ -291,9 +297,15 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
             const double eff = (double)d.total / (double)(cdiv(d.total, G) * G);
             s = (rem == 0 || eff >= 0.9 || d.ipt < 4) ? GEMM_SCHED_DATA_PARALLEL : GEMM_SCHED_HYBRID;
         } else {
-            s = d.ipt >= 4 ? GEMM_SCHED_STREAM_K : GEMM_SCHED_DATA_PARALLEL;
+            // fewer tiles than workgroup slots: nearly full waves run as they are;
+            // otherwise cut K, interleaved when every tile gets >= 4 units
+            // (no tile straddles two workgroups), else stream-K ranges
+            const int S = std::min(G / d.total, d.ipt / kMinSplitIters);
+            if (d.ipt < 4 || (double)d.total >= 0.85 * G) s = GEMM_SCHED_DATA_PARALLEL;
+            else s = S >= 4 ? GEMM_SCHED_SPLIT_K : GEMM_SCHED_STREAM_K;
         }
     }
+    if (s == GEMM_SCHED_SPLIT_K && d.total >= G) s = GEMM_SCHED_DATA_PARALLEL;
     if (s == GEMM_SCHED_HYBRID && (d.total < G || d.total % G == 0))
         s = d.total < G ? GEMM_SCHED_STREAM_K : GEMM_SCHED_DATA_PARALLEL;
     d.sched = s;
@@ -312,6 +324,16 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
         if (g > G) g = G;
         if (g < d.total && pl->sk_grid <= 0) g = d.total < G ? d.total : G;
         d.grid = (int)(g > 0 ? g : 1);
+        break;
+    }
+    case GEMM_SCHED_SPLIT_K: {
+        // `split` interleaved K units per tile, each with >= kMinSplitIters k-tiles
+        int S = G / d.total;
+        if (S > d.ipt / kMinSplitIters) S = d.ipt / kMinSplitIters;
+        if (S < 1) S = 1;
+        d.split = S;
+        d.sk_tiles = d.total;
+        d.grid = d.total * S;
         break;
     }
     default:   // hybrid: whole waves data-parallel, the remainder stream-K
@@ -466,9 +488,10 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
     a.s.sk_iters = d.sk_iters;
     a.s.group_m = d.group_m;
     a.s.xcd_remap = 1;
+    a.s.split = d.split;
     a.s.partials = nullptr;
     a.s.counters = nullptr;
-    if (d.sk_tiles > 0) {
+    if (d.sk_tiles > 0 && d.split != 1) {
         const size_t pbytes = (size_t)2 * d.grid * d.e->bm * d.e->bn * sizeof(float);
         if ((st = ensure_workspace(pl, pbytes, (size_t)d.sk_tiles, hs)) != GEMM_OK) return st;
         a.s.partials = pl->partials;
@@ -555,7 +578,7 @@ gemm_status gemm_plan_destroy(gemm_plan_t p) {
 
 gemm_status gemm_plan_set_config(gemm_plan_t p, gemm_schedule s, gemm_tile t, int32_t sk_grid) {
     if (!plan_ok(p)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_set_config: invalid plan handle");
-    if (s < GEMM_SCHED_AUTO || s > GEMM_SCHED_HYBRID)
+    if (s < GEMM_SCHED_AUTO || s > GEMM_SCHED_SPLIT_K)
         return fail(GEMM_INVALID_ARG, "gemm_plan_set_config: unknown schedule %d", (int)s);
     if (t < GEMM_TILE_AUTO || t > GEMM_TILE_GENERIC)
         return fail(GEMM_INVALID_ARG, "gemm_plan_set_config: unknown tile %d", (int)t);
@@ -720,9 +743,10 @@ gemm_status gemm_plan_describe(gemm_plan_t pl, int64_t M, int64_t N, int64_t K, 
     if (st != GEMM_OK) return st;
     snprintf(buf, (size_t)len,
              "{\"kernel\": \"%s\", \"tile\": \"%s\", \"bk\": %d, \"waves\": %d, \"schedule\": \"%s\", "
-             "\"tiles\": %d, \"ipt\": %d, \"sk_tiles\": %d, \"grid\": %d, \"generic_reason\": \"%s\"}",
+             "\"tiles\": %d, \"ipt\": %d, \"sk_tiles\": %d, \"split\": %d, \"grid\": %d, "
+             "\"generic_reason\": \"%s\"}",
              d.e ? "tile" : "generic", tile_name(d.e), d.e ? d.e->bk : 16, d.e ? d.e->nt / 64 : 4,
-             sched_name(d.sched), d.total, d.ipt, d.sk_tiles, d.grid, d.why_generic);
+             sched_name(d.sched), d.total, d.ipt, d.sk_tiles, d.split, d.grid, d.why_generic);
     return ok();
 }
 

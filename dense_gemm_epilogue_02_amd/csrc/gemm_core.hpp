@@ -119,7 +119,11 @@ struct EpiArgs {
 
 // Persistent schedule: schedule indices [0, sk_tiles) are split stream-K
 // style over `grid` workgroups; [sk_tiles, total) are whole tiles dealt out
-// round robin.
+// round robin. With split > 0 every tile is instead cut into `split` units
+// (grid = tiles * split): unit c takes k-tiles c, c + split, c + 2 split, ...,
+// so the units of one tile, which run side by side, read neighbouring
+// segments of every operand row (DRAM page locality on skinny, HBM-bound
+// shapes).
 struct Sched {
     int grid;
     int total_tiles;
@@ -127,6 +131,7 @@ struct Sched {
     int64_t sk_iters;       // sk_tiles * ipt
     int group_m;            // raster: tile rows per swizzle group
     int xcd_remap;          // map consecutive virtual ids onto one XCD
+    int split;              // > 0: interleaved split-K, `split` units per tile
     float *partials;        // stream-K workspace: 2 * grid slots of BM*BN fp32
     int *counters;          // one arrival counter per stream-K tile (self-resetting)
 };
@@ -377,13 +382,7 @@ template <int R, int ESZ, int NT, int CH> struct DirectStager {
 // (more than 2 only when both operands are K-contiguous).
 // PIPE: 0 = fragment reads scheduled by the compiler; 3 = the fragments of
 // substep s+1 are read (as one burst) before the MFMAs of substep s, with
-// scheduling fences; 4 = as 3, with the k-loop unrolled over the LDS stages
-// (all LDS offsets become immediates) and the barrier placed before the last
-// substep of each k-tile, so the next k-tile's first fragments are read while
-// that substep's MFMAs run (needs STAGES >= 3 and direct loads); 5 = as 3,
-// with the next k-tile's LDS-DMA instructions spread through the MFMA
-// stream (one after every few MFMAs) instead of issued as one burst, which
-// would stall every wave's MFMA issue behind the CU's memory queue.
+// scheduling fences.
 template <int FAM_, bool A_KC, bool B_KC, int BM_, int BN_, int WM_, int WN_, int KB = 128,
           int STAGES = 2, int PIPE = 0>
 struct Tile {
@@ -404,8 +403,6 @@ struct Tile {
     static constexpr int LDS_BYTES = STAGES * (A_BYTES + B_BYTES);
     static_assert(CH == 8 || CH == 4, "64- or 128-byte LDS rows");
     static_assert(STAGES == 2 || (A_KC && B_KC), "deep pipelines need direct loads");
-    static_assert(PIPE != 4 || (STAGES >= 3 && SUBSTEPS % 2 == 0 && A_KC && B_KC),
-                  "cross-tile fragment prefetch");
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
@@ -554,63 +551,6 @@ struct Tile {
         }
     }
 
-    // Copy plan of the next k-tile for PIPE 5.
-    struct Dma {
-        __amdgpu_buffer_rsrc_t ra, rb;
-        char *la, *lb;
-        int on;   // 0: nothing to copy
-    };
-
-    // Copy J goes right after MFMA call floor(J * NMT / NL) of the k-tile.
-    template <int M, int J = 0>
-    static __device__ __forceinline__ void dma_slot(const Loader &L, const Dma &d, int wave) {
-        constexpr int NMT = SUBSTEPS * FN * FM;     // MFMA calls per k-tile
-        constexpr int NL = DA::IPW + DB::IPW;       // copies per k-tile
-        if constexpr (J < NL) {
-            if constexpr ((J * NMT) / NL == M) {
-                __builtin_amdgcn_sched_barrier(0);
-                if (d.on) {
-                    if constexpr (J < DA::IPW) L.da.issue_one(d.ra, J, d.la, wave);
-                    else L.db.issue_one(d.rb, J - DA::IPW, d.lb, wave);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            dma_slot<M, J + 1>(L, d, wave);
-        }
-    }
-
-    template <int S, int K = 0>
-    static __device__ __forceinline__ void mma_dma(const Frags &f, Acc &acc, const Loader &L,
-                                                   const Dma &d, int wave) {
-        if constexpr (K < FN * FM) {
-            constexpr int i = K / FM, j = K % FM;
-            F::mma(acc.v[i][j], f.x[i], f.y[j]);
-            dma_slot<S * FN * FM + K>(L, d, wave);
-            mma_dma<S, K + 1>(f, acc, L, d, wave);
-        }
-    }
-
-    template <int S>
-    static __device__ __forceinline__ void p5_substeps(const char *sA, const char *sB, Frags (&f)[2],
-                                                       Acc &acc, const Loader &L, const Dma &d,
-                                                       int lane, int wm, int wn, int wave) {
-        if constexpr (S < SUBSTEPS) {
-            if constexpr (S + 1 < SUBSTEPS) load_frags(sA, sB, S + 1, f[(S + 1) & 1], lane, wm, wn);
-            __builtin_amdgcn_sched_barrier(0);
-            mma_dma<S>(f[S & 1], acc, L, d, wave);
-            __builtin_amdgcn_sched_barrier(0);
-            p5_substeps<S + 1>(sA, sB, f, acc, L, d, lane, wm, wn, wave);
-        }
-    }
-
-    static __device__ __forceinline__ void compute_p5(const char *sA, const char *sB, Acc &acc,
-                                                      const Loader &L, const Dma &d, int lane,
-                                                      int wm, int wn, int wave) {
-        Frags f[2];
-        load_frags(sA, sB, 0, f[0], lane, wm, wn);
-        p5_substeps<0>(sA, sB, f, acc, L, d, lane, wm, wn, wave);
-    }
-
     template <int P>
     static __device__ __forceinline__ void compute_any(const char *sA, const char *sB, Acc &acc,
                                                        int lane, int wm, int wn) {
@@ -663,130 +603,53 @@ struct Tile {
         wait_vmcnt<0>();
     }
 
-    // PIPE 4: one k-tile at compile-time stage U (see the PIPE notes above).
-    template <int U>
-    static __device__ __forceinline__ void step4(const Prob &p, int tm, int tn, int kt, int kt1,
-                                                 int last, int k_tail, Loader &L, Frags (&f)[2],
-                                                 Acc &acc, char *lds, int tid, int lane, int wm,
-                                                 int wn) {
-        const char *sA = lds + U * A_BYTES;
-        const char *sB = lds + B_OFF + U * B_BYTES;
-#pragma unroll
-        for (int s = 0; s + 1 < SUBSTEPS; ++s) {
-            load_frags(sA, sB, s + 1, f[(s + 1) & 1], lane, wm, wn);
-            __builtin_amdgcn_sched_barrier(0);
-            mma_frags(f[s & 1], acc);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // k-tile kt+1 must be in LDS; later ones may stay in flight
-        wait_tiles_after(imin64(STAGES - 3, kt1 - 2 - kt));
-        barrier_no_fence();
-        constexpr int UN = (U + 1) % STAGES;        // stage of kt+1
-        constexpr int UD = (U + STAGES - 1) % STAGES;  // stage of kt-1, refilled with kt+S-1
-        if (kt + STAGES - 1 < kt1)
-            issue_stage(p, tm, tn, kt + STAGES - 1, kt + STAGES - 1 == last ? k_tail : BK, lds, UD,
-                        L, tid);
-        if (kt + 1 < kt1)
-            load_frags(lds + UN * A_BYTES, lds + B_OFF + UN * B_BYTES, 0, f[0], lane, wm, wn);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_frags(f[(SUBSTEPS - 1) & 1], acc);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-
-    template <int U>
-    static __device__ __forceinline__ void steps4(const Prob &p, int tm, int tn, int kg, int kt1,
-                                                  int last, int k_tail, Loader &L, Frags (&f)[2],
-                                                  Acc &acc, char *lds, int tid, int lane, int wm,
-                                                  int wn) {
-        if constexpr (U < STAGES) {
-            if (kg + U < kt1) {
-                step4<U>(p, tm, tn, kg + U, kt1, last, k_tail, L, f, acc, lds, tid, lane, wm, wn);
-                steps4<U + 1>(p, tm, tn, kg, kt1, last, k_tail, L, f, acc, lds, tid, lane, wm, wn);
-            }
-        }
-    }
-
-    // acc = sum over k-tiles [kt0, kt1) of the tile (tm, tn). Ends with a
-    // barrier, so LDS may be reused immediately afterwards.
-    static __device__ __forceinline__ void mainloop(const Prob &p, int tm, int tn, int kt0_, int kt1_,
-                                                    Acc &acc, char *lds) {
+    // acc = sum over the n k-tiles kt0, kt0 + stride, ..., kt0 + (n-1) stride
+    // of the tile (tm, tn). Ends with a barrier, so LDS may be reused
+    // immediately afterwards.
+    static __device__ __forceinline__ void mainloop(const Prob &p, int tm, int tn, int kt0_, int n_,
+                                                    int stride_, Acc &acc, char *lds) {
         const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
         const int wm = wave / WN, wn = wave % WN;
-        const int kt0 = uniform(kt0_), kt1 = uniform(kt1_);
+        const int kt0 = uniform(kt0_), n = uniform(n_), stride = uniform(stride_);
         zero(acc);
-        if (kt0 >= kt1) return;
+        if (n <= 0) return;
         // valid k of the last k-tile of K (the only one that can be partial)
         const int last = uniform(p.ipt) - 1;
         const int k_tail = uniform((int)(p.K - (int64_t)last * BK));
+        auto kvalid = [&](int kt) { return kt == last ? k_tail : BK; };
         Loader L;
         loader_init(p, tm, tn, L, tid);
-        if constexpr (PIPE == 4) {
-            // k-tile kt lives in stage (kt - kt0) % STAGES
+        if constexpr (STAGES > 2) {
+            // Deep pipeline: k-tiles i+1 .. i+STAGES-2 stay in flight while i
+            // is multiplied; the stage refilled at iteration i held i-1.
 #pragma unroll
             for (int j = 0; j < STAGES - 1; ++j)
-                if (kt0 + j < kt1)
-                    issue_stage(p, tm, tn, kt0 + j, kt0 + j == last ? k_tail : BK, lds, j, L, tid);
-            wait_tiles_after(imin64(STAGES - 2, kt1 - 1 - kt0));
-            barrier_no_fence();
-            Frags f[2];
-            load_frags(lds, lds + B_OFF, 0, f[0], lane, wm, wn);
-            for (int kg = kt0; kg < kt1; kg += STAGES)
-                steps4<0>(p, tm, tn, kg, kt1, last, k_tail, L, f, acc, lds, tid, lane, wm, wn);
-        } else if constexpr (STAGES > 2) {
-            // Deep pipeline: k-tiles kt+1 .. kt+STAGES-2 stay in flight while
-            // kt is multiplied; the stage refilled at iteration kt held kt-1.
-#pragma unroll
-            for (int j = 0; j < STAGES - 1; ++j)
-                if (kt0 + j < kt1)
-                    issue_stage(p, tm, tn, kt0 + j, kt0 + j == last ? k_tail : BK, lds, j, L, tid);
+                if (j < n) issue_stage(p, tm, tn, kt0 + j * stride, kvalid(kt0 + j * stride), lds, j, L, tid);
             int stage = 0;
-            for (int kt = kt0; kt < kt1; ++kt) {
-                wait_tiles_after(imin64(STAGES - 2, kt1 - 1 - kt));
+            for (int i = 0; i < n; ++i) {
+                wait_tiles_after(imin64(STAGES - 2, n - 1 - i));
                 barrier_no_fence();
-                if (kt + STAGES - 1 < kt1) {
+                if (i + STAGES - 1 < n) {
                     const int st = stage == 0 ? STAGES - 1 : stage - 1;
-                    issue_stage(p, tm, tn, kt + STAGES - 1, kt + STAGES - 1 == last ? k_tail : BK,
-                                lds, st, L, tid);
+                    const int kt = kt0 + (i + STAGES - 1) * stride;
+                    issue_stage(p, tm, tn, kt, kvalid(kt), lds, st, L, tid);
                 }
                 compute_any<PIPE>(lds + stage * A_BYTES, lds + B_OFF + stage * B_BYTES, acc, lane,
                                   wm, wn);
                 stage = stage + 1 == STAGES ? 0 : stage + 1;
             }
-        } else if constexpr (PIPE == 5) {
-            static_assert(A_KC && B_KC && STAGES == 2, "PIPE 5: direct loads, two stages");
-            issue_stage(p, tm, tn, kt0, kt0 == last ? k_tail : BK, lds, 0, L, tid);
-            for (int kt = kt0; kt < kt1; ++kt) {
-                const int par = (kt - kt0) & 1;
-                wait_vmcnt<0>();   // this wave's copies of kt landed
-                __syncthreads();
-                Dma d;
-                d.on = 0;
-                if (kt + 1 < kt1) {
-                    if (kt + 1 == last && k_tail < BK) {   // ragged K tail: plain copy
-                        issue_stage(p, tm, tn, kt + 1, k_tail, lds, par ^ 1, L, tid);
-                    } else {
-                        d.on = 1;
-                        d.ra = L.da.rsrc(kt + 1);
-                        d.rb = L.db.rsrc(kt + 1);
-                        d.la = lds + (par ^ 1) * A_BYTES;
-                        d.lb = lds + B_OFF + (par ^ 1) * B_BYTES;
-                    }
-                }
-                compute_p5(lds + par * A_BYTES, lds + B_OFF + par * B_BYTES, acc, L, d, lane, wm, wn,
-                           wave);
-            }
         } else {
-            issue_stage(p, tm, tn, kt0, kt0 == last ? k_tail : BK, lds, 0, L, tid);
+            issue_stage(p, tm, tn, kt0, kvalid(kt0), lds, 0, L, tid);
             store_regs(lds, 0, L, tid);
-            for (int kt = kt0; kt < kt1; ++kt) {
-                const int par = (kt - kt0) & 1;
-                wait_vmcnt<0>();   // this wave's copies of kt landed
+            for (int i = 0; i < n; ++i) {
+                const int par = i & 1;
+                wait_vmcnt<0>();   // this wave's copies of k-tile i landed
                 __syncthreads();
-                if (kt + 1 < kt1)
-                    issue_stage(p, tm, tn, kt + 1, kt + 1 == last ? k_tail : BK, lds, par ^ 1, L, tid);
+                const int kt = kt0 + (i + 1) * stride;
+                if (i + 1 < n) issue_stage(p, tm, tn, kt, kvalid(kt), lds, par ^ 1, L, tid);
                 compute_any<PIPE>(lds + par * A_BYTES, lds + B_OFF + par * B_BYTES, acc, lane, wm,
                                   wn);
-                if (kt + 1 < kt1) store_regs(lds, par ^ 1, L, tid);
+                if (i + 1 < n) store_regs(lds, par ^ 1, L, tid);
             }
         }
         __syncthreads();
@@ -991,6 +854,36 @@ __global__ void __launch_bounds__(TL::NT) gemm_persistent(KArgs a) {
     typename TL::Acc acc;
     int tm, tn;
 
+    if (s.split > 0) {
+        const int S = s.split;
+        if (v >= s.sk_tiles * S) return;
+        const int t = v / S, c = v - (v / S) * S;
+        tile_coords(t, p.tiles_m, p.tiles_n, s.group_m, tm, tn);
+        TL::mainloop(p, tm, tn, c, (p.ipt - c + S - 1) / S, S, acc, lds);
+        if (S == 1) {
+            TL::epilogue(p, a.e, tm, tn, acc);
+            return;
+        }
+        const size_t slot_elems = (size_t)TL::BM * TL::BN;
+        TL::store_partial(s.partials + (size_t)v * slot_elems, acc);
+        wait_vmcnt<0>();   // this thread's device-scope stores are complete
+        __syncthreads();   // ... and every thread's, before the arrival is counted
+        if (threadIdx.x == 0) {
+            const int old =
+                __hip_atomic_fetch_add(&s.counters[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last_flag = (old == S - 1);
+        }
+        __syncthreads();
+        if (last_flag) {   // sum the units in order c = 0 .. S-1 (deterministic)
+            for (int u = 0; u < S; ++u)
+                TL::add_partial(s.partials + ((size_t)t * S + u) * slot_elems, acc, u == 0);
+            TL::epilogue(p, a.e, tm, tn, acc);
+            if (threadIdx.x == 0)
+                __hip_atomic_store(&s.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return;
+    }
+
     if (s.sk_tiles > 0 && p.ipt > 0) {
         const int64_t T = s.sk_iters;
         const int G = s.grid;
@@ -1003,7 +896,7 @@ __global__ void __launch_bounds__(TL::NT) gemm_persistent(KArgs a) {
             const int k0 = (int)(it - tile_it0);
             const int k1 = (int)(imin64(end, tile_it0 + p.ipt) - tile_it0);
             tile_coords(t, p.tiles_m, p.tiles_n, s.group_m, tm, tn);
-            TL::mainloop(p, tm, tn, k0, k1, acc, lds);
+            TL::mainloop(p, tm, tn, k0, k1 - k0, 1, acc, lds);
             if (k0 == 0 && k1 == p.ipt) {
                 TL::epilogue(p, a.e, tm, tn, acc);
             } else {
@@ -1040,7 +933,7 @@ __global__ void __launch_bounds__(TL::NT) gemm_persistent(KArgs a) {
     }
     for (int t = s.sk_tiles + v; t < s.total_tiles; t += s.grid) {
         tile_coords(t, p.tiles_m, p.tiles_n, s.group_m, tm, tn);
-        TL::mainloop(p, tm, tn, 0, p.ipt, acc, lds);
+        TL::mainloop(p, tm, tn, 0, p.ipt, 1, acc, lds);
         TL::epilogue(p, a.e, tm, tn, acc);
     }
 }
@@ -1061,7 +954,7 @@ __global__ void __launch_bounds__(TL::NT) gemm_grouped(GroupArgs g) {
         const Prob p = g.desc[lo].p;
         int tm, tn;
         tile_coords(t - g.desc[lo].tile_start, p.tiles_m, p.tiles_n, g.group_m, tm, tn);
-        TL::mainloop(p, tm, tn, 0, p.ipt, acc, lds);
+        TL::mainloop(p, tm, tn, 0, p.ipt, 1, acc, lds);
         TL::epilogue(p, g.e, tm, tn, acc);
     }
 }

@@ -81,7 +81,8 @@ typedef enum {
     GEMM_SCHED_AUTO = 0,          /* heuristic: data-parallel, stream-K or hybrid */
     GEMM_SCHED_DATA_PARALLEL = 1, /* one work unit per output tile */
     GEMM_SCHED_STREAM_K = 2,      /* every tile's MAC iterations split evenly */
-    GEMM_SCHED_HYBRID = 3         /* whole waves data-parallel, the rest stream-K */
+    GEMM_SCHED_HYBRID = 3,        /* whole waves data-parallel, the rest stream-K */
+    GEMM_SCHED_SPLIT_K = 4        /* each tile cut into interleaved K units (skinny shapes) */
 } gemm_schedule;
 
 /* Output tile shape (rows of D x columns of D per workgroup). */

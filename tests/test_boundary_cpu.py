@@ -143,10 +143,18 @@ def test_describe_small_and_skinny_use_stream_k():
     assert d["tile"] == "128x128" and d["schedule"] == "stream_k" and d["ipt"] == 16
     p.close()
     q = _plan("f8e4m3")
-    for M, tile in ((16, "32x256"), (64, "64x256"), (128, "128x128")):
+    # decode GEMMs: N = 8192 gives 32-64 tiles, so each tile is cut into
+    # interleaved K units that fill the 512 workgroup slots
+    for M, tile, split in ((16, "64x256", 16), (64, "64x256", 16), (128, "128x128", 8)):
         d = q.describe(M, 8192, 28672)
-        assert d["tile"] == tile and d["schedule"] == "stream_k", d
-        assert d["bk"] == 128
+        assert d["tile"] == tile and d["schedule"] == "split_k", d
+        assert d["split"] == split and d["grid"] == d["tiles"] * split and d["bk"] == 128
+    # N = 57344: 224 tiles of 64x256 leave room for only two units per tile
+    d = q.describe(16, 57344, 8192)
+    assert d["tile"] == "64x256" and d["schedule"] == "stream_k" and d["split"] == 0, d
+    # 448 tiles of 128x128 fill 87.5% of the slots: data-parallel
+    d = q.describe(128, 57344, 8192)
+    assert d["tile"] == "128x128" and d["schedule"] == "data_parallel" and d["grid"] == 448, d
     q.close()
 
 
@@ -164,6 +172,11 @@ def test_describe_forced_configs():
     p.set_config(g.Schedule.STREAM_K, g.Tile.T256x256, 0)
     d = p.describe(4096, 8192, 8192)
     assert d["schedule"] == "stream_k" and d["tile"] == "256x256"
+    p.set_config(g.Schedule.SPLIT_K, g.Tile.T128x128, 0)
+    d = p.describe(256, 256, 8192)      # 4 tiles, 128 k-tiles: 16 units of 8
+    assert d["schedule"] == "split_k" and d["split"] == 16 and d["grid"] == 64, d
+    d = p.describe(4096, 8192, 8192)    # more tiles than slots: no split
+    assert d["schedule"] == "data_parallel" and d["split"] == 0, d
     p.set_config(g.Schedule.DATA_PARALLEL, g.Tile.GENERIC, 0)
     assert p.describe(64, 64, 64)["kernel"] == "generic"
     p.close()

@@ -165,13 +165,25 @@ def test_integer_exact_stream_k(dab, dcd, sched, tile, relu):
 
 
 @pytest.mark.parametrize("dab,dcd", FAMS)
+@pytest.mark.parametrize("tile", [T.T128x128, T.T64x256, T.T32x256])
+@pytest.mark.parametrize("relu", [False, True])
+@pytest.mark.parametrize("lb", ["col", "row"])
+def test_integer_exact_split_k(dab, dcd, tile, relu, lb):
+    # few tiles, long ragged K: units of 8+ k-tiles, the first ones one longer
+    p = _int_problem(dab, dcd, "row", lb, "row", M=200, N=272, K=2064, seed=11)
+    got = run(p, relu=relu, tile=tile, schedule=S.SPLIT_K)
+    exact(got, p, relu=relu, what=f"{dab} split-K {tile.name} lb={lb}")
+
+
+@pytest.mark.parametrize("dab,dcd", FAMS)
 @pytest.mark.parametrize("la,lb,lc", [("row", "row", "row"), ("col", "col", "col"),
                                       ("row", "col", "row"), ("col", "row", "col")])
 def test_random_tolerance(dab, dcd, la, lb, lc):
     p = syn.make_problem(336, 400, 520, dtype_ab=dab, dtype_cd=dcd, la=la, lb=lb, lc=lc,
                          dist_c="normal", alpha=0.75, beta=-0.5, seed=7)
-    for sched in (S.DATA_PARALLEL, S.STREAM_K):
-        close(run(p, relu=True, schedule=sched), p, relu=True, what=f"{dab} {la}{lb}{lc}")
+    for sched in (S.DATA_PARALLEL, S.STREAM_K, S.SPLIT_K):
+        close(run(p, relu=True, schedule=sched), p, relu=True,
+              what=f"{dab} {la}{lb}{lc} {sched.name}")
 
 
 # ------------------------------------------------------------ stream-K
@@ -185,6 +197,17 @@ def test_stream_k_deterministic_and_equivalent():
         assert np.array_equal(a, b), f"stream-K grid {grid} not bitwise repeatable"
         close(a, p, what=f"stream-K grid {grid}")
     close(dp, p, what="data-parallel")
+
+
+@pytest.mark.parametrize("grid", [0, 12, 24])
+def test_split_k_deterministic_and_close(grid):
+    # fp8 decode-like: 16 rows, 4 column tiles, K = 8192 (64 k-tiles of 128)
+    p = syn.make_problem(16, 1024, 8192, dtype_ab="f8e4m3", dtype_cd="bf16", lb="col",
+                         dist_c="normal", beta=0.5, seed=12)
+    a = run(p, schedule=S.SPLIT_K, tile=T.T64x256, sk_grid=grid)
+    b = run(p, schedule=S.SPLIT_K, tile=T.T64x256, sk_grid=grid)
+    assert np.array_equal(a, b), f"split-K grid {grid} not bitwise repeatable"
+    close(a, p, what=f"split-K grid {grid}")
 
 
 def test_stream_k_matches_dp_on_integers():
