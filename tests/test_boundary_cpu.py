@@ -143,15 +143,13 @@ def test_describe_small_and_skinny_use_stream_k():
     assert d["tile"] == "128x128" and d["schedule"] == "stream_k" and d["ipt"] == 16
     p.close()
     q = _plan("f8e4m3")
-    # decode GEMMs: N = 8192 gives 32-64 tiles, so each tile is cut into
-    # interleaved K units that fill the 512 workgroup slots
-    for M, tile, split in ((16, "64x256", 16), (64, "64x256", 16), (128, "128x128", 8)):
-        d = q.describe(M, 8192, 28672)
-        assert d["tile"] == tile and d["schedule"] == "split_k", d
-        assert d["split"] == split and d["grid"] == d["tiles"] * split and d["bk"] == 128
-    # N = 57344: 224 tiles of 64x256 leave room for only two units per tile
-    d = q.describe(16, 57344, 8192)
-    assert d["tile"] == "64x256" and d["schedule"] == "stream_k" and d["split"] == 0, d
+    # decode GEMMs: 32-224 tiles for 512 workgroup slots, so stream-K over
+    # one workgroup per CU
+    for M, N, K, tile in ((16, 8192, 28672, "64x256"), (64, 8192, 28672, "64x256"),
+                          (128, 8192, 28672, "128x128"), (16, 57344, 8192, "64x256")):
+        d = q.describe(M, N, K)
+        assert d["tile"] == tile and d["schedule"] == "stream_k", d
+        assert d["grid"] == 256 and d["split"] == 0 and d["bk"] == 128, d
     # 448 tiles of 128x128 fill 87.5% of the slots: data-parallel
     d = q.describe(128, 57344, 8192)
     assert d["tile"] == "128x128" and d["schedule"] == "data_parallel" and d["grid"] == 448, d
