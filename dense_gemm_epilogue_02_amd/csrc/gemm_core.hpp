@@ -803,6 +803,54 @@ struct Tile {
                 }
     }
 
+    // acc = sum of the partials slot(0) .. slot(n-1), added in that order.
+    // Small accumulators fetch two partials per round, halving the number of
+    // dependent load round trips (the sum and its rounding are unchanged).
+    static constexpr bool PAIRED_FIXUP = FN * FM <= 4;
+
+    static __device__ __forceinline__ void load_partial(const float *slot, f32x4 (&t)[FN * FM * 4]) {
+        const int tid = threadIdx.x;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot);
+#pragma unroll
+        for (int g = 0; g < FN * FM * 4; ++g)
+            t[g] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((g * NT + tid) * 16), 0, SC1));
+    }
+    static __device__ __forceinline__ void accumulate(const f32x4 (&t)[FN * FM * 4], Acc &acc, bool first) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float v = t[(i * FM + j) * 4 + q][e];
+                        acc.v[i][j][q * 4 + e] = first ? v : acc.v[i][j][q * 4 + e] + v;
+                    }
+    }
+
+    template <class SlotFn>
+    static __device__ __forceinline__ void add_partials(SlotFn slot, int n, Acc &acc) {
+        if constexpr (PAIRED_FIXUP) {
+            int u = 0;
+            for (; u + 1 < n; u += 2) {
+                f32x4 t0[FN * FM * 4], t1[FN * FM * 4];
+                load_partial(slot(u), t0);
+                load_partial(slot(u + 1), t1);
+                accumulate(t0, acc, u == 0);
+                accumulate(t1, acc, false);
+            }
+            if (u < n) {
+                f32x4 t0[FN * FM * 4];
+                load_partial(slot(u), t0);
+                accumulate(t0, acc, u == 0);
+            }
+        } else {
+            for (int u = 0; u < n; ++u) add_partial(slot(u), acc, u == 0);
+        }
+    }
+
     static __device__ __forceinline__ void add_partial(const float *slot, Acc &acc, bool first) {
         const int tid = threadIdx.x;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot);
@@ -894,9 +942,9 @@ gemm_persistent(KArgs a) {
         TL::store_partial(s.partials + (size_t)v * slot_elems, acc);
         wait_vmcnt<0>();   // this thread's device-scope stores are complete
         __syncthreads();   // ... and every thread's, before the arrival is counted
-        if (arrive_last(&s.counters[t], S - 1, lds)) {   // sum the units in order c = 0 .. S-1 (deterministic)
-            for (int u = 0; u < S; ++u)
-                TL::add_partial(s.partials + ((size_t)t * S + u) * slot_elems, acc, u == 0);
+        if (arrive_last(&s.counters[t], S - 1, lds)) {
+            // sum the units in order c = 0 .. S-1 (deterministic)
+            TL::add_partials([&](int u) { return s.partials + ((size_t)t * S + u) * slot_elems; }, S, acc);
             TL::epilogue(p, a.e, tm, tn, acc);
             if (threadIdx.x == 0)
                 __hip_atomic_store(&s.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -931,11 +979,13 @@ gemm_persistent(KArgs a) {
                 const int v1 = sk_owner(tile_it0 + p.ipt - 1, T, G);
                 if (arrive_last(&s.counters[t], v1 - v0, lds)) {
                     // every contributor's partial is complete at device scope
-                    for (int u = v0; u <= v1; ++u) {
-                        const int ft = (int)(((int64_t)u * T / G) / p.ipt);
-                        const int slot = 2 * u + (t == ft ? 0 : 1);
-                        TL::add_partial(s.partials + slot * slot_elems, acc, u == v0);
-                    }
+                    TL::add_partials(
+                        [&](int k) {
+                            const int u = v0 + k;
+                            const int ft = (int)(((int64_t)u * T / G) / p.ipt);
+                            return s.partials + (size_t)(2 * u + (t == ft ? 0 : 1)) * slot_elems;
+                        },
+                        v1 - v0 + 1, acc);
                     TL::epilogue(p, a.e, tm, tn, acc);
                     if (threadIdx.x == 0)
                         __hip_atomic_store(&s.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
