@@ -383,8 +383,12 @@ template <int R, int ESZ, int NT, int CH> struct DirectStager {
 // PIPE: 0 = fragment reads scheduled by the compiler; 3 = the fragments of
 // substep s+1 are read (as one burst) before the MFMAs of substep s, with
 // scheduling fences.
+// COPY_WAVES: how many waves issue the LDS-DMA copies (0 = all). With half
+// of them (one per SIMD), the other wave of every SIMD starts its MFMAs right
+// after the barrier while its partner waits on the CU's copy queue, which
+// takes ~1100 cycles to accept the 64 KiB of a 256x256 k-tile.
 template <int FAM_, bool A_KC, bool B_KC, int BM_, int BN_, int WM_, int WN_, int KB = 128,
-          int STAGES = 2, int PIPE = 0>
+          int STAGES = 2, int PIPE = 0, int COPY_WAVES = 0>
 struct Tile {
     static constexpr int FAM = FAM_, BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int CH = KB / 16;
@@ -419,8 +423,11 @@ struct Tile {
     // registers and transposed.
     using SA = Stager<BM, ESZ, false, NT, CH>;
     using SB = Stager<BN, ESZ, false, NT, CH>;
-    using DA = DirectStager<BM, ESZ, NT, CH>;
-    using DB = DirectStager<BN, ESZ, NT, CH>;
+    static constexpr int COPY_NT = COPY_WAVES > 0 ? 64 * COPY_WAVES : NT;
+    static_assert(COPY_NT <= NT && NT % COPY_NT == 0, "copy waves");
+    static_assert(COPY_NT == NT || STAGES == 2, "subset copies with the two-stage loop only");
+    using DA = DirectStager<BM, ESZ, COPY_NT, CH>;
+    using DB = DirectStager<BN, ESZ, COPY_NT, CH>;
     static constexpr int LPS = DA::IPW + DB::IPW;   // direct loads per stage per wave
 
     struct Acc {
@@ -497,14 +504,15 @@ struct Tile {
         const char *base;
         uint32_t ld;
         int rl, kl;
+        const bool copy_wave = COPY_NT == NT || uniform(tid >> 6) < COPY_NT / 64;
         if constexpr (A_KC) {
-            L.da.issue(kt, k_left, stage, tid);
+            if (copy_wave) L.da.issue(kt, k_left, stage, tid);
         } else {
             a_tile(p, tm, kt, base, ld, rl, kl);
             L.sa.load(base, ld, rl, kl, tid);
         }
         if constexpr (B_KC) {
-            L.db.issue(kt, k_left, lds + B_OFF + st * B_BYTES, tid);
+            if (copy_wave) L.db.issue(kt, k_left, lds + B_OFF + st * B_BYTES, tid);
         } else {
             b_tile(p, tn, kt, base, ld, rl, kl);
             L.sb.load(base, ld, rl, kl, tid);

@@ -5,8 +5,21 @@
 
 // 128-byte LDS rows, two stages, compiler-scheduled fragment reads (PIPE 0):
 // in interleaved same-box measurements this matched or beat the hand-ordered
-// pipelines (PIPE 3 / 5) on the layer GEMMs.
-#define MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN) mg::Tile<FAM, AKC, BKC, BM, BN, WM, WN, 128, 2, 0>
+// pipelines (PIPE 3) on the layer GEMMs.
+namespace mg {
+template <int FAM, bool AKC, bool BKC, int BM, int BN, int WM, int WN> struct TileCfg {
+    using type = Tile<FAM, AKC, BKC, BM, BN, WM, WN, 128, 2, 0>;
+};
+// 256x256 with both operands K-contiguous: the LDS-DMA copies are issued by
+// four of the eight waves (one per SIMD); 2-4 % faster than all eight on the
+// transformer-layer shapes in interleaved same-box runs.
+template <int FAM> struct TileCfg<FAM, true, true, 256, 256, 2, 4> {
+    using type = Tile<FAM, true, true, 256, 256, 2, 4, 128, 2, 0, 4>;
+};
+}  // namespace mg
+
+#define MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN) \
+    typename mg::TileCfg<FAM, AKC, BKC, BM, BN, WM, WN>::type
 
 #define MG_ROW(FAM, AKC, BKC, TILEID, BM, BN, WM, WN, GROUPED) \
     mg::make_entry<MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN), GROUPED>(TILEID, AKC, BKC)
