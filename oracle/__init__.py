@@ -53,7 +53,7 @@ def lib():
         L.oracle_encode.argtypes = [ctypes.c_int, ctypes.c_double]
         L.oracle_decode_n.argtypes = [ctypes.c_int, vp, ctypes.c_int64, vp]
         L.oracle_encode_n.argtypes = [ctypes.c_int, vp, ctypes.c_int64, vp]
-        common = [ctypes.c_int] * 8 + [ctypes.c_int64] * 3 + [vp] * 3 + \
+        common = [ctypes.c_int] * 8 + [ctypes.c_int64] * 3 + [vp] * 4 + \
                  [ctypes.c_float] * 4
         L.oracle_gemm_rows.restype = ctypes.c_int
         L.oracle_gemm_rows.argtypes = common + [i64p, ctypes.c_int64, vp, vp, vp]
@@ -104,26 +104,43 @@ def _scalars(p):
     return float(p.alpha), float(p.beta), float(sa), float(sb)
 
 
+# Activations of the epilogue (the codes the C oracle takes).
+ACT = {"identity": 0, "relu": 1, "sigmoid": 2, "tanh": 3}
+
+
 def _operands(p):
     from synthetic import raw   # storage bytes only
     A = raw(p.A)
     B = raw(p.B)
     C = raw(p.C) if (p.C is not None and p.beta != 0.0) else None
-    return A, B, C
+    bias = raw(p.bias) if getattr(p, "bias", None) is not None else None
+    return A, B, C, bias
 
 
-def _head(p, relu):
+def _act_code(relu: bool, act: Optional[str]) -> int:
+    if act is None:
+        return ACT["relu"] if relu else ACT["identity"]
+    if relu and act != "relu":
+        raise ValueError("relu=True conflicts with act=%r" % act)
+    return ACT[act]
+
+
+def _head(p, relu, act=None):
     return (DT[p.dtype_ab], DT[p.dtype_ab], DT[p.dtype_cd], DT[p.dtype_cd],
-            LAYOUT[p.la], LAYOUT[p.lb], LAYOUT[p.lc], int(bool(relu)),
+            LAYOUT[p.la], LAYOUT[p.lb], LAYOUT[p.lc], _act_code(relu, act),
             p.M, p.N, p.K)
 
 
-def gemm(p, relu: bool = False, rows: Optional[Sequence[int]] = None) -> Result:
-    """Full rows of D for the problem ``p`` (a ``synthetic.Problem``).
+def gemm(p, relu: bool = False, rows: Optional[Sequence[int]] = None,
+         act: Optional[str] = None) -> Result:
+    """Full rows of D for the problem ``p`` (a ``synthetic.Problem``; its
+    ``bias``, if any, is added to every row before the activation).
 
     ``rows`` = None computes all M rows; outputs are [n_rows, N] arrays.
+    ``act`` names the activation ("identity", "relu", "sigmoid", "tanh");
+    ``relu=True`` is shorthand for act="relu".
     """
-    A, B, C = _operands(p)
+    A, B, C, bias = _operands(p)
     al, be, sa, sb = _scalars(p)
     if rows is None:
         rows_arr, n = None, p.M
@@ -135,17 +152,17 @@ def gemm(p, relu: bool = False, rows: Optional[Sequence[int]] = None) -> Result:
     d = np.empty((n, p.N), dtype=np.uint32)
     rp = None if rows_arr is None else rows_arr.ctypes.data_as(
         ctypes.POINTER(ctypes.c_int64))
-    rc = lib().oracle_gemm_rows(*_head(p, relu), _ptr(A), _ptr(B), _ptr(C),
-                                al, be, sa, sb, rp, n, _ptr(ref), _ptr(S),
+    rc = lib().oracle_gemm_rows(*_head(p, relu, act), _ptr(A), _ptr(B), _ptr(C),
+                                _ptr(bias), al, be, sa, sb, rp, n, _ptr(ref), _ptr(S),
                                 _ptr(d))
     if rc != 0:
         raise ValueError("oracle_gemm_rows: bad arguments")
     return Result(ref, S, d, p.dtype_cd)
 
 
-def gemm_entries(p, ii, jj, relu: bool = False) -> Result:
+def gemm_entries(p, ii, jj, relu: bool = False, act: Optional[str] = None) -> Result:
     """Selected outputs D[ii[t], jj[t]], each computed on its own."""
-    A, B, C = _operands(p)
+    A, B, C, bias = _operands(p)
     al, be, sa, sb = _scalars(p)
     ii = np.ascontiguousarray(np.asarray(ii, dtype=np.int64))
     jj = np.ascontiguousarray(np.asarray(jj, dtype=np.int64))
@@ -154,8 +171,8 @@ def gemm_entries(p, ii, jj, relu: bool = False) -> Result:
     S = np.empty(n, dtype=np.float64)
     d = np.empty(n, dtype=np.uint32)
     P = ctypes.POINTER(ctypes.c_int64)
-    rc = lib().oracle_gemm_entries(*_head(p, relu), _ptr(A), _ptr(B), _ptr(C),
-                                   al, be, sa, sb, ii.ctypes.data_as(P),
+    rc = lib().oracle_gemm_entries(*_head(p, relu, act), _ptr(A), _ptr(B), _ptr(C),
+                                   _ptr(bias), al, be, sa, sb, ii.ctypes.data_as(P),
                                    jj.ctypes.data_as(P), n, _ptr(ref), _ptr(S),
                                    _ptr(d))
     if rc != 0:
@@ -163,6 +180,6 @@ def gemm_entries(p, ii, jj, relu: bool = False) -> Result:
     return Result(ref, S, d, p.dtype_cd)
 
 
-def grouped(problems: List, relu: bool = False) -> List[Result]:
+def grouped(problems: List, relu: bool = False, act: Optional[str] = None) -> List[Result]:
     """Grouped GEMM = the independent single GEMMs, one after another."""
-    return [gemm(p, relu) for p in problems]
+    return [gemm(p, relu, act=act) for p in problems]

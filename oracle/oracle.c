@@ -2,7 +2,7 @@
  * CPU oracle for D = alpha * A * B + beta * C   (TEST INFRASTRUCTURE ONLY)
  *
  * A plain, slow, obviously correct fp64 implementation of the general matrix
- * multiply with the fused ReLU epilogue. Only the test-suite, the smoke check
+ * multiply with the fused bias / activation epilogue. Only the test-suite, the smoke check
  * and the benchmark's CPU-baseline leg load this library; the GPU library
  * never links or calls it, and it shares no code with the GPU library.
  *
@@ -17,13 +17,20 @@
  *   - "Python packages associated with CUTLASS", Current functionality:
  *     GEMM, fused elementwise epilogue, grouped GEMM (independent problems).
  *   - "Generating State-of-the-Art GEMMs with TorchInductor's CuteDSL backend",
- *     section 5.1: FP8 GEMM as a scaled mm (per-tensor scales here).
+ *     section 5.1: FP8 GEMM as a scaled mm (per-tensor scales here);
+ *     section 7: the epilogue-fusion kernels take activations ReLU, Sigmoid
+ *     and Tanh.
+ *   - "CUTLASS Python接口" (kwkr.cn), the fused BiasAdd-ReLU GEMM example:
+ *     Output = Activation(Input * Weight + Bias), Bias a length-N vector
+ *     added to every row.
  *
  * Definition computed, for each selected output (i, j):
  *   acc     = sum_{k=0}^{K-1} a(i,k) * b(k,j)            fp64, increasing k
  *   acc     = acc * s_A * s_B                             (scales; 1 unless fp8)
- *   v       = alpha * acc + (beta != 0 ? beta * c(i,j) : 0)
- *   v       = relu ? (v > 0 ? v : +0) : v
+ *   v       = alpha * acc + (beta != 0 ? beta * c(i,j) : 0) + bias(j)
+ *             (bias(j) = 0 without a bias vector)
+ *   v       = act(v): identity; ReLU: v > 0 ? v : +0; Sigmoid: 1/(1+e^-v);
+ *             Tanh: tanh(v)  (all in fp64)
  *   ref     = v                                           (fp64, unrounded)
  *   d_exact = v rounded once, to nearest even, to element_D
  *   S       = |alpha * s_A * s_B| * sum_k |a(i,k) * b(k,j)|  (tolerance scale)
@@ -39,6 +46,7 @@
 
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F8E4M3 = 3 };
 enum { LAYOUT_ROW = 0, LAYOUT_COL = 1 };
+enum { ACT_IDENTITY = 0, ACT_RELU = 1, ACT_SIGMOID = 2, ACT_TANH = 3 };
 
 /* ---- exact decoders, one per storage format (sign, exponent, fraction) ---- */
 
@@ -140,13 +148,24 @@ static double elem(const void *base, int dtype, int layout, int64_t rows,
 
 static int valid_dtype(int d) { return d >= DT_F32 && d <= DT_F8E4M3; }
 
-/* Epilogue of one output: scales, linear combination, activation. */
+/* Epilogue of one output: scales, linear combination, bias, activation. */
 static double finish(double acc, double sab, double alpha, double beta,
-                     double c, int relu) {
+                     double c, double bias, int act) {
     double v = alpha * (acc * sab);
     if (beta != 0.0) v += beta * c;
-    if (relu) v = (v > 0.0) ? v : 0.0;
+    v += bias;
+    switch (act) {
+    case ACT_RELU: v = (v > 0.0) ? v : 0.0; break;
+    case ACT_SIGMOID: v = 1.0 / (1.0 + exp(-v)); break;
+    case ACT_TANH: v = tanh(v); break;
+    default: break;
+    }
     return v;
+}
+
+/* bias(j): element j of the length-N vector in element type dtype, or 0. */
+static double bias_at(const void *bias, int dtype, int64_t j) {
+    return bias ? oracle_decode(dtype, load_bits(bias, dtype, j)) : 0.0;
 }
 
 /*
@@ -156,13 +175,15 @@ static double finish(double acc, double sab, double alpha, double beta,
  * optional). Returns 0 on success, -1 on bad arguments.
  */
 int oracle_gemm_rows(int dtA, int dtB, int dtC, int dtD, int la, int lb,
-                     int lc, int relu, int64_t M, int64_t N, int64_t K,
-                     const void *A, const void *B, const void *C, float alpha,
+                     int lc, int act, int64_t M, int64_t N, int64_t K,
+                     const void *A, const void *B, const void *C,
+                     const void *bias, float alpha,
                      float beta, float scale_a, float scale_b,
                      const int64_t *rows, int64_t n_rows, double *ref,
                      double *S, uint32_t *d_bits) {
     if (!valid_dtype(dtA) || !valid_dtype(dtB) || !valid_dtype(dtC) ||
-        !valid_dtype(dtD) || M < 0 || N < 0 || K < 0 || !ref)
+        !valid_dtype(dtD) || M < 0 || N < 0 || K < 0 || !ref ||
+        act < ACT_IDENTITY || act > ACT_TANH)
         return -1;
     if (rows == NULL) n_rows = M;
     const double al = (double)alpha, be = (double)beta;
@@ -184,7 +205,7 @@ int oracle_gemm_rows(int dtA, int dtB, int dtC, int dtD, int la, int lb,
         }
         for (int64_t j = 0; j < N; ++j) {
             double c = (be != 0.0) ? elem(C, dtC, lc, M, N, i, j) : 0.0;
-            double v = finish(acc[j], sab, al, be, c, relu);
+            double v = finish(acc[j], sab, al, be, c, bias_at(bias, dtC, j), act);
             ref[r * N + j] = v;
             if (S) S[r * N + j] = fabs(al * sab) * sab_abs[j];
             if (d_bits) d_bits[r * N + j] = oracle_encode(dtD, v);
@@ -200,13 +221,14 @@ int oracle_gemm_rows(int dtA, int dtB, int dtC, int dtD, int la, int lb,
  * Outputs ref[t], S[t] (optional), d_bits[t] (optional).
  */
 int oracle_gemm_entries(int dtA, int dtB, int dtC, int dtD, int la, int lb,
-                        int lc, int relu, int64_t M, int64_t N, int64_t K,
+                        int lc, int act, int64_t M, int64_t N, int64_t K,
                         const void *A, const void *B, const void *C,
-                        float alpha, float beta, float scale_a, float scale_b,
+                        const void *bias, float alpha, float beta, float scale_a, float scale_b,
                         const int64_t *ii, const int64_t *jj, int64_t n,
                         double *ref, double *S, uint32_t *d_bits) {
     if (!valid_dtype(dtA) || !valid_dtype(dtB) || !valid_dtype(dtC) ||
-        !valid_dtype(dtD) || M < 0 || N < 0 || K < 0 || !ref || !ii || !jj)
+        !valid_dtype(dtD) || M < 0 || N < 0 || K < 0 || !ref || !ii || !jj ||
+        act < ACT_IDENTITY || act > ACT_TANH)
         return -1;
     const double al = (double)alpha, be = (double)beta;
     const double sab = (double)scale_a * (double)scale_b;
@@ -222,7 +244,7 @@ int oracle_gemm_entries(int dtA, int dtB, int dtC, int dtD, int la, int lb,
             sabs += fabs(p);
         }
         double c = (be != 0.0) ? elem(C, dtC, lc, M, N, i, j) : 0.0;
-        double v = finish(acc, sab, al, be, c, relu);
+        double v = finish(acc, sab, al, be, c, bias_at(bias, dtC, j), act);
         ref[t] = v;
         if (S) S[t] = fabs(al * sab) * sabs;
         if (d_bits) d_bits[t] = oracle_encode(dtD, v);

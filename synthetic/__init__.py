@@ -80,6 +80,7 @@ class Problem:
     la: str = ROW
     lb: str = ROW
     lc: str = ROW
+    bias: Optional[torch.Tensor] = None   # length-N row vector in dtype_cd (None: no bias)
 
     @property
     def flops(self) -> int:
@@ -112,8 +113,10 @@ def make_problem(M: int, N: int, K: int, *, dtype_ab: str, dtype_cd: str,
                  dist_a: str = "normal", dist_b: str = "normal",
                  dist_c: Optional[str] = None, std_b: float = 1.0,
                  alpha: float = 1.0, beta: float = 0.0,
+                 dist_bias: Optional[str] = None,
                  seed: int = 0, rng=None) -> Problem:
-    """Draw A (M x K), B (K x N) and, if ``dist_c`` is given, C (M x N)."""
+    """Draw A (M x K), B (K x N), then C (M x N) if ``dist_c`` is given and a
+    length-N bias if ``dist_bias`` is given (in that order)."""
     rng = np.random.default_rng(seed) if rng is None else rng
     a32 = _draw(rng, (M, K), dist_a)
     b32 = _draw(rng, (K, N), dist_b, std_b)
@@ -121,6 +124,9 @@ def make_problem(M: int, N: int, K: int, *, dtype_ab: str, dtype_cd: str,
     if dist_c is not None:
         c32 = _draw(rng, (M, N), dist_c)
         c = cast(to_storage(c32, lc), dtype_cd)
+    bias = None
+    if dist_bias is not None:
+        bias = cast(_draw(rng, (N,), dist_bias), dtype_cd)
     sa = sb = None
     if dtype_ab == F8:
         A, sa = quantize_e4m3(to_storage(a32, la))
@@ -129,14 +135,14 @@ def make_problem(M: int, N: int, K: int, *, dtype_ab: str, dtype_cd: str,
         A = cast(to_storage(a32, la), dtype_ab)
         B = cast(to_storage(b32, lb), dtype_ab)
     return Problem(M, N, K, A, B, c, alpha, beta, sa, sb, dtype_ab, dtype_cd,
-                   la, lb, lc)
+                   la, lb, lc, bias)
 
 
 def integer_problem(M: int, N: int, K: int, *, dtype_ab: str, dtype_cd: str,
                     la: str = ROW, lb: str = ROW, lc: str = ROW,
                     lo: int = -2, hi: int = 2, beta: float = 1.0,
                     alpha: float = 1.0, with_c: bool = True,
-                    seed: int = 0) -> Problem:
+                    with_bias: bool = False, seed: int = 0) -> Problem:
     """Integer-valued operands in [lo, hi] (exact in every storage type)."""
     rng = np.random.default_rng(seed)
     a32 = rng.integers(lo, hi + 1, size=(M, K)).astype(np.float32)
@@ -145,11 +151,14 @@ def integer_problem(M: int, N: int, K: int, *, dtype_ab: str, dtype_cd: str,
     if with_c:
         c32 = rng.integers(lo, hi + 1, size=(M, N)).astype(np.float32)
         c = cast(to_storage(c32, lc), dtype_cd)
+    bias = None
+    if with_bias:
+        bias = cast(rng.integers(lo, hi + 1, size=(N,)).astype(np.float32), dtype_cd)
     A = cast(to_storage(a32, la), dtype_ab)
     B = cast(to_storage(b32, lb), dtype_ab)
     sa = sb = (1.0 if dtype_ab == F8 else None)
     return Problem(M, N, K, A, B, c, alpha, beta if with_c else 0.0, sa, sb,
-                   dtype_ab, dtype_cd, la, lb, lc)
+                   dtype_ab, dtype_cd, la, lb, lc, bias)
 
 
 # ---------------------------------------------------------------------------

@@ -389,3 +389,96 @@ def test_acceptance_rules():
     with pytest.raises(AssertionError):
         acceptance.check_close([1.1], [1.0], [1.0], "f16", "f16")
     acceptance.check_exact([0.0, 1.0], [-0.0, 1.0])
+
+
+# ---------------------------------------------------------------- bias + activations
+
+def _k0_problem(dtype, values, bias_values, beta=1.0):
+    """K = 0 makes D = act(beta * C + bias) with no products involved."""
+    M, N = len(values), len(values[0])
+    p = syn.make_problem(M, N, 0, dtype_ab=dtype, dtype_cd=dtype, dist_c="zeros",
+                         beta=beta, seed=20)
+    _with_operand(p, "C", np.array(values, dtype=np.float32), dtype)
+    p.bias = syn.cast(np.array(bias_values, dtype=np.float32), dtype)
+    return p
+
+
+def test_sigmoid_tanh_closed_forms():
+    ln3, ln2 = float(np.float32(np.log(3.0))), float(np.float32(np.log(2.0)))
+    p = _k0_problem("f32", [[0.0, ln3, -ln3, ln2]], [0.0, 0.0, 0.0, 0.0])
+    s = oracle.gemm(p, act="sigmoid").ref[0]
+    assert s[0] == 0.5                                   # sigma(0) = 1/2
+    assert abs(s[1] - 0.75) < 1e-8 and abs(s[2] - 0.25) < 1e-8   # sigma(ln 3) = 3/4
+    t = oracle.gemm(p, act="tanh").ref[0]
+    assert t[0] == 0.0                                   # tanh(0) = 0
+    assert abs(t[3] - 0.6) < 1e-8                        # tanh(ln 2) = 3/5
+    assert t[2] == -t[1]                                 # odd
+    # saturation: sigma(40) rounds to 1 in fp64, tanh(40) too
+    q = _k0_problem("f32", [[40.0, -40.0]], [0.0, 0.0])
+    assert oracle.gemm(q, act="sigmoid").ref[0][0] == 1.0
+    assert oracle.gemm(q, act="tanh").ref[0][0] == 1.0
+    assert 0.0 < oracle.gemm(q, act="sigmoid").ref[0][1] < 1e-17
+
+
+def test_sigmoid_is_half_shifted_tanh():
+    """sigma(x) = (1 + tanh(x/2)) / 2 ties the two activations together, so a
+    sign or scale slip in either one fails."""
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((6, 20)) * 4).astype(np.float32)
+    p = _k0_problem("f32", x, np.zeros(20, dtype=np.float32))
+    s = oracle.gemm(p, act="sigmoid").ref
+    p.beta = 0.5                                         # v = x / 2 exactly
+    t = oracle.gemm(p, act="tanh").ref
+    assert np.allclose(s, (1.0 + t) / 2.0, rtol=0, atol=4e-16)
+    assert ((s > 0) & (s < 1)).all()
+
+
+@pytest.mark.parametrize("dtype_ab,dtype_cd", [("f32", "f32"), ("f16", "f16"),
+                                               ("bf16", "bf16"), ("f8e4m3", "bf16")])
+@pytest.mark.parametrize("act", ["identity", "relu"])
+def test_bias_brute_force_fraction_tiny(dtype_ab, dtype_cd, act):
+    rng = np.random.default_rng(22)
+    for trial in range(5):
+        M, N, K = (int(v) for v in rng.integers(1, 7, 3))
+        la, lb, lc = (LAYOUTS[int(v)] for v in rng.integers(0, 2, 3))
+        p = syn.integer_problem(M, N, K, dtype_ab=dtype_ab, dtype_cd=dtype_cd,
+                                la=la, lb=lb, lc=lc, lo=-5, hi=5,
+                                alpha=float(rng.choice([1.0, -0.5])),
+                                beta=float(rng.choice([0.0, 1.0])),
+                                with_bias=True, seed=200 + trial)
+        r = oracle.gemm(p, act=act)
+        exact = _fraction_gemm(p, False)
+        bias = p.bias.to(torch.float64).numpy()
+        for i in range(M):
+            for j in range(N):
+                v = exact[i][j] + Fraction(float(bias[j]))
+                if act == "relu" and v <= 0:
+                    v = Fraction(0)
+                assert Fraction(float(r.ref[i, j])) == v
+
+
+def test_bias_is_per_column():
+    """A planted mistake (the bias indexed by row) fails: with M != N and a
+    bias that differs per column, D - D(no bias) must equal bias[j] in every
+    row."""
+    p = syn.integer_problem(5, 7, 9, dtype_ab="bf16", dtype_cd="bf16", lo=-2, hi=2,
+                            with_bias=True, seed=23)
+    with_b = oracle.gemm(p).ref
+    bias = p.bias.to(torch.float64).numpy()
+    p.bias = None
+    without = oracle.gemm(p).ref
+    diff = with_b - without
+    assert np.array_equal(diff, np.tile(bias, (5, 1)))
+    assert not np.array_equal(diff, np.tile(bias[:5, None], (1, 7)))
+
+
+def test_bias_activation_rows_equal_entries():
+    p = syn.make_problem(12, 40, 33, dtype_ab="f16", dtype_cd="f16", lc="col",
+                         dist_c="normal", beta=0.5, dist_bias="normal", seed=24)
+    for act in ("sigmoid", "tanh"):
+        rows = oracle.gemm(p, act=act)
+        rng = np.random.default_rng(25)
+        ii, jj = rng.integers(0, 12, 60), rng.integers(0, 40, 60)
+        ent = oracle.gemm_entries(p, ii, jj, act=act)
+        assert np.array_equal(ent.ref, rows.ref[ii, jj])
+        assert np.array_equal(ent.d_bits, rows.d_bits[ii, jj])
