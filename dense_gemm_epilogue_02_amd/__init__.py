@@ -37,6 +37,8 @@ class Layout(IntEnum):
 class Epilogue(IntEnum):
     LINEAR = 0
     RELU = 1
+    SIGMOID = 2
+    TANH = 3
 
 
 class Status(IntEnum):
@@ -103,6 +105,8 @@ def _load():
     L.gemm_plan_run.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp]
     L.gemm_plan_run_scaled.restype = st
     L.gemm_plan_run_scaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp, vp, vp]
+    L.gemm_plan_run_ex.restype = st
+    L.gemm_plan_run_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp, vp, vp]
     L.grouped_gemm_run.restype = st
     L.grouped_gemm_run.argtypes = [vp, ctypes.POINTER(gemm_problem), i32, f32, f32, vp]
     L.gemm_plan_describe.restype = st
@@ -124,7 +128,7 @@ lib = _load()
 
 EXPORTED = ("gemm_plan_create", "gemm_plan_create_simple", "gemm_plan_destroy",
             "gemm_plan_set_config", "gemm_plan_run", "gemm_plan_run_scaled",
-            "grouped_gemm_run", "gemm_plan_describe", "gemm_last_error",
+            "gemm_plan_run_ex", "grouped_gemm_run", "gemm_plan_describe", "gemm_last_error",
             "gemm_status_string", "gemm_supported_count", "gemm_supported_get",
             "gemm_version")
 
@@ -186,6 +190,12 @@ def gemm_plan_run_scaled(plan: int, A, B, C, D, M: int, N: int, K: int, alpha: f
                          beta: float, scale_a, scale_b, stream=None) -> None:
     _check(lib.gemm_plan_run_scaled(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), M, N, K, alpha,
                                     beta, _ptr(scale_a), _ptr(scale_b), _stream(stream)))
+
+
+def gemm_plan_run_ex(plan: int, A, B, C, D, bias, M: int, N: int, K: int, alpha: float,
+                     beta: float, scale_a=None, scale_b=None, stream=None) -> None:
+    _check(lib.gemm_plan_run_ex(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(bias), M, N, K,
+                                alpha, beta, _ptr(scale_a), _ptr(scale_b), _stream(stream)))
 
 
 def grouped_gemm_run(plan: int, problems: Sequence[tuple], alpha: float = 1.0,
@@ -257,13 +267,21 @@ def _need(t, n: int, name: str, dtype: Dtype):
 class Plan:
     """A plan bound to element types, layouts and epilogue (reusable across shapes)."""
 
+    _ACT = {"linear": Epilogue.LINEAR, "identity": Epilogue.LINEAR, "relu": Epilogue.RELU,
+            "sigmoid": Epilogue.SIGMOID, "tanh": Epilogue.TANH}
+
     def __init__(self, dtype_ab="bf16", dtype_cd=None, la="row", lb="row", lc="row",
-                 relu: bool = False):
+                 relu: bool = False, activation: Optional[str] = None):
         dtype_cd = dtype_cd or ("bf16" if dtype_ab == "f8e4m3" else dtype_ab)
         self.dab, self.dcd = _TORCH_DT[dtype_ab], _TORCH_DT[dtype_cd]
+        if activation is None:
+            epi = Epilogue.RELU if relu else Epilogue.LINEAR
+        else:
+            if relu and activation != "relu":
+                raise ValueError(f"relu=True conflicts with activation={activation!r}")
+            epi = self._ACT[activation]
         self.handle = gemm_plan_create(self.dab, self.dab, self.dcd, self.dcd, Dtype.F32,
-                                       _LAYOUT[la], _LAYOUT[lb], _LAYOUT[lc],
-                                       Epilogue.RELU if relu else Epilogue.LINEAR)
+                                       _LAYOUT[la], _LAYOUT[lb], _LAYOUT[lc], epi)
 
     def close(self):
         if self.handle:
@@ -295,9 +313,14 @@ class Plan:
                 _need(C, M * N, "C", self.dcd)
 
     def run(self, A, B, C, D, M, N, K, alpha=1.0, beta=0.0, scale_a=None, scale_b=None,
-            stream=None):
+            stream=None, bias=None):
         self.check(A, B, C, D, M, N, K, beta)
-        if scale_a is None and scale_b is None:
+        if bias is not None:
+            if M and N:
+                _need(bias, N, "bias", self.dcd)
+            gemm_plan_run_ex(self.handle, A, B, C, D, bias, M, N, K, alpha, beta, scale_a,
+                             scale_b, stream)
+        elif scale_a is None and scale_b is None:
             gemm_plan_run(self.handle, A, B, C, D, M, N, K, alpha, beta, stream)
         else:
             gemm_plan_run_scaled(self.handle, A, B, C, D, M, N, K, alpha, beta, scale_a,

@@ -247,13 +247,15 @@ int min_iters(int fam) { return fam == FAM_F32 ? 1 : 8; }
 // `occ_of` gives workgroups per CU for an entry (live query or estimate).
 template <class OccFn>
 gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const void *C, const void *D,
-                   int64_t M, int64_t N, int64_t K, float beta, int cus, OccFn occ_of, Decision &d) {
+                   const void *bias, int64_t M, int64_t N, int64_t K, float beta, int cus, OccFn occ_of,
+                   Decision &d) {
     const int fam = pl->fam;
     const int esz = elem_bytes(fam), osz = out_bytes(fam);
     const bool a_kc = pl->la == GEMM_ROW_MAJOR, b_kc = pl->lb == GEMM_COL_MAJOR;
     d.vec_cd = (pl->lc == GEMM_ROW_MAJOR && N % 4 == 0 &&
                 reinterpret_cast<uintptr_t>(D) % (4 * osz) == 0 &&
-                (beta == 0.0f || reinterpret_cast<uintptr_t>(C) % (4 * osz) == 0))
+                (beta == 0.0f || reinterpret_cast<uintptr_t>(C) % (4 * osz) == 0) &&
+                reinterpret_cast<uintptr_t>(bias) % (4 * osz) == 0)
                    ? 1 : 0;
     if (pl->tile != GEMM_TILE_GENERIC) {
         gemm_tile t = pl->tile == GEMM_TILE_AUTO ? pick_tile(fam, M, N, cus) : pl->tile;
@@ -438,13 +440,15 @@ Prob make_prob(const void *A, const void *B, const void *C, void *D, int64_t M, 
     return p;
 }
 
-EpiArgs make_epi(const gemm_plan_s *pl, float alpha, float beta, const float *sa, const float *sb) {
+EpiArgs make_epi(const gemm_plan_s *pl, float alpha, float beta, const float *sa, const float *sb,
+                 const void *bias) {
     EpiArgs e;
     e.alpha = alpha;
     e.beta = beta;
     e.scale_a = sa;
     e.scale_b = sb;
-    e.relu = pl->epi == GEMM_EPI_RELU ? 1 : 0;
+    e.bias = bias;
+    e.act = (int)pl->epi;
     e.lc_row = pl->lc == GEMM_ROW_MAJOR ? 1 : 0;
     return e;
 }
@@ -462,7 +466,7 @@ gemm_status run_generic(const gemm_plan_s *pl, const Prob &p, const EpiArgs &ep,
 
 gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C, void *D, int64_t M,
                     int64_t N, int64_t K, float alpha, float beta, const float *sa, const float *sb,
-                    void *stream) {
+                    const void *bias, void *stream) {
     if (!plan_ok(pl)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_run: invalid plan handle");
     gemm_status st = validate_problem(pl, A, B, C, D, M, N, K, beta, "gemm_plan_run");
     if (st != GEMM_OK) return st;
@@ -474,14 +478,14 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
     if ((st = device_cus(dev, &cus)) != GEMM_OK) return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     Decision d;
-    st = decide(pl, A, B, C, D, M, N, K, beta, cus,
+    st = decide(pl, A, B, C, D, bias, M, N, K, beta, cus,
                 [&](const KernelEntry *e, int *occ) {
                     return kernel_occupancy(dev, e->fn_persistent, e->nt, occ);
                 },
                 d);
     if (st != GEMM_OK) return st;
     const Prob p = make_prob(A, B, C, D, M, N, K, d);
-    const EpiArgs ep = make_epi(pl, alpha, beta, sa, sb);
+    const EpiArgs ep = make_epi(pl, alpha, beta, sa, sb, bias);
     if (!d.e) {
         st = run_generic(pl, p, ep, hs);
         if (st == GEMM_OK) note_stream(pl, hs);
@@ -525,8 +529,8 @@ gemm_status gemm_plan_create(gemm_plan_t *out, gemm_dtype a, gemm_dtype b, gemm_
     auto bad_layout = [](gemm_layout l) { return l != GEMM_ROW_MAJOR && l != GEMM_COL_MAJOR; };
     if (bad_layout(la) || bad_layout(lb) || bad_layout(lc))
         return fail(GEMM_INVALID_ARG, "gemm_plan_create: layout must be ROW_MAJOR or COL_MAJOR");
-    if (epi != GEMM_EPI_LINEAR && epi != GEMM_EPI_RELU)
-        return fail(GEMM_INVALID_ARG, "gemm_plan_create: epilogue must be LINEAR or RELU");
+    if (epi < GEMM_EPI_LINEAR || epi > GEMM_EPI_TANH)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_create: epilogue must be LINEAR, RELU, SIGMOID or TANH");
     int fam = -1;
     for (const Tuple &t : kSupported)
         if (t.a == a && t.b == b && t.c == c && t.d == d && t.acc == acc) fam = t.fam;
@@ -599,13 +603,19 @@ gemm_status gemm_plan_set_config(gemm_plan_t p, gemm_schedule s, gemm_tile t, in
 
 gemm_status gemm_plan_run(gemm_plan_t p, const void *A, const void *B, const void *C, void *D, int64_t M,
                           int64_t N, int64_t K, float alpha, float beta, void *stream) {
-    return run_one(p, A, B, C, D, M, N, K, alpha, beta, nullptr, nullptr, stream);
+    return run_one(p, A, B, C, D, M, N, K, alpha, beta, nullptr, nullptr, nullptr, stream);
 }
 
 gemm_status gemm_plan_run_scaled(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,
                                  int64_t M, int64_t N, int64_t K, float alpha, float beta,
                                  const float *scale_a, const float *scale_b, void *stream) {
-    return run_one(p, A, B, C, D, M, N, K, alpha, beta, scale_a, scale_b, stream);
+    return run_one(p, A, B, C, D, M, N, K, alpha, beta, scale_a, scale_b, nullptr, stream);
+}
+
+gemm_status gemm_plan_run_ex(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,
+                             const void *bias, int64_t M, int64_t N, int64_t K, float alpha,
+                             float beta, const float *scale_a, const float *scale_b, void *stream) {
+    return run_one(p, A, B, C, D, M, N, K, alpha, beta, scale_a, scale_b, bias, stream);
 }
 
 gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32_t count, float alpha,
@@ -631,7 +641,7 @@ gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32
     const bool a_kc = pl->la == GEMM_ROW_MAJOR, b_kc = pl->lb == GEMM_COL_MAJOR;
     const KernelEntry *e = registry().find(pl->fam, a_kc, b_kc, TILE_128x128);
     const int esz = elem_bytes(pl->fam), osz = out_bytes(pl->fam);
-    const EpiArgs ep = make_epi(pl, alpha, beta, nullptr, nullptr);
+    const EpiArgs ep = make_epi(pl, alpha, beta, nullptr, nullptr, nullptr);
 
     std::vector<GroupDesc> table;
     std::vector<int32_t> scalar_path;
@@ -750,7 +760,7 @@ gemm_status gemm_plan_describe(gemm_plan_t pl, int64_t M, int64_t N, int64_t K, 
     // aligned stand-in pointers: describes the vector-load path
     const void *fake = reinterpret_cast<const void *>(uintptr_t(1) << 20);
     Decision d;
-    gemm_status st = decide(pl, fake, fake, fake, fake, M, N, K, 1.0f, cus,
+    gemm_status st = decide(pl, fake, fake, fake, fake, nullptr, M, N, K, 1.0f, cus,
                             [](const KernelEntry *e, int *occ) {
                                 *occ = static_occupancy(e);
                                 return GEMM_OK;

@@ -110,12 +110,36 @@ struct Prob {
     int vec_cd;                  // C/D allow 4-element vector access
 };
 
+// Epilogue activations (the values of gemm_epilogue).
+enum { ACT_LINEAR = 0, ACT_RELU = 1, ACT_SIGMOID = 2, ACT_TANH = 3 };
+
 struct EpiArgs {
     float alpha, beta;
     const float *scale_a, *scale_b;   // device pointers or null (1.0)
-    int relu;
+    const void *bias;                 // N elements of the output type, or null
+    int act;                          // ACT_*
     int lc_row;                       // C/D RowMajor
 };
+
+// act(v): identity, max(v, +0) (NaN -> +0), 1/(1+e^-v), tanh(v). The two
+// transcendental ones use the hardware base-2 exponential and reciprocal
+// (about one fp32 ulp each): e^x = 2^(x log2 e); tanh|v| = (1 - t)/(1 + t)
+// with t = e^(-2|v|) <= 1, so nothing overflows; the absolute error near 0
+// stays below 1e-7.
+__device__ __forceinline__ float exp_e(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+__device__ __forceinline__ float apply_act(float v, int act) {
+    switch (act) {
+    case ACT_RELU: return v > 0.0f ? v : 0.0f;
+    case ACT_SIGMOID: return __builtin_amdgcn_rcpf(1.0f + exp_e(-v));
+    case ACT_TANH: {
+        const float t = exp_e(-2.0f * __builtin_fabsf(v));
+        return __builtin_copysignf((1.0f - t) * __builtin_amdgcn_rcpf(1.0f + t), v);
+    }
+    default: return v;
+    }
+}
 
 // Persistent schedule: schedule indices [0, sk_tiles) are split stream-K
 // style over `grid` workgroups; [sk_tiles, total) are whole tiles dealt out
@@ -674,13 +698,9 @@ struct Tile {
 
     // ---- epilogue ------------------------------------------------------------
     //
-    // v = alpha' * acc + beta * C (C not read when beta == 0), alpha' = alpha
-    // times the per-tensor scales; ReLU maps v to max(v, +0) (NaN -> +0); one
+    // v = alpha' * acc + beta * C (C not read when beta == 0) + bias[n],
+    // alpha' = alpha times the per-tensor scales; then the activation; one
     // round-to-nearest-even conversion into the output type.
-
-    static __device__ __forceinline__ float act(float v, int relu) {
-        return relu ? (v > 0.0f ? v : 0.0f) : v;
-    }
 
     static __device__ __forceinline__ float eff_alpha(const EpiArgs &e) {
         float a = e.alpha;
@@ -691,11 +711,38 @@ struct Tile {
 
     // Interior tile, RowMajor C/D with 4-element vector access: every lane
     // owns four consecutive n of one m for each (i, j, q).
+    // Four consecutive elements of an output-typed vector as floats.
+    static __device__ __forceinline__ void load4(const Out *src, int64_t idx, float (&v)[4]) {
+        if constexpr (sizeof(Out) == 4) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(src + idx);
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4) v[t4] = t[t4];
+        } else {
+            const u32x2 t = *reinterpret_cast<const u32x2 *>(src + idx);
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4)
+                v[t4] = (float)__builtin_bit_cast(Out, (uint16_t)(t[t4 >> 1] >> (16 * (t4 & 1))));
+        }
+    }
+
     template <bool BETA>
     static __device__ __forceinline__ void epi_fast(const Prob &p, const EpiArgs &e, float alpha,
                                                     int64_t m_base, int64_t n_base, const Acc &acc) {
         Out *D = reinterpret_cast<Out *>(p.D);
         const Out *C = reinterpret_cast<const Out *>(p.C);
+        const Out *bias = reinterpret_cast<const Out *>(e.bias);
+        const int act = e.act;
+        // the bias depends on n only: one vector per (i, q), shared by every row
+        float bv[FN][4][4];
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (bias) load4(bias, n_base + i * 32 + q * 8, bv[i][q]);
+                else
+#pragma unroll
+                    for (int t4 = 0; t4 < 4; ++t4) bv[i][q][t4] = 0.0f;
+            }
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
             const int64_t row = (m_base + j * 32) * p.N;
@@ -707,24 +754,16 @@ struct Tile {
                     float v[4];
                     if constexpr (BETA) {
                         float c[4];
-                        if constexpr (sizeof(Out) == 4) {
-                            const f32x4 t = *reinterpret_cast<const f32x4 *>(C + idx);
-#pragma unroll
-                            for (int t4 = 0; t4 < 4; ++t4) c[t4] = t[t4];
-                        } else {
-                            const u32x2 t = *reinterpret_cast<const u32x2 *>(C + idx);
-#pragma unroll
-                            for (int t4 = 0; t4 < 4; ++t4)
-                                c[t4] = (float)__builtin_bit_cast(
-                                    Out, (uint16_t)(t[t4 >> 1] >> (16 * (t4 & 1))));
-                        }
+                        load4(C, idx, c);
 #pragma unroll
                         for (int t4 = 0; t4 < 4; ++t4)
-                            v[t4] = act(__builtin_fmaf(alpha, acc.v[i][j][q * 4 + t4], e.beta * c[t4]),
-                                        e.relu);
+                            v[t4] = apply_act(__builtin_fmaf(alpha, acc.v[i][j][q * 4 + t4],
+                                                             e.beta * c[t4]) + bv[i][q][t4],
+                                              act);
                     } else {
 #pragma unroll
-                        for (int t4 = 0; t4 < 4; ++t4) v[t4] = act(alpha * acc.v[i][j][q * 4 + t4], e.relu);
+                        for (int t4 = 0; t4 < 4; ++t4)
+                            v[t4] = apply_act(alpha * acc.v[i][j][q * 4 + t4] + bv[i][q][t4], act);
                     }
                     if constexpr (sizeof(Out) == 4) {
                         *reinterpret_cast<f32x4 *>(D + idx) = f32x4{v[0], v[1], v[2], v[3]};
@@ -757,7 +796,8 @@ struct Tile {
                         const float a = vals[((i * FM + j) * 4 + q) * 4 + t4];
                         float v = alpha * a;
                         if (e.beta != 0.0f) v = __builtin_fmaf(alpha, a, e.beta * (float)C[idx]);
-                        D[idx] = (Out)act(v, e.relu);
+                        if (e.bias) v += (float)reinterpret_cast<const Out *>(e.bias)[n];
+                        D[idx] = (Out)apply_act(v, e.act);
                     }
         }
     }

@@ -97,8 +97,8 @@ __global__ void __launch_bounds__(256) gemm_generic(GenericArgs a) {
             const int64_t idx = a.e.lc_row ? m * p.N + n : m + n * p.M;
             float v = alpha * acc[i][j];
             if (a.e.beta != 0.0f) v = __builtin_fmaf(alpha, acc[i][j], a.e.beta * (float)C[idx]);
-            if (a.e.relu) v = v > 0.0f ? v : 0.0f;
-            D[idx] = (Out)v;
+            if (a.e.bias) v += (float)reinterpret_cast<const Out *>(a.e.bias)[n];
+            D[idx] = (Out)apply_act(v, a.e.act);
         }
 }
 

@@ -62,9 +62,20 @@ typedef enum {
 
 typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout;
 
-/* Epilogue: LINEAR gives v = alpha*acc + beta*C; RELU gives max(v, +0)
- * (NaN maps to +0), both rounded once, to nearest even, into element_D. */
-typedef enum { GEMM_EPI_LINEAR = 0, GEMM_EPI_RELU = 1 } gemm_epilogue;
+/* Epilogue activation, applied to v = alpha*acc + beta*C (+ bias[n] with
+ * gemm_plan_run_ex) and then rounded once, to nearest even, into element_D:
+ * LINEAR keeps v; RELU gives max(v, +0) (NaN maps to +0); SIGMOID gives
+ * 1/(1+exp(-v)); TANH gives tanh(v) ("CUTLASS Python 接口全解析" section 2.3;
+ * "Generating State-of-the-Art GEMMs with TorchInductor's CuteDSL backend",
+ * section 7: ReLU, Sigmoid and Tanh in the fused epilogue). SIGMOID and TANH
+ * are evaluated in fp32 with the hardware exponential and reciprocal (a few
+ * fp32 ulp; absolute error below 1e-7 near 0). */
+typedef enum {
+    GEMM_EPI_LINEAR = 0,
+    GEMM_EPI_RELU = 1,
+    GEMM_EPI_SIGMOID = 2,
+    GEMM_EPI_TANH = 3
+} gemm_epilogue;
 
 typedef enum {
     GEMM_OK = 0,
@@ -141,6 +152,19 @@ gemm_status gemm_plan_run_scaled(gemm_plan_t plan, const void *A,
                                  int64_t M, int64_t N, int64_t K, float alpha,
                                  float beta, const float *scale_a,
                                  const float *scale_b, void *stream);
+
+/* Fused bias ("CUTLASS Python接口", the BiasAdd-ReLU GEMM example:
+ * Output = Activation(Input * Weight + Bias)):
+ *   D = act(alpha * s_A * s_B * (A B) + beta * C + bias[n])
+ * bias points to N elements of element_C (device memory, one value per
+ * column of D, added to every row); NULL means no bias. scale_a / scale_b are
+ * as in gemm_plan_run_scaled (NULL = 1.0). This is the general form of the
+ * two calls above. */
+gemm_status gemm_plan_run_ex(gemm_plan_t plan, const void *A, const void *B,
+                             const void *C, void *D, const void *bias,
+                             int64_t M, int64_t N, int64_t K, float alpha,
+                             float beta, const float *scale_a,
+                             const float *scale_b, void *stream);
 
 /* One problem of a grouped call; pointers follow the conventions above. */
 typedef struct {

@@ -61,11 +61,15 @@ def scales(p):
 
 
 def run(p, relu=False, schedule=g.Schedule.AUTO, tile=g.Tile.AUTO, sk_grid=0, plan=None,
-        operands=None, in_place=False):
-    """Run p on the GPU and return D as fp64 [M, N] (plus the plan's describe())."""
+        operands=None, in_place=False, act=None, bias_offset=0):
+    """Run p on the GPU and return D as fp64 [M, N] (plus the plan's describe()).
+
+    act names the activation (None: ReLU if relu else linear); p.bias, if set,
+    goes to the device bias_offset elements into a larger buffer (an offset
+    of 1 misaligns it)."""
     own = plan is None
     if own:
-        plan = g.Plan(p.dtype_ab, p.dtype_cd, p.la, p.lb, p.lc, relu)
+        plan = g.Plan(p.dtype_ab, p.dtype_cd, p.la, p.lb, p.lc, relu, activation=act)
     plan.set_config(schedule, tile, sk_grid)
     A, B, C = operands if operands is not None else device_operands(p)
     if in_place:
@@ -74,9 +78,14 @@ def run(p, relu=False, schedule=g.Schedule.AUTO, tile=g.Tile.AUTO, sk_grid=0, pl
     else:
         buf, D = make_out(p)
     sa, sb = scales(p)
-    print(f"[gpu] {p.dtype_ab} {p.la}{p.lb}{p.lc} M={p.M} N={p.N} K={p.K} relu={relu} "
-          f"{plan.describe(p.M, p.N, p.K)}", flush=True)
-    plan.run(A, B, C, D, p.M, p.N, p.K, p.alpha, p.beta, sa, sb)
+    bias = None
+    if getattr(p, "bias", None) is not None:
+        hold = torch.zeros(p.N + bias_offset, dtype=p.bias.dtype, device=DEV)
+        hold[bias_offset:] = p.bias.to(DEV)
+        bias = hold[bias_offset:]
+    print(f"[gpu] {p.dtype_ab} {p.la}{p.lb}{p.lc} M={p.M} N={p.N} K={p.K} relu={relu} act={act} "
+          f"bias={bias is not None}+{bias_offset} {plan.describe(p.M, p.N, p.K)}", flush=True)
+    plan.run(A, B, C, D, p.M, p.N, p.K, p.alpha, p.beta, sa, sb, bias=bias)
     torch.cuda.synchronize()
     if buf is not None:
         check_guards(buf, p)

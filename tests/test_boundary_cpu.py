@@ -178,3 +178,29 @@ def test_describe_forced_configs():
     p.set_config(g.Schedule.DATA_PARALLEL, g.Tile.GENERIC, 0)
     assert p.describe(64, 64, 64)["kernel"] == "generic"
     p.close()
+
+
+def test_activation_epilogues_and_run_ex_validation():
+    D, L, E = g.Dtype, g.Layout, g.Epilogue
+    for epi in (E.LINEAR, E.RELU, E.SIGMOID, E.TANH):
+        h = g.gemm_plan_create(D.BF16, D.BF16, D.BF16, D.BF16, D.F32, L.ROW_MAJOR,
+                               L.COL_MAJOR, L.ROW_MAJOR, epi)
+        g.gemm_plan_destroy(h)
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_plan_create(D.BF16, D.BF16, D.BF16, D.BF16, D.F32, 0, 0, 0, 4)
+    assert e.value.status == g.Status.INVALID_ARG and "SIGMOID" in str(e.value)
+    run_ex = g.lib.gemm_plan_run_ex
+    assert run_ex(None, None, None, None, None, None, 1, 1, 1, 1.0, 0.0, None, None, None) == \
+        g.Status.NOT_INITIALIZED
+    h = g.gemm_plan_create_simple(D.F16, L.ROW_MAJOR, E.TANH)
+    try:
+        # negative sizes and a missing D fail before any device call
+        assert run_ex(h, 16, 16, None, 16, 16, -1, 4, 4, 1.0, 0.0, None, None, None) == \
+            g.Status.INVALID_ARG
+        assert run_ex(h, 16, 16, None, None, 16, 4, 4, 4, 1.0, 0.0, None, None, None) == \
+            g.Status.INVALID_ARG
+        # an empty output is a no-op, bias or not
+        assert run_ex(h, None, None, None, None, None, 0, 4, 4, 1.0, 0.0, None, None, None) == \
+            g.Status.OK
+    finally:
+        g.gemm_plan_destroy(h)

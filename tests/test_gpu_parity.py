@@ -25,13 +25,13 @@ LAYOUTS = list(itertools.product(("row", "col"), repeat=3))
 S, T = g.Schedule, g.Tile
 
 
-def close(got, p, relu=False, what=""):
-    r = oracle.gemm(p, relu=relu)
+def close(got, p, relu=False, what="", act=None):
+    r = oracle.gemm(p, relu=relu, act=act)
     return acceptance.check_close(got, r.ref, r.S, p.dtype_ab, p.dtype_cd, what)
 
 
-def exact(got, p, relu=False, what=""):
-    r = oracle.gemm(p, relu=relu)
+def exact(got, p, relu=False, what="", act=None):
+    r = oracle.gemm(p, relu=relu, act=act)
     acceptance.check_exact(got, r.d_exact, what)
 
 
@@ -361,3 +361,55 @@ def test_fp8_scales_read_on_device():
                             lo=-1, hi=1, seed=20)
     p.scale_a, p.scale_b = 0.5, 0.25
     exact(run(p), p)
+
+
+# ------------------------------------------------------------ bias + activations
+
+@pytest.mark.parametrize("dab,dcd", FAMS)
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("act", ["linear", "relu"])
+def test_bias_integer_exact(dab, dcd, tile, act):
+    # RowMajor C/D (vector epilogue on interior tiles), ragged edges
+    p = _int_problem(dab, dcd, "row", "col", "row", M=272, N=304, K=192, seed=31)
+    p.bias = syn.cast(np.random.default_rng(32).integers(-2, 3, p.N).astype(np.float32), dcd)
+    got = run(p, tile=tile, schedule=S.DATA_PARALLEL, act=act)
+    exact(got, p, act="identity" if act == "linear" else act, what=f"{dab} {tile.name} {act}")
+
+
+@pytest.mark.parametrize("dab,dcd", FAMS)
+@pytest.mark.parametrize("sched", [S.STREAM_K, S.SPLIT_K])
+def test_bias_integer_exact_split_schedules_col_c(dab, dcd, sched):
+    # the epilogue after a partial-tile fixup, ColumnMajor C/D (element path)
+    p = _int_problem(dab, dcd, "row", "col", "col", M=200, N=264, K=1024, seed=33)
+    p.bias = syn.cast(np.random.default_rng(34).integers(-2, 3, p.N).astype(np.float32), dcd)
+    got = run(p, tile=T.T128x128, schedule=sched, act="relu", relu=True)
+    exact(got, p, relu=True, what=f"{dab} {sched.name} col C")
+
+
+@pytest.mark.parametrize("dab,dcd", FAMS)
+@pytest.mark.parametrize("act", ["sigmoid", "tanh"])
+@pytest.mark.parametrize("lb", ["col", "row"])
+def test_sigmoid_tanh_with_bias(dab, dcd, act, lb):
+    p = syn.make_problem(336, 400, 520, dtype_ab=dab, dtype_cd=dcd, lb=lb, dist_c="normal",
+                         alpha=0.05, beta=0.5, dist_bias="normal", seed=35)
+    for tile in (T.AUTO, T.T32x256, T.GENERIC):
+        close(run(p, act=act, tile=tile), p, act=act, what=f"{dab} {act} lb={lb} {tile.name}")
+
+
+def test_misaligned_bias_uses_element_epilogue():
+    p = syn.make_problem(256, 512, 256, dtype_ab="bf16", dtype_cd="bf16", lb="col",
+                         dist_bias="normal", seed=36)
+    a = run(p, act="relu", relu=True, tile=T.T256x256, schedule=S.DATA_PARALLEL)
+    b = run(p, act="relu", relu=True, tile=T.T256x256, schedule=S.DATA_PARALLEL, bias_offset=1)
+    assert np.array_equal(a, b)     # same arithmetic, element-wise stores
+    close(b, p, relu=True, what="misaligned bias")
+
+
+def test_bias_without_activation_equals_shifted_linear():
+    # D(bias) - D(no bias) == bias[n] exactly on integer data, every row
+    p = _int_problem("f16", "f16", "row", "col", "row", M=128, N=256, K=64, seed=37)
+    base = run(p)
+    p.bias = syn.cast(np.random.default_rng(38).integers(-3, 4, p.N).astype(np.float32), "f16")
+    shifted = run(p)
+    want = np.tile(p.bias.to(torch.float64).numpy(), (p.M, 1))
+    assert np.array_equal(shifted - base, want)
