@@ -107,6 +107,9 @@ def _load():
     L.gemm_plan_run_scaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp, vp, vp]
     L.gemm_plan_run_ex.restype = st
     L.gemm_plan_run_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp, vp, vp]
+    L.gemm_plan_run_batched.restype = st
+    L.gemm_plan_run_batched.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                        i64, i64, f32, f32, vp, vp, vp]
     L.grouped_gemm_run.restype = st
     L.grouped_gemm_run.argtypes = [vp, ctypes.POINTER(gemm_problem), i32, f32, f32, vp]
     L.gemm_plan_describe.restype = st
@@ -128,7 +131,7 @@ lib = _load()
 
 EXPORTED = ("gemm_plan_create", "gemm_plan_create_simple", "gemm_plan_destroy",
             "gemm_plan_set_config", "gemm_plan_run", "gemm_plan_run_scaled",
-            "gemm_plan_run_ex", "grouped_gemm_run", "gemm_plan_describe", "gemm_last_error",
+            "gemm_plan_run_ex", "gemm_plan_run_batched", "grouped_gemm_run", "gemm_plan_describe", "gemm_last_error",
             "gemm_status_string", "gemm_supported_count", "gemm_supported_get",
             "gemm_version")
 
@@ -196,6 +199,15 @@ def gemm_plan_run_ex(plan: int, A, B, C, D, bias, M: int, N: int, K: int, alpha:
                      beta: float, scale_a=None, scale_b=None, stream=None) -> None:
     _check(lib.gemm_plan_run_ex(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(bias), M, N, K,
                                 alpha, beta, _ptr(scale_a), _ptr(scale_b), _stream(stream)))
+
+
+def gemm_plan_run_batched(plan: int, A, B, C, D, bias, M: int, N: int, K: int, batch: int,
+                          stride_a: int, stride_b: int, stride_c: int, stride_d: int,
+                          alpha: float, beta: float, scale_a=None, scale_b=None,
+                          stream=None) -> None:
+    _check(lib.gemm_plan_run_batched(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(bias), M, N,
+                                     K, batch, stride_a, stride_b, stride_c, stride_d, alpha,
+                                     beta, _ptr(scale_a), _ptr(scale_b), _stream(stream)))
 
 
 def grouped_gemm_run(plan: int, problems: Sequence[tuple], alpha: float = 1.0,
@@ -325,6 +337,23 @@ class Plan:
         else:
             gemm_plan_run_scaled(self.handle, A, B, C, D, M, N, K, alpha, beta, scale_a,
                                  scale_b, stream)
+
+    def run_batched(self, A, B, C, D, M, N, K, batch, strides, alpha=1.0, beta=0.0,
+                    scale_a=None, scale_b=None, stream=None, bias=None):
+        """strides: (stride_a, stride_b, stride_c, stride_d) in elements."""
+        sa, sb, sc, sd = (int(x) for x in strides)
+        if min(M, N, K, batch, sa, sb, sc, sd) >= 0 and M and N and batch:
+            last = batch - 1
+            _need(D, last * sd + M * N, "D", self.dcd)
+            if K:
+                _need(A, last * sa + M * K, "A", self.dab)
+                _need(B, last * sb + K * N, "B", self.dab)
+            if beta != 0.0:
+                _need(C, last * sc + M * N, "C", self.dcd)
+            if bias is not None:
+                _need(bias, N, "bias", self.dcd)
+        gemm_plan_run_batched(self.handle, A, B, C, D, bias, M, N, K, batch, sa, sb, sc, sd,
+                              alpha, beta, scale_a, scale_b, stream)
 
     def run_grouped(self, problems: Iterable[tuple], alpha=1.0, beta=0.0, stream=None):
         probs = list(problems)

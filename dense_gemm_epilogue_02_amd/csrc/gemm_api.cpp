@@ -248,7 +248,7 @@ int min_iters(int fam) { return fam == FAM_F32 ? 1 : 8; }
 template <class OccFn>
 gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const void *C, const void *D,
                    const void *bias, int64_t M, int64_t N, int64_t K, float beta, int cus, OccFn occ_of,
-                   Decision &d) {
+                   Decision &d, int64_t batch = 1) {
     const int fam = pl->fam;
     const int esz = elem_bytes(fam), osz = out_bytes(fam);
     const bool a_kc = pl->la == GEMM_ROW_MAJOR, b_kc = pl->lb == GEMM_COL_MAJOR;
@@ -282,9 +282,9 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
     }
     const KernelEntry *e = d.e;
     const int64_t tm = cdiv(M, e->bm), tn = cdiv(N, e->bn), ipt = cdiv(K, e->bk);
-    if (tm * tn > 0x7FFFFFFFLL || ipt > 0x7FFFFFFFLL || tm * tn * ipt > (1LL << 52))
-        return fail(GEMM_UNSUPPORTED, "problem %lldx%lldx%lld has too many tiles", (long long)M,
-                    (long long)N, (long long)K);
+    if (tm * tn * batch > 0x7FFFFFFFLL || ipt > 0x7FFFFFFFLL || tm * tn * batch * ipt > (1LL << 52))
+        return fail(GEMM_UNSUPPORTED, "problem %lldx%lldx%lld (batch %lld) has too many tiles",
+                    (long long)M, (long long)N, (long long)K, (long long)batch);
     d.tiles_m = (int)tm;
     d.tiles_n = (int)tn;
     // raster groups of 8 tile rows for 256x256 tiles: a workgroup wave then
@@ -292,7 +292,7 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
     // groups of 4 on the transformer-layer shapes (fewer column-panel re-reads)
     d.group_m = e->tile == TILE_256x256 ? 8 : 4;
     d.ipt = (int)ipt;
-    d.total = (int)(tm * tn);
+    d.total = (int)(tm * tn * batch);
     int occ = 1;
     gemm_status st = occ_of(e, &occ);
     if (st != GEMM_OK) return st;
@@ -437,8 +437,16 @@ Prob make_prob(const void *A, const void *B, const void *C, void *D, int64_t M, 
     p.tiles_n = d.tiles_n;
     p.ipt = d.ipt;
     p.vec_cd = d.vec_cd;
+    p.batch = 1;
+    p.stride_a = p.stride_b = p.stride_c = p.stride_d = 0;
     return p;
 }
+
+// Batch shape of one run (a single GEMM is batch 1 with zero strides).
+struct Batch {
+    int64_t count = 1;
+    int64_t sa = 0, sb = 0, sc = 0, sd = 0;   // element strides
+};
 
 EpiArgs make_epi(const gemm_plan_s *pl, float alpha, float beta, const float *sa, const float *sb,
                  const void *bias) {
@@ -466,12 +474,28 @@ gemm_status run_generic(const gemm_plan_s *pl, const Prob &p, const EpiArgs &ep,
 
 gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C, void *D, int64_t M,
                     int64_t N, int64_t K, float alpha, float beta, const float *sa, const float *sb,
-                    const void *bias, void *stream) {
+                    const void *bias, void *stream, const Batch &bt = Batch()) {
     if (!plan_ok(pl)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_run: invalid plan handle");
     gemm_status st = validate_problem(pl, A, B, C, D, M, N, K, beta, "gemm_plan_run");
     if (st != GEMM_OK) return st;
-    if (M == 0 || N == 0) return ok();
+    if (M == 0 || N == 0 || bt.count == 0) return ok();
     if (beta == 0.0f) C = nullptr;
+    const int esz = elem_bytes(pl->fam), osz = out_bytes(pl->fam);
+    // batch entries whose operands cannot keep the tile kernel's 16-byte
+    // alignment (or whose tile count overflows) run one by one
+    const bool batched = bt.count > 1;
+    if (batched && ((bt.sa * esz) % 16 != 0 || (bt.sb * esz) % 16 != 0 || bt.sc % 4 != 0 ||
+                    bt.sd % 4 != 0 || cdiv(M, 32) * cdiv(N, 32) * bt.count > 0x7FFFFFFFLL)) {
+        for (int64_t b = 0; b < bt.count; ++b) {
+            st = run_one(pl, static_cast<const char *>(A) + b * bt.sa * esz,
+                         static_cast<const char *>(B) + b * bt.sb * esz,
+                         C ? static_cast<const char *>(C) + b * bt.sc * osz : nullptr,
+                         static_cast<char *>(D) + b * bt.sd * osz, M, N, K, alpha, beta, sa, sb, bias,
+                         stream);
+            if (st != GEMM_OK) return st;
+        }
+        return ok();
+    }
     int dev = 0;
     if ((st = check_device(pl, &dev)) != GEMM_OK) return st;
     int cus = 0;
@@ -482,12 +506,27 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
                 [&](const KernelEntry *e, int *occ) {
                     return kernel_occupancy(dev, e->fn_persistent, e->nt, occ);
                 },
-                d);
+                d, bt.count);
     if (st != GEMM_OK) return st;
-    const Prob p = make_prob(A, B, C, D, M, N, K, d);
+    Prob p = make_prob(A, B, C, D, M, N, K, d);
+    p.batch = (int)bt.count;
+    p.stride_a = bt.sa;
+    p.stride_b = bt.sb;
+    p.stride_c = bt.sc;
+    p.stride_d = bt.sd;
     const EpiArgs ep = make_epi(pl, alpha, beta, sa, sb, bias);
     if (!d.e) {
-        st = run_generic(pl, p, ep, hs);
+        if (batched) {   // the scalar kernel takes one problem per launch
+            for (int64_t b = 0; b < bt.count && st == GEMM_OK; ++b) {
+                Prob q = make_prob(static_cast<const char *>(A) + b * bt.sa * esz,
+                                   static_cast<const char *>(B) + b * bt.sb * esz,
+                                   C ? static_cast<const char *>(C) + b * bt.sc * osz : nullptr,
+                                   static_cast<char *>(D) + b * bt.sd * osz, M, N, K, d);
+                st = run_generic(pl, q, ep, hs);
+            }
+        } else {
+            st = run_generic(pl, p, ep, hs);
+        }
         if (st == GEMM_OK) note_stream(pl, hs);
         return st == GEMM_OK ? ok() : st;
     }
@@ -610,6 +649,34 @@ gemm_status gemm_plan_run_scaled(gemm_plan_t p, const void *A, const void *B, co
                                  int64_t M, int64_t N, int64_t K, float alpha, float beta,
                                  const float *scale_a, const float *scale_b, void *stream) {
     return run_one(p, A, B, C, D, M, N, K, alpha, beta, scale_a, scale_b, nullptr, stream);
+}
+
+gemm_status gemm_plan_run_batched(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,
+                                  const void *bias, int64_t M, int64_t N, int64_t K,
+                                  int64_t batch_count, int64_t stride_a, int64_t stride_b,
+                                  int64_t stride_c, int64_t stride_d, float alpha, float beta,
+                                  const float *scale_a, const float *scale_b, void *stream) {
+    if (!plan_ok(p)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_run_batched: invalid plan handle");
+    if (batch_count < 0 || stride_a < 0 || stride_b < 0 || stride_c < 0 || stride_d < 0)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_run_batched: negative batch count or stride");
+    if (batch_count > 1 && M > 0 && N > 0 && stride_d < M * N)
+        return fail(GEMM_INVALID_ARG,
+                    "gemm_plan_run_batched: stride_d = %lld < M*N = %lld makes the outputs overlap",
+                    (long long)stride_d, (long long)(M * N));
+    if (batch_count > 0x7FFFFFFFLL)
+        return fail(GEMM_UNSUPPORTED, "gemm_plan_run_batched: batch count beyond 2^31");
+    if (batch_count == 0) {   // nothing to read or write: NULL buffers are fine
+        if (M < 0 || N < 0 || K < 0)
+            return fail(GEMM_INVALID_ARG, "gemm_plan_run_batched: negative size");
+        return ok();
+    }
+    Batch bt;
+    bt.count = batch_count;
+    bt.sa = stride_a;
+    bt.sb = stride_b;
+    bt.sc = stride_c;
+    bt.sd = stride_d;
+    return run_one(p, A, B, C, D, M, N, K, alpha, beta, scale_a, scale_b, bias, stream, bt);
 }
 
 gemm_status gemm_plan_run_ex(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,

@@ -108,6 +108,11 @@ struct Prob {
     int64_t M, N, K;
     int tiles_m, tiles_n, ipt;   // tile grid and k-tiles per output tile
     int vec_cd;                  // C/D allow 4-element vector access
+    // Batched GEMM: `batch` problems of the same shape whose operands lie
+    // stride_* elements apart (a stride of 0 shares an operand); the tile
+    // space is batch-major. batch <= 1 is a single GEMM.
+    int batch;
+    int64_t stride_a, stride_b, stride_c, stride_d;
 };
 
 // Epilogue activations (the values of gemm_epilogue).
@@ -494,6 +499,11 @@ struct Tile {
         r_left = (int)imin64(p.N - n0, BN);
         k_left = (int)imin64(p.K - k0, BK);
     }
+
+    // The problem that schedule tile t belongs to (its batch entry's
+    // operands) and the tile's coordinates within it.
+    static __device__ __forceinline__ Prob tile_problem(const Prob &p, int t, int group_m, int &tm,
+                                                         int &tn);
 
     // Per-work-unit copy state: direct stagers for K-contiguous operands,
     // register stagers (with in-register transpose) for the others.
@@ -966,6 +976,26 @@ __device__ __forceinline__ bool arrive_last(int *counter, int expected, char *ld
     return last;
 }
 
+template <int FAM_, bool A_KC, bool B_KC, int BM_, int BN_, int WM_, int WN_, int KB, int STAGES,
+          int PIPE, int COPY_WAVES>
+__device__ __forceinline__ Prob
+Tile<FAM_, A_KC, B_KC, BM_, BN_, WM_, WN_, KB, STAGES, PIPE, COPY_WAVES>::tile_problem(
+    const Prob &p, int t, int group_m, int &tm, int &tn) {
+    if (p.batch <= 1) {
+        tile_coords(t, p.tiles_m, p.tiles_n, group_m, tm, tn);
+        return p;
+    }
+    const int per = p.tiles_m * p.tiles_n;
+    const int b = t / per;
+    tile_coords(t - b * per, p.tiles_m, p.tiles_n, group_m, tm, tn);
+    Prob q = p;
+    q.A = p.A + (size_t)(b * p.stride_a) * ESZ;
+    q.B = p.B + (size_t)(b * p.stride_b) * ESZ;
+    if (p.C) q.C = p.C + (size_t)(b * p.stride_c) * sizeof(Out);
+    q.D = p.D + (size_t)(b * p.stride_d) * sizeof(Out);
+    return q;
+}
+
 template <class TL>
 __global__ void __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::WAVES_PER_EU)))
 gemm_persistent(KArgs a) {
@@ -980,10 +1010,10 @@ gemm_persistent(KArgs a) {
         const int S = s.split;
         if (v >= s.sk_tiles * S) return;
         const int t = v / S, c = v - (v / S) * S;
-        tile_coords(t, p.tiles_m, p.tiles_n, s.group_m, tm, tn);
-        TL::mainloop(p, tm, tn, c, (p.ipt - c + S - 1) / S, S, acc, lds);
+        const Prob pt = TL::tile_problem(p, t, s.group_m, tm, tn);
+        TL::mainloop(pt, tm, tn, c, (p.ipt - c + S - 1) / S, S, acc, lds);
         if (S == 1) {
-            TL::epilogue(p, a.e, tm, tn, acc);
+            TL::epilogue(pt, a.e, tm, tn, acc);
             return;
         }
         const size_t slot_elems = (size_t)TL::BM * TL::BN;
@@ -993,7 +1023,7 @@ gemm_persistent(KArgs a) {
         if (arrive_last(&s.counters[t], S - 1, lds)) {
             // sum the units in order c = 0 .. S-1 (deterministic)
             TL::add_partials([&](int u) { return s.partials + ((size_t)t * S + u) * slot_elems; }, S, acc);
-            TL::epilogue(p, a.e, tm, tn, acc);
+            TL::epilogue(pt, a.e, tm, tn, acc);
             if (threadIdx.x == 0)
                 __hip_atomic_store(&s.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -1011,10 +1041,10 @@ gemm_persistent(KArgs a) {
             const int64_t tile_it0 = (int64_t)t * p.ipt;
             const int k0 = (int)(it - tile_it0);
             const int k1 = (int)(imin64(end, tile_it0 + p.ipt) - tile_it0);
-            tile_coords(t, p.tiles_m, p.tiles_n, s.group_m, tm, tn);
-            TL::mainloop(p, tm, tn, k0, k1 - k0, 1, acc, lds);
+            const Prob pt = TL::tile_problem(p, t, s.group_m, tm, tn);
+            TL::mainloop(pt, tm, tn, k0, k1 - k0, 1, acc, lds);
             if (k0 == 0 && k1 == p.ipt) {
-                TL::epilogue(p, a.e, tm, tn, acc);
+                TL::epilogue(pt, a.e, tm, tn, acc);
             } else {
                 // every contributor publishes its partial, the last to arrive
                 // sums all partials in contributor order (deterministic)
@@ -1034,7 +1064,7 @@ gemm_persistent(KArgs a) {
                             return s.partials + (size_t)(2 * u + (t == ft ? 0 : 1)) * slot_elems;
                         },
                         v1 - v0 + 1, acc);
-                    TL::epilogue(p, a.e, tm, tn, acc);
+                    TL::epilogue(pt, a.e, tm, tn, acc);
                     if (threadIdx.x == 0)
                         __hip_atomic_store(&s.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
@@ -1044,9 +1074,9 @@ gemm_persistent(KArgs a) {
         }
     }
     for (int t = s.sk_tiles + v; t < s.total_tiles; t += s.grid) {
-        tile_coords(t, p.tiles_m, p.tiles_n, s.group_m, tm, tn);
-        TL::mainloop(p, tm, tn, 0, p.ipt, 1, acc, lds);
-        TL::epilogue(p, a.e, tm, tn, acc);
+        const Prob pt = TL::tile_problem(p, t, s.group_m, tm, tn);
+        TL::mainloop(pt, tm, tn, 0, p.ipt, 1, acc, lds);
+        TL::epilogue(pt, a.e, tm, tn, acc);
     }
 }
 

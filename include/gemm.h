@@ -166,6 +166,29 @@ gemm_status gemm_plan_run_ex(gemm_plan_t plan, const void *A, const void *B,
                              float beta, const float *scale_a,
                              const float *scale_b, void *stream);
 
+/* Batched GEMM ("CUTLASS Python接口", batched GEMM: batch_count and
+ * batch_stride_A/B/C): batch_count problems of one shape M x N x K; problem b
+ * reads A + b*stride_a, B + b*stride_b, C + b*stride_c and writes
+ * D + b*stride_d (strides in elements of the operand's type, each operand in
+ * the plan's layout). A stride of 0 shares that operand across the batch
+ * (C too); stride_d must be at least M*N when batch_count > 1, so outputs do
+ * not overlap. bias (N elements of the C/D type, or NULL), scale_a and
+ * scale_b (device fp32 scalars, or NULL for 1.0) are shared by every problem,
+ * with the meaning gemm_plan_run_ex gives them. All problems run in one
+ * persistent launch over a batch-major tile space; batch entries whose
+ * strides break the tile kernels' 16-byte alignment run one launch each.
+ * batch_count == 0 is a no-op; a negative count or stride, or overlapping
+ * outputs, give GEMM_INVALID_ARG; batch_count > 2^31 gives GEMM_UNSUPPORTED.
+ * The caller keeps ownership of every buffer. */
+gemm_status gemm_plan_run_batched(gemm_plan_t plan, const void *A, const void *B,
+                                  const void *C, void *D, const void *bias,
+                                  int64_t M, int64_t N, int64_t K,
+                                  int64_t batch_count, int64_t stride_a,
+                                  int64_t stride_b, int64_t stride_c,
+                                  int64_t stride_d, float alpha, float beta,
+                                  const float *scale_a, const float *scale_b,
+                                  void *stream);
+
 /* One problem of a grouped call; pointers follow the conventions above. */
 typedef struct {
     int64_t M, N, K;

@@ -183,3 +183,14 @@ def gemm_entries(p, ii, jj, relu: bool = False, act: Optional[str] = None) -> Re
 def grouped(problems: List, relu: bool = False, act: Optional[str] = None) -> List[Result]:
     """Grouped GEMM = the independent single GEMMs, one after another."""
     return [gemm(p, relu, act=act) for p in problems]
+
+
+def batched(problems: List, relu: bool = False, act: Optional[str] = None) -> List[Result]:
+    """Batched GEMM ("CUTLASS Python接口", batched GEMM: a batch count and a
+    stride per operand) = one independent GEMM per batch index, all of one
+    shape; how the batch is laid out in memory (the strides) is the caller's
+    packing, not arithmetic, so each entry is passed as its own problem."""
+    if problems and any((p.M, p.N, p.K) != (problems[0].M, problems[0].N, problems[0].K)
+                        for p in problems):
+        raise ValueError("batched GEMM problems share one M x N x K")
+    return [gemm(p, relu, act=act) for p in problems]

@@ -204,3 +204,28 @@ def test_activation_epilogues_and_run_ex_validation():
             g.Status.OK
     finally:
         g.gemm_plan_destroy(h)
+
+
+def test_batched_validation_before_any_device_call():
+    run_b = g.lib.gemm_plan_run_batched
+    args = lambda h, cnt, sa, sb, sc, sd, M=8, N=8: (h, 16, 16, None, 16, None, M, N, 8, cnt, sa,
+                                                      sb, sc, sd, 1.0, 0.0, None, None, None)
+    assert run_b(*args(None, 2, 64, 64, 64, 64)) == g.Status.NOT_INITIALIZED
+    h = g.gemm_plan_create_simple(g.Dtype.BF16, g.Layout.ROW_MAJOR, g.Epilogue.LINEAR)
+    try:
+        assert run_b(*args(h, -1, 64, 64, 64, 64)) == g.Status.INVALID_ARG
+        assert run_b(*args(h, 2, -64, 64, 64, 64)) == g.Status.INVALID_ARG
+        assert "negative" in g.gemm_last_error()
+        # outputs of entries 0 and 1 would overlap
+        assert run_b(*args(h, 2, 64, 64, 64, 63)) == g.Status.INVALID_ARG
+        assert "overlap" in g.gemm_last_error()
+        assert run_b(*args(h, 1 << 32, 64, 64, 64, 64)) == g.Status.UNSUPPORTED
+        # empty batch or empty output: no-ops that touch no device
+        assert run_b(*args(h, 0, 64, 64, 64, 64)) == g.Status.OK
+        assert run_b(h, None, None, None, None, None, 8, 8, 8, 0, 0, 0, 0, 0, 1.0, 0.0, None,
+                     None, None) == g.Status.OK
+        assert run_b(*args(h, 3, 64, 64, 64, 0, M=0)) == g.Status.OK
+        with pytest.raises(ValueError):   # the binding checks buffer extents too
+            g.Plan("bf16").run_batched(None, None, None, None, 8, 8, 8, 2, (64, 64, 64, 64))
+    finally:
+        g.gemm_plan_destroy(h)
