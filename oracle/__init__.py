@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-DT = {"f32": 0, "f16": 1, "bf16": 2, "f8e4m3": 3}
+DT = {"f32": 0, "f16": 1, "bf16": 2, "f8e4m3": 3, "e8m0": 4}
 LAYOUT = {"row": 0, "col": 1}
 
 _lib = None
@@ -53,7 +53,7 @@ def lib():
         L.oracle_encode.argtypes = [ctypes.c_int, ctypes.c_double]
         L.oracle_decode_n.argtypes = [ctypes.c_int, vp, ctypes.c_int64, vp]
         L.oracle_encode_n.argtypes = [ctypes.c_int, vp, ctypes.c_int64, vp]
-        common = [ctypes.c_int] * 8 + [ctypes.c_int64] * 3 + [vp] * 4 + \
+        common = [ctypes.c_int] * 8 + [ctypes.c_int64] * 3 + [vp] * 6 + \
                  [ctypes.c_float] * 4
         L.oracle_gemm_rows.restype = ctypes.c_int
         L.oracle_gemm_rows.argtypes = common + [i64p, ctypes.c_int64, vp, vp, vp]
@@ -114,7 +114,9 @@ def _operands(p):
     B = raw(p.B)
     C = raw(p.C) if (p.C is not None and p.beta != 0.0) else None
     bias = raw(p.bias) if getattr(p, "bias", None) is not None else None
-    return A, B, C, bias
+    xa = raw(p.mx_a) if getattr(p, "mx_a", None) is not None else None
+    xb = raw(p.mx_b) if getattr(p, "mx_b", None) is not None else None
+    return A, B, C, bias, xa, xb
 
 
 def _act_code(relu: bool, act: Optional[str]) -> int:
@@ -134,13 +136,14 @@ def _head(p, relu, act=None):
 def gemm(p, relu: bool = False, rows: Optional[Sequence[int]] = None,
          act: Optional[str] = None) -> Result:
     """Full rows of D for the problem ``p`` (a ``synthetic.Problem``; its
-    ``bias``, if any, is added to every row before the activation).
+    ``bias``, if any, is added to every row before the activation; its
+    ``mx_a`` / ``mx_b``, if set, are the E8M0 block scales of an MX problem).
 
     ``rows`` = None computes all M rows; outputs are [n_rows, N] arrays.
     ``act`` names the activation ("identity", "relu", "sigmoid", "tanh");
     ``relu=True`` is shorthand for act="relu".
     """
-    A, B, C, bias = _operands(p)
+    A, B, C, bias, xa, xb = _operands(p)
     al, be, sa, sb = _scalars(p)
     if rows is None:
         rows_arr, n = None, p.M
@@ -153,8 +156,8 @@ def gemm(p, relu: bool = False, rows: Optional[Sequence[int]] = None,
     rp = None if rows_arr is None else rows_arr.ctypes.data_as(
         ctypes.POINTER(ctypes.c_int64))
     rc = lib().oracle_gemm_rows(*_head(p, relu, act), _ptr(A), _ptr(B), _ptr(C),
-                                _ptr(bias), al, be, sa, sb, rp, n, _ptr(ref), _ptr(S),
-                                _ptr(d))
+                                _ptr(bias), _ptr(xa), _ptr(xb), al, be, sa, sb, rp, n,
+                                _ptr(ref), _ptr(S), _ptr(d))
     if rc != 0:
         raise ValueError("oracle_gemm_rows: bad arguments")
     return Result(ref, S, d, p.dtype_cd)
@@ -162,7 +165,7 @@ def gemm(p, relu: bool = False, rows: Optional[Sequence[int]] = None,
 
 def gemm_entries(p, ii, jj, relu: bool = False, act: Optional[str] = None) -> Result:
     """Selected outputs D[ii[t], jj[t]], each computed on its own."""
-    A, B, C, bias = _operands(p)
+    A, B, C, bias, xa, xb = _operands(p)
     al, be, sa, sb = _scalars(p)
     ii = np.ascontiguousarray(np.asarray(ii, dtype=np.int64))
     jj = np.ascontiguousarray(np.asarray(jj, dtype=np.int64))
@@ -172,7 +175,8 @@ def gemm_entries(p, ii, jj, relu: bool = False, act: Optional[str] = None) -> Re
     d = np.empty(n, dtype=np.uint32)
     P = ctypes.POINTER(ctypes.c_int64)
     rc = lib().oracle_gemm_entries(*_head(p, relu, act), _ptr(A), _ptr(B), _ptr(C),
-                                   _ptr(bias), al, be, sa, sb, ii.ctypes.data_as(P),
+                                   _ptr(bias), _ptr(xa), _ptr(xb), al, be, sa, sb,
+                                   ii.ctypes.data_as(P),
                                    jj.ctypes.data_as(P), n, _ptr(ref), _ptr(S),
                                    _ptr(d))
     if rc != 0:

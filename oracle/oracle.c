@@ -23,9 +23,19 @@
  *   - "CUTLASS Python接口" (kwkr.cn), the fused BiasAdd-ReLU GEMM example:
  *     Output = Activation(Input * Weight + Bias), Bias a length-N vector
  *     added to every row.
+ *   - "Generating State-of-the-Art GEMMs with TorchInductor's CuteDSL
+ *     backend", sections 5.1 (feature list: the scaled mm family for MXFP8,
+ *     with its own scale type, block size and layout) and 5.2 (MXFP8
+ *     results). The pages name the format only; its definition is taken from
+ *     the OCP Microscaling (MX) specification v1.0: 32 consecutive elements
+ *     along K share one E8M0 scale (an 8-bit biased power of two, bias 127,
+ *     0xFF = NaN), the elements are e4m3.
  *
  * Definition computed, for each selected output (i, j):
  *   acc     = sum_{k=0}^{K-1} a(i,k) * b(k,j)            fp64, increasing k
+ *             MX: each product also times X_A(i, k/32) * X_B(j, k/32), the
+ *             decoded E8M0 scales of A's row i and B's column j for the
+ *             32-element block holding k
  *   acc     = acc * s_A * s_B                             (scales; 1 unless fp8)
  *   v       = alpha * acc + (beta != 0 ? beta * c(i,j) : 0) + bias(j)
  *             (bias(j) = 0 without a bias vector)
@@ -33,18 +43,21 @@
  *             Tanh: tanh(v)  (all in fp64)
  *   ref     = v                                           (fp64, unrounded)
  *   d_exact = v rounded once, to nearest even, to element_D
- *   S       = |alpha * s_A * s_B| * sum_k |a(i,k) * b(k,j)|  (tolerance scale)
+ *   S       = |alpha * s_A * s_B| * sum_k |a(i,k) * b(k,j)|  (tolerance scale;
+ *             MX: the scaled products)
  * Operands are decoded exactly from their storage bits by this file's own
  * decoders; products of fp32/fp16/bf16/e4m3 values are exact in fp64.
  * Layouts: RowMajor X[r][c] = base[r*cols + c]; ColumnMajor X[r][c] =
  * base[r + c*rows] (packed operands, leading dimension implied).
+ * MX scales: X_A is [M][K/32] and X_B is [N][K/32] bytes, row-major, whatever
+ * the layouts of A and B.
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F8E4M3 = 3 };
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F8E4M3 = 3, DT_E8M0 = 4 };
 enum { LAYOUT_ROW = 0, LAYOUT_COL = 1 };
 enum { ACT_IDENTITY = 0, ACT_RELU = 1, ACT_SIGMOID = 2, ACT_TANH = 3 };
 
@@ -87,12 +100,20 @@ static double dec_e4m3(uint32_t u) {
     return s ? -v : v;
 }
 
+/* OCP MX E8M0 scale: 8 exponent bits (bias 127), no sign, no fraction;
+ * 0xFF is NaN, 0x00 is 2^-127. */
+static double dec_e8m0(uint32_t u) {
+    u &= 255u;
+    return u == 255u ? NAN : ldexp(1.0, (int)u - 127);
+}
+
 double oracle_decode(int dtype, uint32_t bits) {
     switch (dtype) {
     case DT_F32: return dec_f32(bits);
     case DT_F16: return dec_f16(bits);
     case DT_BF16: return dec_bf16(bits);
     case DT_F8E4M3: return dec_e4m3(bits);
+    case DT_E8M0: return dec_e8m0(bits);
     }
     return NAN;
 }
@@ -148,6 +169,20 @@ static double elem(const void *base, int dtype, int layout, int64_t rows,
 
 static int valid_dtype(int d) { return d >= DT_F32 && d <= DT_F8E4M3; }
 
+/* MX block size along K (OCP MX v1.0). */
+#define MX_BLOCK 32
+
+/* X(r, k/32) of an MX scale array [rows][K/32], or 1 without one. */
+static double mx_scale(const uint8_t *x, int64_t K, int64_t r, int64_t k) {
+    return x ? oracle_decode(DT_E8M0, x[r * (K / MX_BLOCK) + k / MX_BLOCK]) : 1.0;
+}
+
+/* MX needs e4m3 elements and whole blocks; both arrays or neither. */
+static int mx_ok(const uint8_t *xa, const uint8_t *xb, int dtA, int dtB, int64_t K) {
+    if (!xa && !xb) return 1;
+    return xa && xb && dtA == DT_F8E4M3 && dtB == DT_F8E4M3 && K % MX_BLOCK == 0;
+}
+
 /* Epilogue of one output: scales, linear combination, bias, activation. */
 static double finish(double acc, double sab, double alpha, double beta,
                      double c, double bias, int act) {
@@ -177,13 +212,13 @@ static double bias_at(const void *bias, int dtype, int64_t j) {
 int oracle_gemm_rows(int dtA, int dtB, int dtC, int dtD, int la, int lb,
                      int lc, int act, int64_t M, int64_t N, int64_t K,
                      const void *A, const void *B, const void *C,
-                     const void *bias, float alpha,
-                     float beta, float scale_a, float scale_b,
+                     const void *bias, const uint8_t *xa, const uint8_t *xb,
+                     float alpha, float beta, float scale_a, float scale_b,
                      const int64_t *rows, int64_t n_rows, double *ref,
                      double *S, uint32_t *d_bits) {
     if (!valid_dtype(dtA) || !valid_dtype(dtB) || !valid_dtype(dtC) ||
         !valid_dtype(dtD) || M < 0 || N < 0 || K < 0 || !ref ||
-        act < ACT_IDENTITY || act > ACT_TANH)
+        act < ACT_IDENTITY || act > ACT_TANH || !mx_ok(xa, xb, dtA, dtB, K))
         return -1;
     if (rows == NULL) n_rows = M;
     const double al = (double)alpha, be = (double)beta;
@@ -196,9 +231,9 @@ int oracle_gemm_rows(int dtA, int dtB, int dtC, int dtD, int la, int lb,
         double *acc = (double *)calloc((size_t)(N ? N : 1), sizeof(double));
         double *sab_abs = (double *)calloc((size_t)(N ? N : 1), sizeof(double));
         for (int64_t k = 0; k < K; ++k) {
-            double a = elem(A, dtA, la, M, K, i, k);
+            double a = elem(A, dtA, la, M, K, i, k) * mx_scale(xa, K, i, k);
             for (int64_t j = 0; j < N; ++j) {
-                double p = a * elem(B, dtB, lb, K, N, k, j);
+                double p = a * (elem(B, dtB, lb, K, N, k, j) * mx_scale(xb, K, j, k));
                 acc[j] += p;
                 sab_abs[j] += fabs(p);
             }
@@ -223,12 +258,13 @@ int oracle_gemm_rows(int dtA, int dtB, int dtC, int dtD, int la, int lb,
 int oracle_gemm_entries(int dtA, int dtB, int dtC, int dtD, int la, int lb,
                         int lc, int act, int64_t M, int64_t N, int64_t K,
                         const void *A, const void *B, const void *C,
-                        const void *bias, float alpha, float beta, float scale_a, float scale_b,
+                        const void *bias, const uint8_t *xa, const uint8_t *xb,
+                        float alpha, float beta, float scale_a, float scale_b,
                         const int64_t *ii, const int64_t *jj, int64_t n,
                         double *ref, double *S, uint32_t *d_bits) {
     if (!valid_dtype(dtA) || !valid_dtype(dtB) || !valid_dtype(dtC) ||
         !valid_dtype(dtD) || M < 0 || N < 0 || K < 0 || !ref || !ii || !jj ||
-        act < ACT_IDENTITY || act > ACT_TANH)
+        act < ACT_IDENTITY || act > ACT_TANH || !mx_ok(xa, xb, dtA, dtB, K))
         return -1;
     const double al = (double)alpha, be = (double)beta;
     const double sab = (double)scale_a * (double)scale_b;
@@ -239,7 +275,8 @@ int oracle_gemm_entries(int dtA, int dtB, int dtC, int dtD, int la, int lb,
         if (i < 0 || i >= M || j < 0 || j >= N) { bad = 1; continue; }
         double acc = 0.0, sabs = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            double p = elem(A, dtA, la, M, K, i, k) * elem(B, dtB, lb, K, N, k, j);
+            double p = (elem(A, dtA, la, M, K, i, k) * mx_scale(xa, K, i, k)) *
+                       (elem(B, dtB, lb, K, N, k, j) * mx_scale(xb, K, j, k));
             acc += p;
             sabs += fabs(p);
         }

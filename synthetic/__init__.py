@@ -54,6 +54,8 @@ def raw(t: torch.Tensor) -> np.ndarray:
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.float8_e4m3fn:
         return t.view(torch.uint8).numpy()
+    if t.dtype == torch.uint8:          # E8M0 scale codes
+        return t.numpy()
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -81,6 +83,10 @@ class Problem:
     lb: str = ROW
     lc: str = ROW
     bias: Optional[torch.Tensor] = None   # length-N row vector in dtype_cd (None: no bias)
+    # MX block scales (E8M0 codes, uint8): mx_a [M, K/32] for the rows of A,
+    # mx_b [N, K/32] for the columns of B; None for a non-MX problem
+    mx_a: Optional[torch.Tensor] = None
+    mx_b: Optional[torch.Tensor] = None
 
     @property
     def flops(self) -> int:
@@ -231,3 +237,75 @@ def config5(M: int, N: int, K: int, seed: int = 0) -> Problem:
     """fp8 e4m3 A, B ~ N(0,1) quantized per tensor, bf16 D, beta = 0; B [N, K]."""
     return make_problem(M, N, K, dtype_ab=F8, dtype_cd=BF16, la=ROW, lb=COL,
                         seed=seed)
+
+
+# ---------------------------------------------------------------------------
+# MX (OCP Microscaling v1.0) inputs: e4m3 elements, one E8M0 scale per 32
+# consecutive elements along K
+# ---------------------------------------------------------------------------
+
+MX_BLOCK = 32
+E4M3_EMAX = 8          # largest e4m3 binade: 448 = 1.75 * 2^8
+
+
+def mx_quantize(x32: np.ndarray) -> Tuple[np.ndarray, torch.Tensor]:
+    """Quantize logical [R, K] fp32 rows block by block (the MX conversion):
+    shared exponent floor(log2(amax)) - 8 per 32-element block, stored as the
+    E8M0 code e + 127 (clamped to 0..254; an all-zero block gets 127), and
+    elements x / 2^e cast to e4m3 (RNE, saturating). Returns (elements as
+    logical fp32 [R, K] before the e4m3 cast, codes [R, K/32] uint8)."""
+    R, K = x32.shape
+    assert K % MX_BLOCK == 0
+    blk = x32.reshape(R, K // MX_BLOCK, MX_BLOCK).astype(np.float64)
+    amax = np.abs(blk).max(axis=2)
+    safe = np.where(amax > 0, amax, 1.0)
+    e = np.where(amax > 0, np.floor(np.log2(safe)) - E4M3_EMAX, 0.0)
+    code = np.clip(e + 127, 0, 254).astype(np.uint8)
+    q = blk / np.exp2(code.astype(np.float64) - 127)[:, :, None]
+    return q.reshape(R, K).astype(np.float32), torch.from_numpy(np.ascontiguousarray(code))
+
+
+def make_mx_problem(M: int, N: int, K: int, *, la: str = ROW, lb: str = COL, lc: str = ROW,
+                    dist_c: Optional[str] = None, alpha: float = 1.0, beta: float = 0.0,
+                    dist_bias: Optional[str] = None, std_b: float = 1.0,
+                    seed: int = 0, rng=None) -> Problem:
+    """MXFP8 problem: A, B ~ N(0,1) (B times std_b) quantized per 32-block of
+    K; bf16 C / D. Draw order A, B, C, bias as in make_problem."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    a32 = _draw(rng, (M, K), "normal")
+    b32 = _draw(rng, (K, N), "normal", std_b)
+    c = None
+    if dist_c is not None:
+        c = cast(to_storage(_draw(rng, (M, N), dist_c), lc), BF16)
+    bias = cast(_draw(rng, (N,), dist_bias), BF16) if dist_bias is not None else None
+    qa, xa = mx_quantize(a32)
+    qbt, xb = mx_quantize(np.ascontiguousarray(b32.T))
+    A = cast(to_storage(qa, la), F8)
+    B = cast(to_storage(np.ascontiguousarray(qbt.T), lb), F8)
+    return Problem(M, N, K, A, B, c, alpha, beta, None, None, F8, BF16, la, lb, lc, bias,
+                   xa, xb)
+
+
+def mx_integer_problem(M: int, N: int, K: int, *, la: str = ROW, lb: str = COL,
+                       lc: str = ROW, lo: int = -2, hi: int = 2, emin: int = -2,
+                       emax: int = 2, with_c: bool = True, beta: float = 1.0,
+                       with_bias: bool = False, seed: int = 0) -> Problem:
+    """MX problem with integer elements in [lo, hi] and scale codes
+    127 + U{emin..emax}: every scaled product and partial sum is a small
+    dyadic number, exact in fp32."""
+    rng = np.random.default_rng(seed)
+    a32 = rng.integers(lo, hi + 1, size=(M, K)).astype(np.float32)
+    b32 = rng.integers(lo, hi + 1, size=(K, N)).astype(np.float32)
+    c = None
+    if with_c:
+        c = cast(to_storage(rng.integers(lo, hi + 1, size=(M, N)).astype(np.float32), lc), BF16)
+    bias = None
+    if with_bias:
+        bias = cast(rng.integers(lo, hi + 1, size=(N,)).astype(np.float32), BF16)
+    nb = K // MX_BLOCK
+    xa = torch.from_numpy((127 + rng.integers(emin, emax + 1, size=(M, nb))).astype(np.uint8))
+    xb = torch.from_numpy((127 + rng.integers(emin, emax + 1, size=(N, nb))).astype(np.uint8))
+    A = cast(to_storage(a32, la), F8)
+    B = cast(to_storage(b32, lb), F8)
+    return Problem(M, N, K, A, B, c, 1.0, beta if with_c else 0.0, None, None, F8, BF16,
+                   la, lb, lc, bias, xa, xb)

@@ -482,3 +482,123 @@ def test_bias_activation_rows_equal_entries():
         ent = oracle.gemm_entries(p, ii, jj, act=act)
         assert np.array_equal(ent.ref, rows.ref[ii, jj])
         assert np.array_equal(ent.d_bits, rows.d_bits[ii, jj])
+
+
+# ---------------------------------------------------------------- MX block scales
+# The pages name MXFP8 among the scaled GEMMs ("Generating State-of-the-Art
+# GEMMs with TorchInductor's CuteDSL backend", sections 5.1 and 5.2); the
+# format (32-element blocks along K, E8M0 scales) is the OCP MX v1.0 one.
+
+def test_decode_e8m0_definition():
+    codes = np.arange(256, dtype=np.uint32)
+    got = oracle.decode("e8m0", codes)
+    # an unsigned biased exponent: code c is 2^(c-127) computed with
+    # torch's ldexp; 0xFF is NaN
+    want = torch.ldexp(torch.ones(255, dtype=torch.float64),
+                       torch.arange(255, dtype=torch.int64) - 127).numpy()
+    assert np.array_equal(got[:255], want)
+    assert np.isnan(got[255])
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127 and got[254] == 2.0 ** 127
+
+
+def _with_mx(p, fa, fb):
+    nb = p.K // 32
+    xa = torch.tensor([[fa(i, b) for b in range(nb)] for i in range(p.M)], dtype=torch.uint8)
+    xb = torch.tensor([[fb(j, b) for b in range(nb)] for j in range(p.N)], dtype=torch.uint8)
+    import dataclasses
+    return dataclasses.replace(p, mx_a=xa, mx_b=xb, scale_a=None, scale_b=None)
+
+
+def test_mx_unit_scales_equal_plain_fp8():
+    p = syn.make_problem(24, 40, 96, dtype_ab="f8e4m3", dtype_cd="bf16", la="row", lb="col",
+                         dist_c="normal", beta=0.5, seed=80)
+    import dataclasses
+    plain = dataclasses.replace(p, scale_a=None, scale_b=None)
+    mx = _with_mx(p, lambda i, b: 127, lambda j, b: 127)
+    r0, r1 = oracle.gemm(plain), oracle.gemm(mx)
+    assert np.array_equal(r0.ref, r1.ref) and np.array_equal(r0.d_bits, r1.d_bits)
+    assert np.array_equal(r0.S, r1.S)
+
+
+def test_mx_all_ones_closed_form():
+    # A = B = 1, four blocks; A's block b of row i scaled 2^(b - i%3), B's
+    # column j scaled 2^(j%2): D = 32 * (1+2+4+8) * 2^(j%2 - i%3)
+    M, N, K = 9, 6, 128
+    p = syn.integer_problem(M, N, K, dtype_ab="f8e4m3", dtype_cd="bf16", lo=1, hi=1,
+                            with_c=False)                       # e4m3 ones
+    p = _with_mx(p, lambda i, b: 127 + b - i % 3, lambda j, b: 127 + j % 2)
+    r = oracle.gemm(p)
+    want = np.array([[480.0 * 2.0 ** (j % 2 - i % 3) for j in range(N)] for i in range(M)])
+    assert np.array_equal(r.ref, want)
+
+
+@pytest.mark.parametrize("la,lb", list(itertools.product(LAYOUTS, LAYOUTS)))
+def test_mx_equals_prescaled_plain_gemm(la, lb):
+    # Scaling a block by 2^e is multiplying its elements by 2^e: with
+    # integer elements in [-2, 2] and |e| <= 2 the premultiplied elements are
+    # exact e4m3 values, so the plain (already pinned) GEMM of the
+    # premultiplied operands must give the same values bit for bit. Scales
+    # differ per row and per block, so a transposed or shifted scale index
+    # changes the result.
+    q = syn.mx_integer_problem(20, 28, 160, la=la, lb=lb, lc="row", seed=81)
+    xa = 2.0 ** (q.mx_a.numpy().astype(np.float64) - 127)       # [M, K/32]
+    xb = 2.0 ** (q.mx_b.numpy().astype(np.float64) - 127)       # [N, K/32]
+    a = oracle.decode("f8e4m3", syn.raw(q.A)).reshape(q.A.shape)
+    b = oracle.decode("f8e4m3", syn.raw(q.B)).reshape(q.B.shape)
+    a_log = a if la == "row" else a.T                            # [M, K]
+    b_log = b if lb == "row" else b.T                            # [K, N]
+    a2 = a_log * np.repeat(xa, 32, axis=1)
+    b2 = b_log * np.repeat(xb, 32, axis=1).T
+    import dataclasses
+    plain = dataclasses.replace(
+        q, A=syn.cast(syn.to_storage(a2.astype(np.float32), la), "f8e4m3"),
+        B=syn.cast(syn.to_storage(b2.astype(np.float32), lb), "f8e4m3"), mx_a=None, mx_b=None,
+        scale_a=1.0, scale_b=1.0)
+    assert np.array_equal(oracle.decode("f8e4m3", syn.raw(plain.A)).reshape(q.A.shape),
+                          syn.to_storage(a2, la))                # premultiplied exactly
+    r_mx, r_plain = oracle.gemm(q), oracle.gemm(plain)
+    assert np.array_equal(r_mx.ref, r_plain.ref)
+    assert np.array_equal(r_mx.S, r_plain.S)
+    assert np.array_equal(r_mx.d_bits, r_plain.d_bits)
+
+
+def test_mx_nan_scale_poisons_one_row_or_column():
+    p = syn.mx_integer_problem(6, 5, 64, seed=82, with_c=False)
+    p.mx_a[2, 1] = 255
+    p.mx_b[4, 0] = 255
+    r = oracle.gemm(p)
+    nan = np.isnan(r.ref)
+    assert nan[2, :].all() and nan[:, 4].all()
+    assert nan.sum() == 5 + 6 - 1
+
+
+def test_mx_rejects_partial_blocks_and_half_scales():
+    p = syn.mx_integer_problem(4, 4, 64, seed=83)
+    import dataclasses
+    with pytest.raises(ValueError):      # K not a multiple of 32
+        oracle.gemm(dataclasses.replace(p, K=48))
+    with pytest.raises(ValueError):      # one operand scaled, the other not
+        oracle.gemm(dataclasses.replace(p, mx_b=None))
+    with pytest.raises(ValueError):      # MX elements must be e4m3
+        q = syn.integer_problem(4, 4, 64, dtype_ab="bf16", dtype_cd="bf16")
+        oracle.gemm(dataclasses.replace(q, mx_a=p.mx_a, mx_b=p.mx_b))
+
+
+def test_mx_quantizer_round_trips_within_e4m3_precision():
+    # the input generator's MX conversion: every block's largest element
+    # lands in e4m3's top binade [256, 448]; dequantized values sit within
+    # half an e4m3 ulp (2^-4 relative) of the fp32 draw, except those above
+    # 448 * 2^e, which saturate to +-448 * 2^e (the MX conversion clamps)
+    rng = np.random.default_rng(84)
+    x = rng.standard_normal((8, 256)).astype(np.float32)
+    q, codes = syn.mx_quantize(x)
+    e = codes.numpy().astype(np.float64) - 127
+    qe = syn.cast(q, "f8e4m3").float().numpy().astype(np.float64)
+    top = np.abs(qe).reshape(8, 8, 32).max(axis=2)
+    assert ((top >= 256) & (top <= 448)).all()
+    X = np.repeat(2.0 ** e, 32, axis=1)
+    deq = qe * X
+    sat = np.abs(x) > 448.0 * X
+    assert sat.any() and (np.abs(deq[sat]) == 448.0 * X[sat]).all()
+    ok = np.abs(deq - x) <= 2.0 ** -4 * np.abs(x) + 2.0 ** -10 * X
+    assert ok[~sat].all()
