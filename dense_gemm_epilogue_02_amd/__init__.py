@@ -107,6 +107,8 @@ def _load():
     L.gemm_plan_run_scaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp, vp, vp]
     L.gemm_plan_run_ex.restype = st
     L.gemm_plan_run_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp, vp, vp]
+    L.gemm_plan_run_mx.restype = st
+    L.gemm_plan_run_mx.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp, vp, vp]
     L.gemm_plan_run_batched.restype = st
     L.gemm_plan_run_batched.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                         i64, i64, f32, f32, vp, vp, vp]
@@ -131,7 +133,7 @@ lib = _load()
 
 EXPORTED = ("gemm_plan_create", "gemm_plan_create_simple", "gemm_plan_destroy",
             "gemm_plan_set_config", "gemm_plan_run", "gemm_plan_run_scaled",
-            "gemm_plan_run_ex", "gemm_plan_run_batched", "grouped_gemm_run", "gemm_plan_describe", "gemm_last_error",
+            "gemm_plan_run_ex", "gemm_plan_run_mx", "gemm_plan_run_batched", "grouped_gemm_run", "gemm_plan_describe", "gemm_last_error",
             "gemm_status_string", "gemm_supported_count", "gemm_supported_get",
             "gemm_version")
 
@@ -199,6 +201,13 @@ def gemm_plan_run_ex(plan: int, A, B, C, D, bias, M: int, N: int, K: int, alpha:
                      beta: float, scale_a=None, scale_b=None, stream=None) -> None:
     _check(lib.gemm_plan_run_ex(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(bias), M, N, K,
                                 alpha, beta, _ptr(scale_a), _ptr(scale_b), _stream(stream)))
+
+
+def gemm_plan_run_mx(plan: int, A, B, C, D, bias, M: int, N: int, K: int, alpha: float,
+                     beta: float, mx_scale_a, mx_scale_b, stream=None) -> None:
+    _check(lib.gemm_plan_run_mx(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(bias), M, N, K,
+                                alpha, beta, _ptr(mx_scale_a), _ptr(mx_scale_b),
+                                _stream(stream)))
 
 
 def gemm_plan_run_batched(plan: int, A, B, C, D, bias, M: int, N: int, K: int, batch: int,
@@ -337,6 +346,23 @@ class Plan:
         else:
             gemm_plan_run_scaled(self.handle, A, B, C, D, M, N, K, alpha, beta, scale_a,
                                  scale_b, stream)
+
+    def run_mx(self, A, B, C, D, M, N, K, mx_scale_a, mx_scale_b, alpha=1.0, beta=0.0,
+               stream=None, bias=None):
+        """MX block-scaled GEMM: mx_scale_a [M, K/32] and mx_scale_b [N, K/32]
+        uint8 E8M0 device tensors."""
+        import torch
+        self.check(A, B, C, D, M, N, K, beta)
+        if min(M, N, K) > 0 and K % 32 == 0:
+            for t, rows, name in ((mx_scale_a, M, "mx_scale_a"), (mx_scale_b, N, "mx_scale_b")):
+                if t is None or not t.is_cuda or t.dtype != torch.uint8 or not t.is_contiguous():
+                    raise ValueError(f"{name} must be a contiguous uint8 device tensor")
+                if t.numel() < rows * (K // 32):
+                    raise ValueError(f"{name} holds {t.numel()} bytes, needs {rows * (K // 32)}")
+            if bias is not None:
+                _need(bias, N, "bias", self.dcd)
+        gemm_plan_run_mx(self.handle, A, B, C, D, bias, M, N, K, alpha, beta, mx_scale_a,
+                         mx_scale_b, stream)
 
     def run_batched(self, A, B, C, D, M, N, K, batch, strides, alpha=1.0, beta=0.0,
                     scale_a=None, scale_b=None, stream=None, bias=None):

@@ -70,7 +70,7 @@ const Tuple kSupported[] = {
 };
 constexpr int kNumSupported = (int)(sizeof(kSupported) / sizeof(kSupported[0]));
 
-int elem_bytes(int fam) { return fam == FAM_F32 ? 4 : fam == FAM_F8 ? 1 : 2; }
+int elem_bytes(int fam) { return fam == FAM_F32 ? 4 : (fam == FAM_F8 || fam == FAM_MXF8) ? 1 : 2; }
 int out_bytes(int fam) { return fam == FAM_F32 ? 4 : 2; }
 
 // ------------------------------------------------------------------ registry
@@ -78,7 +78,8 @@ int out_bytes(int fam) { return fam == FAM_F32 ? 4 : 2; }
 struct Registry {
     std::vector<KernelEntry> all;
     Registry() {
-        const KernelEntry *(*tables[])(int *) = {entries_f32, entries_f16, entries_bf16, entries_f8};
+        const KernelEntry *(*tables[])(int *) = {entries_f32, entries_f16, entries_bf16, entries_f8,
+                                                 entries_mxf8};
         for (auto t : tables) {
             int n = 0;
             const KernelEntry *e = t(&n);
@@ -248,8 +249,9 @@ int min_iters(int fam) { return fam == FAM_F32 ? 1 : 8; }
 template <class OccFn>
 gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const void *C, const void *D,
                    const void *bias, int64_t M, int64_t N, int64_t K, float beta, int cus, OccFn occ_of,
-                   Decision &d, int64_t batch = 1) {
-    const int fam = pl->fam;
+                   Decision &d, int64_t batch = 1, const void *mx_a = nullptr,
+                   const void *mx_b = nullptr) {
+    const int fam = mx_a ? FAM_MXF8 : pl->fam;
     const int esz = elem_bytes(fam), osz = out_bytes(fam);
     const bool a_kc = pl->la == GEMM_ROW_MAJOR, b_kc = pl->lb == GEMM_COL_MAJOR;
     d.vec_cd = (pl->lc == GEMM_ROW_MAJOR && N % 4 == 0 &&
@@ -267,6 +269,14 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
             why = operand_vec_problem(A, a_kc, a_kc ? K : M, e ? e->bm : 0, esz, kb);
             if (!why) why = operand_vec_problem(B, b_kc, b_kc ? K : N, e ? e->bn : 0, esz, kb);
         }
+        // MX tile kernels copy each row's four block scales of a k-tile as one
+        // word, at a 32-bit offset
+        if (!why && mx_a &&
+            (K % 128 != 0 || reinterpret_cast<uintptr_t>(mx_a) % 4 != 0 ||
+             reinterpret_cast<uintptr_t>(mx_b) % 4 != 0))
+            why = "MX tile kernels need K % 128 == 0 and 4-byte aligned scale arrays";
+        if (!why && mx_a && (M * (K / 32) > 0x7FFFFFFFLL || N * (K / 32) > 0x7FFFFFFFLL))
+            why = "MX scale arrays beyond 2^31 bytes";
         if (e && !why) d.e = e;
         else d.why_generic = why ? why : "no tile kernel for this layout";
     } else {
@@ -439,13 +449,16 @@ Prob make_prob(const void *A, const void *B, const void *C, void *D, int64_t M, 
     p.vec_cd = d.vec_cd;
     p.batch = 1;
     p.stride_a = p.stride_b = p.stride_c = p.stride_d = 0;
+    p.mx_a = p.mx_b = nullptr;
     return p;
 }
 
-// Batch shape of one run (a single GEMM is batch 1 with zero strides).
-struct Batch {
+// Options of one run beyond a single GEMM: a strided batch (a single GEMM is
+// batch 1 with zero strides) and MX block scales.
+struct RunOpts {
     int64_t count = 1;
     int64_t sa = 0, sb = 0, sc = 0, sd = 0;   // element strides
+    const uint8_t *mx_a = nullptr, *mx_b = nullptr;
 };
 
 EpiArgs make_epi(const gemm_plan_s *pl, float alpha, float beta, const float *sa, const float *sb,
@@ -461,20 +474,21 @@ EpiArgs make_epi(const gemm_plan_s *pl, float alpha, float beta, const float *sa
     return e;
 }
 
-gemm_status run_generic(const gemm_plan_s *pl, const Prob &p, const EpiArgs &ep, hipStream_t st) {
+gemm_status run_generic(const gemm_plan_s *pl, int fam, const Prob &p, const EpiArgs &ep,
+                        hipStream_t st) {
     GenericArgs g;
     g.p = p;
     g.e = ep;
     g.la_row = pl->la == GEMM_ROW_MAJOR;
     g.lb_row = pl->lb == GEMM_ROW_MAJOR;
-    hipError_t e = launch_generic(pl->fam, g, st);
+    hipError_t e = launch_generic(fam, g, st);
     if (e != hipSuccess) return hip_fail(e, "generic kernel launch");
     return GEMM_OK;
 }
 
 gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C, void *D, int64_t M,
                     int64_t N, int64_t K, float alpha, float beta, const float *sa, const float *sb,
-                    const void *bias, void *stream, const Batch &bt = Batch()) {
+                    const void *bias, void *stream, const RunOpts &bt = RunOpts()) {
     if (!plan_ok(pl)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_run: invalid plan handle");
     gemm_status st = validate_problem(pl, A, B, C, D, M, N, K, beta, "gemm_plan_run");
     if (st != GEMM_OK) return st;
@@ -506,14 +520,17 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
                 [&](const KernelEntry *e, int *occ) {
                     return kernel_occupancy(dev, e->fn_persistent, e->nt, occ);
                 },
-                d, bt.count);
+                d, bt.count, bt.mx_a, bt.mx_b);
     if (st != GEMM_OK) return st;
+    const int fam = bt.mx_a ? FAM_MXF8 : pl->fam;
     Prob p = make_prob(A, B, C, D, M, N, K, d);
     p.batch = (int)bt.count;
     p.stride_a = bt.sa;
     p.stride_b = bt.sb;
     p.stride_c = bt.sc;
     p.stride_d = bt.sd;
+    p.mx_a = bt.mx_a;
+    p.mx_b = bt.mx_b;
     const EpiArgs ep = make_epi(pl, alpha, beta, sa, sb, bias);
     if (!d.e) {
         if (batched) {   // the scalar kernel takes one problem per launch
@@ -522,10 +539,10 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
                                    static_cast<const char *>(B) + b * bt.sb * esz,
                                    C ? static_cast<const char *>(C) + b * bt.sc * osz : nullptr,
                                    static_cast<char *>(D) + b * bt.sd * osz, M, N, K, d);
-                st = run_generic(pl, q, ep, hs);
+                st = run_generic(pl, fam, q, ep, hs);
             }
         } else {
-            st = run_generic(pl, p, ep, hs);
+            st = run_generic(pl, fam, p, ep, hs);
         }
         if (st == GEMM_OK) note_stream(pl, hs);
         return st == GEMM_OK ? ok() : st;
@@ -670,13 +687,32 @@ gemm_status gemm_plan_run_batched(gemm_plan_t p, const void *A, const void *B, c
             return fail(GEMM_INVALID_ARG, "gemm_plan_run_batched: negative size");
         return ok();
     }
-    Batch bt;
+    RunOpts bt;
     bt.count = batch_count;
     bt.sa = stride_a;
     bt.sb = stride_b;
     bt.sc = stride_c;
     bt.sd = stride_d;
     return run_one(p, A, B, C, D, M, N, K, alpha, beta, scale_a, scale_b, bias, stream, bt);
+}
+
+gemm_status gemm_plan_run_mx(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,
+                             const void *bias, int64_t M, int64_t N, int64_t K, float alpha,
+                             float beta, const uint8_t *mx_scale_a, const uint8_t *mx_scale_b,
+                             void *stream) {
+    if (!plan_ok(p)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_run_mx: invalid plan handle");
+    if (p->fam != FAM_F8)
+        return fail(GEMM_UNSUPPORTED, "gemm_plan_run_mx: MX block scaling needs an F8_E4M3 plan");
+    if (K % 32 != 0)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_run_mx: K = %lld is not a multiple of the "
+                    "32-element MX block", (long long)K);
+    if (M > 0 && N > 0 && K > 0 && (!mx_scale_a || !mx_scale_b))
+        return fail(GEMM_INVALID_ARG, "gemm_plan_run_mx: a block-scale array is NULL");
+    RunOpts ro;
+    ro.mx_a = mx_scale_a;
+    ro.mx_b = mx_scale_b;
+    if (K == 0) ro.mx_a = ro.mx_b = nullptr;   // nothing to scale: beta*C (+bias) only
+    return run_one(p, A, B, C, D, M, N, K, alpha, beta, nullptr, nullptr, bias, stream, ro);
 }
 
 gemm_status gemm_plan_run_ex(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,
@@ -812,7 +848,7 @@ gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32
         Decision d;
         d.vec_cd = 0;
         const Prob p = make_prob(q.A, q.B, beta == 0.0f ? nullptr : q.C, q.D, q.M, q.N, q.K, d);
-        if ((st = run_generic(pl, p, ep, hs)) != GEMM_OK) return st;
+        if ((st = run_generic(pl, pl->fam, p, ep, hs)) != GEMM_OK) return st;
         note_stream(pl, hs);
     }
     return ok();

@@ -44,7 +44,9 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 
-enum Family { FAM_F32 = 0, FAM_F16 = 1, FAM_BF16 = 2, FAM_F8 = 3 };
+// FAM_MXF8: e4m3 operands with MX block scales (one E8M0 scale per 32
+// elements along K, per row of A and per column of B).
+enum Family { FAM_F32 = 0, FAM_F16 = 1, FAM_BF16 = 2, FAM_F8 = 3, FAM_MXF8 = 4 };
 
 constexpr uint32_t OOB_OFFSET = 0x80000000u;
 constexpr int NUM_RECORDS = 0x7FFFFFFF;
@@ -56,6 +58,7 @@ template <int FAM> struct Fam;
 
 template <> struct Fam<FAM_BF16> {
     static constexpr int ESZ = 2, CPL = 1;
+    static constexpr bool MX = false;
     using Out = __bf16;
     static __device__ __forceinline__ void mma(f32x16 &c, const u32x4 *x, const u32x4 *y) {
         c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[0]),
@@ -64,6 +67,7 @@ template <> struct Fam<FAM_BF16> {
 };
 template <> struct Fam<FAM_F16> {
     static constexpr int ESZ = 2, CPL = 1;
+    static constexpr bool MX = false;
     using Out = _Float16;
     static __device__ __forceinline__ void mma(f32x16 &c, const u32x4 *x, const u32x4 *y) {
         c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x[0]),
@@ -72,6 +76,7 @@ template <> struct Fam<FAM_F16> {
 };
 template <> struct Fam<FAM_F32> {
     static constexpr int ESZ = 4, CPL = 1;
+    static constexpr bool MX = false;
     using Out = float;
     static __device__ __forceinline__ void mma(f32x16 &c, const u32x4 *x, const u32x4 *y) {
         const f32x4 xv = __builtin_bit_cast(f32x4, x[0]);
@@ -84,6 +89,7 @@ template <> struct Fam<FAM_F32> {
 };
 template <> struct Fam<FAM_F8> {
     static constexpr int ESZ = 1, CPL = 2;
+    static constexpr bool MX = false;
     using Out = __bf16;
     static __device__ __forceinline__ void mma(f32x16 &c, const u32x4 *x, const u32x4 *y) {
         i32x8 a, b;
@@ -94,6 +100,29 @@ template <> struct Fam<FAM_F8> {
         }
         // format 0 = FP8 E4M3 for both operands; E8M0 scale 127 = 1.0
         c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    }
+};
+// The 32x32x64 scaled MFMA reads, in lane l, 32 bytes of row l%32: bytes
+// 0-15 belong to the first 32-element block of its 64 K positions, bytes
+// 16-31 to the second; the E8M0 scale of (row r, block b) comes from lane
+// r + 32b, byte OPSEL of its scale register (lane layout measured on gfx950).
+// The MX tile kernels therefore give lane group g chunks 2s*2+g and 2s*2+2+g
+// of substep s, so each hardware block holds one real 32-element K block.
+template <> struct Fam<FAM_MXF8> {
+    static constexpr int ESZ = 1, CPL = 2;
+    static constexpr bool MX = true;
+    using Out = __bf16;
+    template <int OPSEL>
+    static __device__ __forceinline__ void mma_mx(f32x16 &c, const u32x4 *x, const u32x4 *y,
+                                                  uint32_t sx, uint32_t sy) {
+        i32x8 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = (int)x[0][e]; a[e + 4] = (int)x[1][e];
+            b[e] = (int)y[0][e]; b[e + 4] = (int)y[1][e];
+        }
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPSEL, (int)sx, OPSEL,
+                                                             (int)sy);
     }
 };
 
@@ -113,6 +142,10 @@ struct Prob {
     // space is batch-major. batch <= 1 is a single GEMM.
     int batch;
     int64_t stride_a, stride_b, stride_c, stride_d;
+    // MX block scales (FAM_MXF8 only): E8M0 bytes [M][K/32] for A's rows and
+    // [N][K/32] for B's columns; the tile kernels need K % 128 == 0 and
+    // 4-byte aligned arrays.
+    const uint8_t *mx_a, *mx_b;
 };
 
 // Epilogue activations (the values of gemm_epilogue).
@@ -430,10 +463,19 @@ struct Tile {
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
     static constexpr int SUBSTEPS = CH / (2 * CPL);
+    static constexpr bool MX = F::MX;
+    static_assert(!MX || (CH == 8 && STAGES == 2 && PIPE == 0),
+                  "MX tiles: 128-byte rows (four scale blocks per k-tile), two stages");
     // LDS: [A stage 0 .. A stage S-1 | B stage 0 .. B stage S-1]
     static constexpr int A_BYTES = BM * KB, B_BYTES = BN * KB;
     static constexpr int B_OFF = STAGES * A_BYTES;
-    static constexpr int LDS_BYTES = STAGES * (A_BYTES + B_BYTES);
+    // MX: each stage also holds one 32-bit word of E8M0 scales (the k-tile's
+    // four blocks) per tile row of A and of B, each region padded to whole
+    // 64-lane copy instructions.
+    static constexpr int SC_A = MX ? (BM + 63) / 64 * 256 : 0;
+    static constexpr int SC_B = MX ? (BN + 63) / 64 * 256 : 0;
+    static constexpr int SC_OFF = STAGES * (A_BYTES + B_BYTES);
+    static constexpr int LDS_BYTES = STAGES * (A_BYTES + B_BYTES + SC_A + SC_B);
     static_assert(CH == 8 || CH == 4, "64- or 128-byte LDS rows");
     static_assert(STAGES == 2 || (A_KC && B_KC), "deep pipelines need direct loads");
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
@@ -462,6 +504,27 @@ struct Tile {
     struct Acc {
         f32x16 v[FN][FM];
     };
+
+    // MX: copy the k-tile's scale words of the tile's rows of A and B into
+    // the stage (LDS DMA, 4 bytes a lane; rows past the edge read as zero).
+    // Byte b of a row's word is the scale of the k-tile's block b.
+    static __device__ __forceinline__ void issue_scales(const Prob &p, int tm, int tn, int kt,
+                                                        char *sc, int tid) {
+        constexpr int IA = SC_A / 256, IB = SC_B / 256, CW = COPY_NT / 64;
+        const int lane = tid & 63, wave = uniform(tid >> 6);
+        const uint32_t nb = (uint32_t)(p.K >> 5);   // scale bytes per row
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.mx_a), rb = make_rsrc(p.mx_b);
+        for (int q = wave; q < IA + IB; q += CW) {
+            const bool is_a = q < IA;
+            const int row = (is_a ? q : q - IA) * 64 + lane;
+            const int64_t g_row = is_a ? (int64_t)tm * BM + row : (int64_t)tn * BN + row;
+            const bool ok = row < (is_a ? BM : BN) && g_row < (is_a ? p.M : p.N);
+            const uint32_t voff = ok ? (uint32_t)g_row * nb : OOB_OFFSET;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                is_a ? ra : rb, (__attribute__((address_space(3))) void *)(sc + q * 256), 4, voff,
+                kt * 4, 0, 0);
+        }
+    }
 
     static __device__ __forceinline__ void zero(Acc &a) {
 #pragma unroll
@@ -539,6 +602,9 @@ struct Tile {
         uint32_t ld;
         int rl, kl;
         const bool copy_wave = COPY_NT == NT || uniform(tid >> 6) < COPY_NT / 64;
+        if constexpr (MX) {
+            if (copy_wave) issue_scales(p, tm, tn, kt, lds + SC_OFF + st * (SC_A + SC_B), tid);
+        }
         if constexpr (A_KC) {
             if (copy_wave) L.da.issue(kt, k_left, stage, tid);
         } else {
@@ -609,10 +675,33 @@ struct Tile {
         else compute(sA, sB, acc, lane, wm, wn);
     }
 
-    // Multiply one LDS stage into the accumulators.
+    // 16-byte chunk of a 128-byte LDS row that lane group g reads as part c
+    // of substep s: contiguous 32-element halves for the unscaled types; for
+    // MX the two halves of each hardware scale block (see Fam<FAM_MXF8>).
+    static __device__ __forceinline__ int frag_chunk(int s, int g, int c) {
+        if constexpr (MX) return s * 2 * CPL + c * 2 + g;
+        else return s * 2 * CPL + g * CPL + c;
+    }
+
+    // Multiply one LDS stage into the accumulators (MX: with the k-tile's
+    // block scales).
     static __device__ __forceinline__ void compute(const char *sA, const char *sB, Acc &acc,
-                                                   int lane, int wm, int wn) {
+                                                   int lane, int wm, int wn,
+                                                   const char *sSc = nullptr) {
         const int g = lane >> 5, r = lane & 31;
+        // MX: this lane's scale words, shifted so byte 2s is the block its
+        // lane group multiplies in substep s
+        uint32_t scx[FN], scy[FM];
+        if constexpr (MX) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+                scx[i] = *reinterpret_cast<const uint32_t *>(sSc + SC_A + (wn * WTN + i * 32 + r) * 4) >>
+                         (8 * g);
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                scy[j] = *reinterpret_cast<const uint32_t *>(sSc + (wm * WTM + j * 32 + r) * 4) >>
+                         (8 * g);
+        }
 #pragma unroll
         for (int s = 0; s < SUBSTEPS; ++s) {
             u32x4 xf[FN][CPL], yf[FM][CPL];
@@ -622,7 +711,7 @@ struct Tile {
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
                     xf[i][c] = *reinterpret_cast<const u32x4 *>(
-                        sB + lds_off<CH>(row, s * 2 * CPL + g * CPL + c));
+                        sB + lds_off<CH>(row, frag_chunk(s, g, c)));
             }
 #pragma unroll
             for (int j = 0; j < FM; ++j) {
@@ -630,12 +719,19 @@ struct Tile {
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
                     yf[j][c] = *reinterpret_cast<const u32x4 *>(
-                        sA + lds_off<CH>(row, s * 2 * CPL + g * CPL + c));
+                        sA + lds_off<CH>(row, frag_chunk(s, g, c)));
             }
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
-                for (int j = 0; j < FM; ++j) F::mma(acc.v[i][j], xf[i], yf[j]);
+                for (int j = 0; j < FM; ++j) {
+                    if constexpr (MX) {
+                        if (s == 0) F::template mma_mx<0>(acc.v[i][j], xf[i], yf[j], scx[i], scy[j]);
+                        else F::template mma_mx<2>(acc.v[i][j], xf[i], yf[j], scx[i], scy[j]);
+                    } else {
+                        F::mma(acc.v[i][j], xf[i], yf[j]);
+                    }
+                }
         }
     }
 
@@ -698,8 +794,12 @@ struct Tile {
                 __syncthreads();
                 const int kt = kt0 + (i + 1) * stride;
                 if (i + 1 < n) issue_stage(p, tm, tn, kt, kvalid(kt), lds, par ^ 1, L, tid);
-                compute_any<PIPE>(lds + par * A_BYTES, lds + B_OFF + par * B_BYTES, acc, lane, wm,
-                                  wn);
+                if constexpr (MX)
+                    compute(lds + par * A_BYTES, lds + B_OFF + par * B_BYTES, acc, lane, wm, wn,
+                            lds + SC_OFF + par * (SC_A + SC_B));
+                else
+                    compute_any<PIPE>(lds + par * A_BYTES, lds + B_OFF + par * B_BYTES, acc, lane,
+                                      wm, wn);
                 if (i + 1 < n) store_regs(lds, par ^ 1, L, tid);
             }
         }

@@ -50,6 +50,7 @@ const KernelEntry *entries_bf16(int *count);
 const KernelEntry *entries_f16(int *count);
 const KernelEntry *entries_f32(int *count);
 const KernelEntry *entries_f8(int *count);
+const KernelEntry *entries_mxf8(int *count);
 
 // Scalar-load kernel for any alignment / stride (kernels_generic.hip).
 struct GenericArgs {

@@ -38,11 +38,18 @@ template <> __device__ __forceinline__ float ld_elem<FAM_F8>(const char *base, i
     return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) | s);
 }
 
+// OCP MX E8M0 scale: 2^(c-127); c = 0 is the fp32 subnormal 2^-127, 255 is NaN.
+__device__ __forceinline__ float e8m0(uint32_t c) {
+    if (c == 255u) return __builtin_nanf("");
+    return __builtin_bit_cast(float, c == 0u ? 0x00400000u : c << 23);
+}
+
 template <int FAM> struct OutT;
 template <> struct OutT<FAM_F32> { using T = float; };
 template <> struct OutT<FAM_F16> { using T = _Float16; };
 template <> struct OutT<FAM_BF16> { using T = __bf16; };
 template <> struct OutT<FAM_F8> { using T = __bf16; };
+template <> struct OutT<FAM_MXF8> { using T = __bf16; };
 
 template <int FAM>
 __global__ void __launch_bounds__(256) gemm_generic(GenericArgs a) {
@@ -63,8 +70,15 @@ __global__ void __launch_bounds__(256) gemm_generic(GenericArgs a) {
             const int64_t k = k0 + kk;
             const int64_t m = m0 + rr, n = n0 + rr;
             float av = 0.0f, bv = 0.0f;
-            if (k < p.K && m < p.M) av = ld_elem<FAM>(p.A, a.la_row ? m * p.K + k : m + k * p.M);
-            if (k < p.K && n < p.N) bv = ld_elem<FAM>(p.B, a.lb_row ? k * p.N + n : k + n * p.K);
+            constexpr int LF = FAM == FAM_MXF8 ? FAM_F8 : FAM;   // element decoder
+            if (k < p.K && m < p.M) av = ld_elem<LF>(p.A, a.la_row ? m * p.K + k : m + k * p.M);
+            if (k < p.K && n < p.N) bv = ld_elem<LF>(p.B, a.lb_row ? k * p.N + n : k + n * p.K);
+            if constexpr (FAM == FAM_MXF8) {
+                // block scales of A's row m and B's column n (K % 32 == 0);
+                // a power of two, so the scaled element is exact
+                if (k < p.K && m < p.M) av *= e8m0(p.mx_a[m * (p.K >> 5) + (k >> 5)]);
+                if (k < p.K && n < p.N) bv *= e8m0(p.mx_b[n * (p.K >> 5) + (k >> 5)]);
+            }
             As[kk][rr] = av;
             Bs[kk][rr] = bv;
         }
@@ -120,6 +134,7 @@ hipError_t launch_generic(int fam, const GenericArgs &a, hipStream_t st) {
     case FAM_F16: hipLaunchKernelGGL(gemm_generic<FAM_F16>, grid, block, 0, st, a); break;
     case FAM_BF16: hipLaunchKernelGGL(gemm_generic<FAM_BF16>, grid, block, 0, st, a); break;
     case FAM_F8: hipLaunchKernelGGL(gemm_generic<FAM_F8>, grid, block, 0, st, a); break;
+    case FAM_MXF8: hipLaunchKernelGGL(gemm_generic<FAM_MXF8>, grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -166,6 +166,27 @@ gemm_status gemm_plan_run_ex(gemm_plan_t plan, const void *A, const void *B,
                              float beta, const float *scale_a,
                              const float *scale_b, void *stream);
 
+/* MX block-scaled GEMM ("Generating State-of-the-Art GEMMs with
+ * TorchInductor's CuteDSL backend", sections 5.1 and 5.2: MXFP8 among the
+ * scaled GEMMs, with their own scale type, block size and layout; the format
+ * itself is the OCP Microscaling v1.0 one). The plan must have the
+ * (F8_E4M3, F8_E4M3, BF16, BF16, F32) tuple; A and B hold e4m3 elements in
+ * the plan's layouts, and
+ *   D = act(alpha * sum_k a(i,k) X_A(i,k/32) b(k,j) X_B(j,k/32) + beta*C + bias)
+ * where mx_scale_a is M x (K/32) and mx_scale_b is N x (K/32) E8M0 bytes,
+ * row-major whatever the operand layouts (scale row i belongs to row i of A,
+ * scale row j to column j of B); an E8M0 byte e is 2^(e-127), 0xFF is NaN.
+ * K must be a multiple of 32 (else GEMM_INVALID_ARG); the MFMA tile kernels
+ * run when K % 128 == 0 and both scale arrays are 4-byte aligned, otherwise
+ * the scalar kernel does. bias as in gemm_plan_run_ex. No per-tensor scales.
+ * A NULL scale array with M, N, K > 0 gives GEMM_INVALID_ARG; a plan of
+ * another type tuple gives GEMM_UNSUPPORTED. Buffers stay the caller's. */
+gemm_status gemm_plan_run_mx(gemm_plan_t plan, const void *A, const void *B,
+                             const void *C, void *D, const void *bias,
+                             int64_t M, int64_t N, int64_t K, float alpha,
+                             float beta, const uint8_t *mx_scale_a,
+                             const uint8_t *mx_scale_b, void *stream);
+
 /* Batched GEMM ("CUTLASS Python接口", batched GEMM: batch_count and
  * batch_stride_A/B/C): batch_count problems of one shape M x N x K; problem b
  * reads A + b*stride_a, B + b*stride_b, C + b*stride_c and writes

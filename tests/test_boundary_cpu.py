@@ -229,3 +229,29 @@ def test_batched_validation_before_any_device_call():
             g.Plan("bf16").run_batched(None, None, None, None, 8, 8, 8, 2, (64, 64, 64, 64))
     finally:
         g.gemm_plan_destroy(h)
+
+
+def test_mx_validation_before_any_device_call():
+    D, L, E = g.Dtype, g.Layout, g.Epilogue
+    run_mx = g.lib.gemm_plan_run_mx
+    args = lambda h, K, xa=16, xb=16: (h, 16, 16, None, 16, None, 8, 8, K, 1.0, 0.0, xa, xb,
+                                       None)
+    assert run_mx(*args(None, 64)) == g.Status.NOT_INITIALIZED
+    h = g.gemm_plan_create_simple(D.BF16, L.ROW_MAJOR, E.LINEAR)
+    try:
+        assert run_mx(*args(h, 64)) == g.Status.UNSUPPORTED
+        assert "F8_E4M3" in g.gemm_last_error()
+    finally:
+        g.gemm_plan_destroy(h)
+    h = g.gemm_plan_create(D.F8_E4M3, D.F8_E4M3, D.BF16, D.BF16, D.F32, L.ROW_MAJOR,
+                           L.COL_MAJOR, L.ROW_MAJOR, E.LINEAR)
+    try:
+        assert run_mx(*args(h, 48)) == g.Status.INVALID_ARG
+        assert "multiple of the 32-element" in g.gemm_last_error()
+        assert run_mx(*args(h, 64, xa=None)) == g.Status.INVALID_ARG
+        assert "NULL" in g.gemm_last_error()
+        # an empty output is a no-op
+        assert run_mx(h, None, None, None, None, None, 0, 8, 64, 1.0, 0.0, None, None,
+                      None) == g.Status.OK
+    finally:
+        g.gemm_plan_destroy(h)
