@@ -53,13 +53,12 @@ def lib():
         L.oracle_encode.argtypes = [ctypes.c_int, ctypes.c_double]
         L.oracle_decode_n.argtypes = [ctypes.c_int, vp, ctypes.c_int64, vp]
         L.oracle_encode_n.argtypes = [ctypes.c_int, vp, ctypes.c_int64, vp]
-        common = [ctypes.c_int] * 8 + [ctypes.c_int64] * 3 + [vp] * 6 + \
-                 [ctypes.c_float] * 4
+        common = [ctypes.c_int] * 8 + [ctypes.c_int64] * 3 + [vp] * 7 + \
+                 [ctypes.c_int] * 2 + [ctypes.c_float] * 4
         L.oracle_gemm_rows.restype = ctypes.c_int
-        L.oracle_gemm_rows.argtypes = common + [i64p, ctypes.c_int64, vp, vp, vp]
+        L.oracle_gemm_rows.argtypes = common + [i64p, ctypes.c_int64] + [vp] * 6
         L.oracle_gemm_entries.restype = ctypes.c_int
-        L.oracle_gemm_entries.argtypes = common + [i64p, i64p, ctypes.c_int64,
-                                                   vp, vp, vp]
+        L.oracle_gemm_entries.argtypes = common + [i64p, i64p, ctypes.c_int64] + [vp] * 6
         _lib = L
     return _lib
 
@@ -87,15 +86,22 @@ def encode(dtype: str, values) -> np.ndarray:
 class Result:
     """Oracle outputs for selected rows or entries."""
 
-    def __init__(self, ref, S, d_bits, dtype_d):
+    def __init__(self, ref, S, d_bits, dtype_d, z_ref=None, z_S=None, z_bits=None):
         self.ref = ref          # fp64 unrounded epilogue value
-        self.S = S              # |alpha s_A s_B| * sum_k |a b|
+        self.S = S              # |alpha s_A s_B| * sum_k |a b| (times the aux op's factor)
         self.d_bits = d_bits    # element_D bits of the once-rounded value
         self.dtype_d = dtype_d
+        self.z_ref = z_ref      # the activation's input (the auxiliary store), fp64
+        self.z_S = z_S          # its tolerance scale
+        self.z_bits = z_bits    # its element_D bits
 
     @property
     def d_exact(self) -> np.ndarray:
         return decode(self.dtype_d, self.d_bits)
+
+    @property
+    def z_exact(self) -> np.ndarray:
+        return decode(self.dtype_d, self.z_bits)
 
 
 def _scalars(p):
@@ -106,6 +112,9 @@ def _scalars(p):
 
 # Activations of the epilogue (the codes the C oracle takes).
 ACT = {"identity": 0, "relu": 1, "sigmoid": 2, "tanh": 3}
+# The auxiliary tensor's elementwise op and its side of the activation.
+AUX_OP = {"add": 0, "sub": 1, "mul": 2, "div": 3}
+AUX_POS = {"before": 0, "after": 1}
 
 
 def _operands(p):
@@ -116,7 +125,20 @@ def _operands(p):
     bias = raw(p.bias) if getattr(p, "bias", None) is not None else None
     xa = raw(p.mx_a) if getattr(p, "mx_a", None) is not None else None
     xb = raw(p.mx_b) if getattr(p, "mx_b", None) is not None else None
-    return A, B, C, bias, xa, xb
+    aux = raw(p.aux) if getattr(p, "aux", None) is not None else None
+    return A, B, C, bias, xa, xb, aux
+
+
+def _aux_args(p, aux):
+    op = AUX_OP[getattr(p, "aux_op", "add")]
+    pos = AUX_POS[getattr(p, "aux_pos", "before")]
+    return _ptr(aux), op, pos
+
+
+def _outputs(shape):
+    return (np.empty(shape, dtype=np.float64), np.empty(shape, dtype=np.float64),
+            np.empty(shape, dtype=np.uint32), np.empty(shape, dtype=np.float64),
+            np.empty(shape, dtype=np.float64), np.empty(shape, dtype=np.uint32))
 
 
 def _act_code(relu: bool, act: Optional[str]) -> int:
@@ -137,51 +159,51 @@ def gemm(p, relu: bool = False, rows: Optional[Sequence[int]] = None,
          act: Optional[str] = None) -> Result:
     """Full rows of D for the problem ``p`` (a ``synthetic.Problem``; its
     ``bias``, if any, is added to every row before the activation; its
-    ``mx_a`` / ``mx_b``, if set, are the E8M0 block scales of an MX problem).
+    ``mx_a`` / ``mx_b``, if set, are the E8M0 block scales of an MX problem;
+    its ``aux``, if set, is the M x N auxiliary tensor combined by
+    ``aux_op`` on the ``aux_pos`` side of the activation, and the result
+    also carries the auxiliary store Z).
 
     ``rows`` = None computes all M rows; outputs are [n_rows, N] arrays.
     ``act`` names the activation ("identity", "relu", "sigmoid", "tanh");
     ``relu=True`` is shorthand for act="relu".
     """
-    A, B, C, bias, xa, xb = _operands(p)
+    A, B, C, bias, xa, xb, aux = _operands(p)
     al, be, sa, sb = _scalars(p)
     if rows is None:
         rows_arr, n = None, p.M
     else:
         rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
         n = rows_arr.size
-    ref = np.empty((n, p.N), dtype=np.float64)
-    S = np.empty((n, p.N), dtype=np.float64)
-    d = np.empty((n, p.N), dtype=np.uint32)
+    outs = _outputs((n, p.N))
     rp = None if rows_arr is None else rows_arr.ctypes.data_as(
         ctypes.POINTER(ctypes.c_int64))
     rc = lib().oracle_gemm_rows(*_head(p, relu, act), _ptr(A), _ptr(B), _ptr(C),
-                                _ptr(bias), _ptr(xa), _ptr(xb), al, be, sa, sb, rp, n,
-                                _ptr(ref), _ptr(S), _ptr(d))
+                                _ptr(bias), _ptr(xa), _ptr(xb), *_aux_args(p, aux),
+                                al, be, sa, sb, rp, n, *(_ptr(o) for o in outs))
     if rc != 0:
         raise ValueError("oracle_gemm_rows: bad arguments")
-    return Result(ref, S, d, p.dtype_cd)
+    ref, S, d, zr, zs, zb = outs
+    return Result(ref, S, d, p.dtype_cd, zr, zs, zb)
 
 
 def gemm_entries(p, ii, jj, relu: bool = False, act: Optional[str] = None) -> Result:
     """Selected outputs D[ii[t], jj[t]], each computed on its own."""
-    A, B, C, bias, xa, xb = _operands(p)
+    A, B, C, bias, xa, xb, aux = _operands(p)
     al, be, sa, sb = _scalars(p)
     ii = np.ascontiguousarray(np.asarray(ii, dtype=np.int64))
     jj = np.ascontiguousarray(np.asarray(jj, dtype=np.int64))
     n = ii.size
-    ref = np.empty(n, dtype=np.float64)
-    S = np.empty(n, dtype=np.float64)
-    d = np.empty(n, dtype=np.uint32)
+    outs = _outputs(n)
     P = ctypes.POINTER(ctypes.c_int64)
     rc = lib().oracle_gemm_entries(*_head(p, relu, act), _ptr(A), _ptr(B), _ptr(C),
-                                   _ptr(bias), _ptr(xa), _ptr(xb), al, be, sa, sb,
-                                   ii.ctypes.data_as(P),
-                                   jj.ctypes.data_as(P), n, _ptr(ref), _ptr(S),
-                                   _ptr(d))
+                                   _ptr(bias), _ptr(xa), _ptr(xb), *_aux_args(p, aux),
+                                   al, be, sa, sb, ii.ctypes.data_as(P),
+                                   jj.ctypes.data_as(P), n, *(_ptr(o) for o in outs))
     if rc != 0:
         raise ValueError("oracle_gemm_entries: bad arguments")
-    return Result(ref, S, d, p.dtype_cd)
+    ref, S, d, zr, zs, zb = outs
+    return Result(ref, S, d, p.dtype_cd, zr, zs, zb)
 
 
 def grouped(problems: List, relu: bool = False, act: Optional[str] = None) -> List[Result]:

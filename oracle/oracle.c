@@ -24,6 +24,10 @@
  *     Output = Activation(Input * Weight + Bias), Bias a length-N vector
  *     added to every row.
  *   - "Generating State-of-the-Art GEMMs with TorchInductor's CuteDSL
+ *     backend", section 7 (epilogue fusion): the fusion kernels load and
+ *     store auxiliary tensors and apply elementwise add, multiply, subtract
+ *     and divide besides the activations.
+ *   - "Generating State-of-the-Art GEMMs with TorchInductor's CuteDSL
  *     backend", sections 5.1 (feature list: the scaled mm family for MXFP8,
  *     with its own scale type, block size and layout) and 5.2 (MXFP8
  *     results). The pages name the format only; its definition is taken from
@@ -39,12 +43,22 @@
  *   acc     = acc * s_A * s_B                             (scales; 1 unless fp8)
  *   v       = alpha * acc + (beta != 0 ? beta * c(i,j) : 0) + bias(j)
  *             (bias(j) = 0 without a bias vector)
- *   v       = act(v): identity; ReLU: v > 0 ? v : +0; Sigmoid: 1/(1+e^-v);
+ *   act     : identity; ReLU: v > 0 ? v : +0; Sigmoid: 1/(1+e^-v);
  *             Tanh: tanh(v)  (all in fp64)
- *   ref     = v                                           (fp64, unrounded)
- *   d_exact = v rounded once, to nearest even, to element_D
+ *   without an auxiliary tensor: D = act(v)
+ *   with an auxiliary M x N tensor X (element_C, layout_C) and an
+ *   elementwise op in {add, sub, mul, div} (y op x = y + x, y - x, y * x,
+ *   y / x):
+ *             before the activation: z = v op X(i,j),  D = act(z)
+ *             after the activation:  z = v,            D = act(v) op X(i,j)
+ *             and the auxiliary store Z(i,j) = z (the activation's input),
+ *             rounded once to element_D; without X, z = v
+ *   ref     = D                                           (fp64, unrounded)
+ *   d_exact = D rounded once, to nearest even, to element_D
  *   S       = |alpha * s_A * s_B| * sum_k |a(i,k) * b(k,j)|  (tolerance scale;
- *             MX: the scaled products)
+ *             MX: the scaled products); a mul multiplies it by |X(i,j)|, a
+ *             div divides it by |X(i,j)| -- for D, and for Z when the op
+ *             comes before the activation
  * Operands are decoded exactly from their storage bits by this file's own
  * decoders; products of fp32/fp16/bf16/e4m3 values are exact in fp64.
  * Layouts: RowMajor X[r][c] = base[r*cols + c]; ColumnMajor X[r][c] =
@@ -60,6 +74,8 @@
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F8E4M3 = 3, DT_E8M0 = 4 };
 enum { LAYOUT_ROW = 0, LAYOUT_COL = 1 };
 enum { ACT_IDENTITY = 0, ACT_RELU = 1, ACT_SIGMOID = 2, ACT_TANH = 3 };
+enum { AUX_ADD = 0, AUX_SUB = 1, AUX_MUL = 2, AUX_DIV = 3 };
+enum { AUX_BEFORE_ACT = 0, AUX_AFTER_ACT = 1 };
 
 /* ---- exact decoders, one per storage format (sign, exponent, fraction) ---- */
 
@@ -183,19 +199,64 @@ static int mx_ok(const uint8_t *xa, const uint8_t *xb, int dtA, int dtB, int64_t
     return xa && xb && dtA == DT_F8E4M3 && dtB == DT_F8E4M3 && K % MX_BLOCK == 0;
 }
 
-/* Epilogue of one output: scales, linear combination, bias, activation. */
-static double finish(double acc, double sab, double alpha, double beta,
-                     double c, double bias, int act) {
-    double v = alpha * (acc * sab);
-    if (beta != 0.0) v += beta * c;
-    v += bias;
+/* The activation of the epilogue, in fp64. */
+static double activate(double v, int act) {
     switch (act) {
-    case ACT_RELU: v = (v > 0.0) ? v : 0.0; break;
-    case ACT_SIGMOID: v = 1.0 / (1.0 + exp(-v)); break;
-    case ACT_TANH: v = tanh(v); break;
-    default: break;
+    case ACT_RELU: return (v > 0.0) ? v : 0.0;
+    case ACT_SIGMOID: return 1.0 / (1.0 + exp(-v));
+    case ACT_TANH: return tanh(v);
+    default: return v;
     }
-    return v;
+}
+
+/* y op x for the auxiliary elementwise op. */
+static double aux_apply(double y, double x, int op) {
+    switch (op) {
+    case AUX_SUB: return y - x;
+    case AUX_MUL: return y * x;
+    case AUX_DIV: return y / x;
+    default: return y + x;
+    }
+}
+
+/* How the op scales an error already in y (the tolerance scale). */
+static double aux_scale(double s, double x, int op) {
+    if (op == AUX_MUL) return s * fabs(x);
+    if (op == AUX_DIV) return s / fabs(x);
+    return s;
+}
+
+/* Everything an output's epilogue needs besides its own accumulator. */
+typedef struct {
+    double sab, alpha, beta;
+    int act;
+    const void *aux;      /* X, or NULL */
+    int aux_op, aux_pos;
+} epi_t;
+
+/* Epilogue of one output: scales, linear combination, bias, then the
+ * auxiliary op on its side of the activation. Returns D's value; *z gets the
+ * activation's input; *sd and *sz the tolerance scales of D and Z, starting
+ * from the accumulator's s_acc. */
+static double finish(const epi_t *e, double acc, double s_acc, double c,
+                     double bias, double x, double *z, double *sd, double *sz) {
+    double v = e->alpha * (acc * e->sab);
+    if (e->beta != 0.0) v += e->beta * c;
+    v += bias;
+    double s = s_acc;
+    if (e->aux && e->aux_pos == AUX_BEFORE_ACT) {
+        v = aux_apply(v, x, e->aux_op);
+        s = aux_scale(s, x, e->aux_op);
+    }
+    *z = v;
+    *sz = s;
+    double d = activate(v, e->act);
+    if (e->aux && e->aux_pos == AUX_AFTER_ACT) {
+        d = aux_apply(d, x, e->aux_op);
+        s = aux_scale(s, x, e->aux_op);
+    }
+    *sd = s;
+    return d;
 }
 
 /* bias(j): element j of the length-N vector in element type dtype, or 0. */
@@ -203,26 +264,55 @@ static double bias_at(const void *bias, int dtype, int64_t j) {
     return bias ? oracle_decode(dtype, load_bits(bias, dtype, j)) : 0.0;
 }
 
+/* Outputs of one (i, j): D's fp64 value, scale and bits; Z's likewise. */
+typedef struct {
+    double *ref, *S, *z_ref, *z_S;
+    uint32_t *d_bits, *z_bits;
+} out_t;
+
+static void put(const out_t *o, int dtD, int64_t t, double d, double sd,
+                double z, double sz) {
+    o->ref[t] = d;
+    if (o->S) o->S[t] = sd;
+    if (o->d_bits) o->d_bits[t] = oracle_encode(dtD, d);
+    if (o->z_ref) o->z_ref[t] = z;
+    if (o->z_S) o->z_S[t] = sz;
+    if (o->z_bits) o->z_bits[t] = oracle_encode(dtD, z);
+}
+
+static int args_ok(int dtA, int dtB, int dtC, int dtD, int act, int64_t M,
+                   int64_t N, int64_t K, const uint8_t *xa, const uint8_t *xb,
+                   int aux_op, int aux_pos) {
+    return valid_dtype(dtA) && valid_dtype(dtB) && valid_dtype(dtC) &&
+           valid_dtype(dtD) && M >= 0 && N >= 0 && K >= 0 &&
+           act >= ACT_IDENTITY && act <= ACT_TANH && mx_ok(xa, xb, dtA, dtB, K) &&
+           aux_op >= AUX_ADD && aux_op <= AUX_DIV &&
+           (aux_pos == AUX_BEFORE_ACT || aux_pos == AUX_AFTER_ACT);
+}
+
 /*
  * Rows mode: computes every column j of each row i listed in `rows`
  * (rows == NULL selects all M rows in order). Outputs are dense row-major
  * [n_rows][N]: ref (fp64), S (fp64, optional), d_bits (element_D bits,
- * optional). Returns 0 on success, -1 on bad arguments.
+ * optional), and for the auxiliary store z_ref, z_S, z_bits (optional).
+ * aux (M x N, element_C, layout_C) may be NULL. Returns 0 on success, -1 on
+ * bad arguments.
  */
 int oracle_gemm_rows(int dtA, int dtB, int dtC, int dtD, int la, int lb,
                      int lc, int act, int64_t M, int64_t N, int64_t K,
                      const void *A, const void *B, const void *C,
                      const void *bias, const uint8_t *xa, const uint8_t *xb,
+                     const void *aux, int aux_op, int aux_pos,
                      float alpha, float beta, float scale_a, float scale_b,
                      const int64_t *rows, int64_t n_rows, double *ref,
-                     double *S, uint32_t *d_bits) {
-    if (!valid_dtype(dtA) || !valid_dtype(dtB) || !valid_dtype(dtC) ||
-        !valid_dtype(dtD) || M < 0 || N < 0 || K < 0 || !ref ||
-        act < ACT_IDENTITY || act > ACT_TANH || !mx_ok(xa, xb, dtA, dtB, K))
+                     double *S, uint32_t *d_bits, double *z_ref, double *z_S,
+                     uint32_t *z_bits) {
+    if (!ref || !args_ok(dtA, dtB, dtC, dtD, act, M, N, K, xa, xb, aux_op, aux_pos))
         return -1;
     if (rows == NULL) n_rows = M;
-    const double al = (double)alpha, be = (double)beta;
-    const double sab = (double)scale_a * (double)scale_b;
+    const epi_t e = {(double)scale_a * (double)scale_b, (double)alpha, (double)beta,
+                     act, aux, aux_op, aux_pos};
+    const out_t o = {ref, S, z_ref, z_S, d_bits, z_bits};
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < n_rows; ++r) {
@@ -239,11 +329,12 @@ int oracle_gemm_rows(int dtA, int dtB, int dtC, int dtD, int la, int lb,
             }
         }
         for (int64_t j = 0; j < N; ++j) {
-            double c = (be != 0.0) ? elem(C, dtC, lc, M, N, i, j) : 0.0;
-            double v = finish(acc[j], sab, al, be, c, bias_at(bias, dtC, j), act);
-            ref[r * N + j] = v;
-            if (S) S[r * N + j] = fabs(al * sab) * sab_abs[j];
-            if (d_bits) d_bits[r * N + j] = oracle_encode(dtD, v);
+            double c = (e.beta != 0.0) ? elem(C, dtC, lc, M, N, i, j) : 0.0;
+            double x = aux ? elem(aux, dtC, lc, M, N, i, j) : 0.0;
+            double z, sd, sz;
+            double d = finish(&e, acc[j], fabs(e.alpha * e.sab) * sab_abs[j], c,
+                              bias_at(bias, dtC, j), x, &z, &sd, &sz);
+            put(&o, dtD, r * N + j, d, sd, z, sz);
         }
         free(acc);
         free(sab_abs);
@@ -253,21 +344,24 @@ int oracle_gemm_rows(int dtA, int dtB, int dtC, int dtD, int la, int lb,
 
 /*
  * Entries mode: computes the n listed outputs (ii[t], jj[t]) one by one.
- * Outputs ref[t], S[t] (optional), d_bits[t] (optional).
+ * Outputs ref[t], S[t], d_bits[t], z_ref[t], z_S[t], z_bits[t] (all but ref
+ * optional).
  */
 int oracle_gemm_entries(int dtA, int dtB, int dtC, int dtD, int la, int lb,
                         int lc, int act, int64_t M, int64_t N, int64_t K,
                         const void *A, const void *B, const void *C,
                         const void *bias, const uint8_t *xa, const uint8_t *xb,
+                        const void *aux, int aux_op, int aux_pos,
                         float alpha, float beta, float scale_a, float scale_b,
                         const int64_t *ii, const int64_t *jj, int64_t n,
-                        double *ref, double *S, uint32_t *d_bits) {
-    if (!valid_dtype(dtA) || !valid_dtype(dtB) || !valid_dtype(dtC) ||
-        !valid_dtype(dtD) || M < 0 || N < 0 || K < 0 || !ref || !ii || !jj ||
-        act < ACT_IDENTITY || act > ACT_TANH || !mx_ok(xa, xb, dtA, dtB, K))
+                        double *ref, double *S, uint32_t *d_bits, double *z_ref,
+                        double *z_S, uint32_t *z_bits) {
+    if (!ref || !ii || !jj ||
+        !args_ok(dtA, dtB, dtC, dtD, act, M, N, K, xa, xb, aux_op, aux_pos))
         return -1;
-    const double al = (double)alpha, be = (double)beta;
-    const double sab = (double)scale_a * (double)scale_b;
+    const epi_t e = {(double)scale_a * (double)scale_b, (double)alpha, (double)beta,
+                     act, aux, aux_op, aux_pos};
+    const out_t o = {ref, S, z_ref, z_S, d_bits, z_bits};
     int bad = 0;
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < n; ++t) {
@@ -280,11 +374,12 @@ int oracle_gemm_entries(int dtA, int dtB, int dtC, int dtD, int la, int lb,
             acc += p;
             sabs += fabs(p);
         }
-        double c = (be != 0.0) ? elem(C, dtC, lc, M, N, i, j) : 0.0;
-        double v = finish(acc, sab, al, be, c, bias_at(bias, dtC, j), act);
-        ref[t] = v;
-        if (S) S[t] = fabs(al * sab) * sabs;
-        if (d_bits) d_bits[t] = oracle_encode(dtD, v);
+        double c = (e.beta != 0.0) ? elem(C, dtC, lc, M, N, i, j) : 0.0;
+        double x = aux ? elem(aux, dtC, lc, M, N, i, j) : 0.0;
+        double z, sd, sz;
+        double d = finish(&e, acc, fabs(e.alpha * e.sab) * sabs, c,
+                          bias_at(bias, dtC, j), x, &z, &sd, &sz);
+        put(&o, dtD, t, d, sd, z, sz);
     }
     return bad ? -1 : 0;
 }

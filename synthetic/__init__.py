@@ -87,6 +87,12 @@ class Problem:
     # mx_b [N, K/32] for the columns of B; None for a non-MX problem
     mx_a: Optional[torch.Tensor] = None
     mx_b: Optional[torch.Tensor] = None
+    # auxiliary M x N tensor of the epilogue (dtype_cd, layout lc), its
+    # elementwise op ("add", "sub", "mul", "div") and side of the activation
+    # ("before", "after"); None: no auxiliary tensor
+    aux: Optional[torch.Tensor] = None
+    aux_op: str = "add"
+    aux_pos: str = "before"
 
     @property
     def flops(self) -> int:
@@ -309,3 +315,30 @@ def mx_integer_problem(M: int, N: int, K: int, *, la: str = ROW, lb: str = COL,
     B = cast(to_storage(b32, lb), F8)
     return Problem(M, N, K, A, B, c, 1.0, beta if with_c else 0.0, None, None, F8, BF16,
                    la, lb, lc, bias, xa, xb)
+
+
+# ---------------------------------------------------------------------------
+# auxiliary tensor of the epilogue
+
+
+def add_aux(p: Problem, op: str = "add", pos: str = "before", dist: str = "normal",
+            seed: int = 0, lo: int = -3, hi: int = 3) -> Problem:
+    """Attach an M x N auxiliary tensor (dtype_cd, layout p.lc) drawn from its
+    own generator ``seed``, so the problem's other draws do not change.
+    dist: "normal" N(0,1); "away" sign * U[0.5, 2) (bounded away from zero,
+    for division); "int" integers in [lo, hi]; "int_nz" the same without 0;
+    "ones"."""
+    rng = np.random.default_rng(seed)
+    shape = (p.M, p.N)
+    if dist == "away":
+        x = (rng.random(shape, dtype=np.float32) * np.float32(1.5) + np.float32(0.5))
+        x = np.where(rng.random(shape) < 0.5, -x, x).astype(np.float32)
+    elif dist in ("int", "int_nz"):
+        x = rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+        if dist == "int_nz":
+            x = np.where(x == 0, np.float32(hi), x).astype(np.float32)
+    else:
+        x = _draw(rng, shape, dist)
+    p.aux = cast(to_storage(x, p.lc), p.dtype_cd)
+    p.aux_op, p.aux_pos = op, pos
+    return p

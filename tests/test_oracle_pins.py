@@ -200,7 +200,7 @@ def _with_operand(p, which, logical, dtype):
 def _logical(p, which):
     """Logical fp64 values of an operand, via torch's decoder (independent)."""
     t = getattr(p, which).to(torch.float64).numpy()
-    layout = {"A": p.la, "B": p.lb, "C": p.lc}[which]
+    layout = {"A": p.la, "B": p.lb, "C": p.lc, "aux": p.lc}[which]
     return t if layout == "row" else t.T
 
 
@@ -602,3 +602,174 @@ def test_mx_quantizer_round_trips_within_e4m3_precision():
     assert sat.any() and (np.abs(deq[sat]) == 448.0 * X[sat]).all()
     ok = np.abs(deq - x) <= 2.0 ** -4 * np.abs(x) + 2.0 ** -10 * X
     assert ok[~sat].all()
+
+
+# ---------------------------------------------------------------- auxiliary tensor
+# The epilogue-fusion kernels load and store auxiliary tensors and combine
+# them by elementwise add, subtract, multiply or divide ("Generating
+# State-of-the-Art GEMMs with TorchInductor's CuteDSL backend", section 7).
+
+AUX_OPS = ("add", "sub", "mul", "div")
+
+
+def _fraction_aux(p, act):
+    """Exact D and Z of an aux problem: the rational GEMM + bias, the op on
+    its side of the activation (relu or identity)."""
+    exact = _fraction_gemm(p, False)
+    bias = p.bias.to(torch.float64).numpy() if p.bias is not None else None
+    X = _logical(p, "aux")
+    ops = {"add": lambda y, x: y + x, "sub": lambda y, x: y - x,
+           "mul": lambda y, x: y * x, "div": lambda y, x: y / x}
+    op = ops[p.aux_op]
+    relu = (lambda v: v if v > 0 else Fraction(0)) if act == "relu" else (lambda v: v)
+    D, Z = [], []
+    for i in range(p.M):
+        drow, zrow = [], []
+        for j in range(p.N):
+            v = exact[i][j] + (Fraction(float(bias[j])) if bias is not None else 0)
+            x = Fraction(float(X[i, j]))
+            if p.aux_pos == "before":
+                z = op(v, x)
+                d = relu(z)
+            else:
+                z = v
+                d = op(relu(v), x)
+            drow.append(d)
+            zrow.append(z)
+        D.append(drow)
+        Z.append(zrow)
+    return D, Z
+
+
+@pytest.mark.parametrize("dtype_ab,dtype_cd", [("f32", "f32"), ("f16", "f16"),
+                                               ("bf16", "bf16"), ("f8e4m3", "bf16")])
+@pytest.mark.parametrize("op", AUX_OPS)
+@pytest.mark.parametrize("pos", ["before", "after"])
+def test_aux_brute_force_fraction_tiny(dtype_ab, dtype_cd, op, pos):
+    """Exact rational brute force: every op on both sides of ReLU / identity,
+    random layouts, with and without bias and beta*C, one K = 0 case. A
+    division is one correctly rounded fp64 quotient of exact values, which is
+    what float(Fraction) gives."""
+    rng = np.random.default_rng(31)
+    for trial in range(5):
+        M, N = (int(v) for v in rng.integers(1, 7, 2))
+        K = 0 if trial == 4 else int(rng.integers(1, 7))
+        la, lb, lc = (LAYOUTS[int(v)] for v in rng.integers(0, 2, 3))
+        p = syn.integer_problem(M, N, K, dtype_ab=dtype_ab, dtype_cd=dtype_cd,
+                                la=la, lb=lb, lc=lc, lo=-5, hi=5,
+                                alpha=float(rng.choice([1.0, -0.5])),
+                                beta=float(rng.choice([0.0, 1.0])),
+                                with_bias=bool(trial % 2), seed=300 + trial)
+        syn.add_aux(p, op, pos, dist="int_nz" if op == "div" else "int", seed=400 + trial)
+        for act in ("identity", "relu"):
+            r = oracle.gemm(p, act=act)
+            D, Z = _fraction_aux(p, act)
+            for i in range(M):
+                for j in range(N):
+                    assert float(r.ref[i, j]) == float(D[i][j]), (trial, act, i, j)
+                    assert float(r.z_ref[i, j]) == float(Z[i][j]), (trial, act, i, j)
+            # by value: a product or quotient of 0 keeps the sign IEEE gives it,
+            # and +0 and -0 are the same result
+            for got, want in ((r.d_bits, D), (r.z_bits, Z)):
+                want_bits = oracle.encode(dtype_cd, [[float(v) for v in row] for row in want])
+                assert np.array_equal(oracle.decode(dtype_cd, got),
+                                      oracle.decode(dtype_cd, want_bits))
+
+
+@pytest.mark.parametrize("lc", LAYOUTS)
+def test_aux_add_and_sub_equal_beta_c(lc):
+    """X + v with beta = 0 is beta = 1 with C = X; v - X is beta = -1."""
+    p = syn.make_problem(9, 13, 20, dtype_ab="f16", dtype_cd="f32", lc=lc,
+                         dist_c="normal", beta=1.0, seed=32)
+    with_c = oracle.gemm(p).ref
+    p.beta = -1.0
+    minus_c = oracle.gemm(p).ref
+    p.aux, p.beta = p.C, 0.0
+    p.aux_op, p.aux_pos = "add", "before"
+    assert np.array_equal(oracle.gemm(p).ref, with_c)
+    p.aux_op = "sub"
+    assert np.array_equal(oracle.gemm(p).ref, minus_c)
+
+
+def test_aux_mul_by_two_and_div_by_half_double_exactly():
+    p = syn.make_problem(7, 11, 40, dtype_ab="bf16", dtype_cd="bf16", dist_c="normal",
+                         beta=0.5, dist_bias="normal", seed=33)
+    base = oracle.gemm(p, act="tanh")
+    for op, val in (("mul", 2.0), ("div", 0.5)):
+        for pos in ("before", "after"):
+            syn.add_aux(p, op, pos, dist="ones")
+            p.aux = p.aux * val
+            r = oracle.gemm(p, act="identity" if pos == "before" else "tanh")
+            want = oracle.gemm(p.__class__(**{**p.__dict__, "aux": None}),
+                               act="identity" if pos == "before" else "tanh").ref * 2.0
+            assert np.array_equal(r.ref, want)
+    p.aux = None
+    assert np.array_equal(oracle.gemm(p, act="tanh").ref, base.ref)
+
+
+def test_aux_store_is_the_activation_input():
+    """Before the activation Z = v op X and D = act(Z); after it, Z is the
+    plain linear result and D = act(Z) op X."""
+    p = syn.make_problem(6, 10, 24, dtype_ab="f16", dtype_cd="f16", dist_c="normal",
+                         beta=1.0, seed=34)
+    plain = oracle.gemm(p).ref
+    syn.add_aux(p, "mul", "before", dist="away", seed=35)
+    r = oracle.gemm(p, act="sigmoid")
+    assert np.allclose(r.ref, 1.0 / (1.0 + np.exp(-r.z_ref)), rtol=1e-15, atol=0)
+    assert np.array_equal(r.z_ref, oracle.gemm(p, act="identity").ref)
+    p.aux_pos = "after"
+    r = oracle.gemm(p, act="relu")
+    assert np.array_equal(r.z_ref, plain)
+    X = _logical(p, "aux")
+    assert np.array_equal(r.ref, np.maximum(plain, 0.0) * X)
+
+
+def test_aux_position_decides_with_negative_factors():
+    """relu(v * X) and relu(v) * X differ where X < 0: the two readings are
+    told apart (a planted swap of the side fails)."""
+    p = syn.integer_problem(6, 6, 5, dtype_ab="f16", dtype_cd="f16", lo=-3, hi=3, seed=36)
+    syn.add_aux(p, "mul", "before", dist="int_nz", seed=37)
+    before = oracle.gemm(p, act="relu").ref
+    p.aux_pos = "after"
+    after = oracle.gemm(p, act="relu").ref
+    assert (before >= 0).all() and (after < 0).any()
+    assert not np.array_equal(before, after)
+
+
+def test_aux_pin_catches_transposed_aux():
+    """A planted mistake (X read with the other layout) fails the rational pin."""
+    p = syn.integer_problem(5, 5, 4, dtype_ab="f32", dtype_cd="f32", lo=-3, hi=3, seed=38)
+    syn.add_aux(p, "sub", "before", dist="int", seed=39)
+    D, _ = _fraction_aux(p, "identity")
+    want = np.array([[float(v) for v in row] for row in D])
+    assert np.array_equal(oracle.gemm(p).ref, want)
+    p.aux = p.aux.T.contiguous()                # the planted transposition
+    assert not np.array_equal(oracle.gemm(p).ref, want)
+
+
+def test_aux_rows_equal_entries():
+    p = syn.make_problem(12, 40, 33, dtype_ab="f16", dtype_cd="f16", lc="col",
+                         dist_c="normal", beta=0.5, dist_bias="normal", seed=40)
+    syn.add_aux(p, "div", "after", dist="away", seed=41)
+    rows = oracle.gemm(p, act="tanh")
+    rng = np.random.default_rng(42)
+    ii, jj = rng.integers(0, 12, 60), rng.integers(0, 40, 60)
+    ent = oracle.gemm_entries(p, ii, jj, act="tanh")
+    for name in ("ref", "S", "d_bits", "z_ref", "z_S", "z_bits"):
+        assert np.array_equal(getattr(ent, name), getattr(rows, name)[ii, jj]), name
+
+
+def test_aux_tolerance_scale_follows_the_op():
+    """The error of v (scale S) is multiplied by |X| through a mul and divided
+    by it through a div; add and sub leave it; Z keeps the plain S when the op
+    comes after the activation."""
+    p = syn.make_problem(5, 8, 16, dtype_ab="f16", dtype_cd="f16", seed=43)
+    S0 = oracle.gemm(p).S
+    for op in AUX_OPS:
+        for pos in ("before", "after"):
+            syn.add_aux(p, op, pos, dist="away", seed=44)
+            X = np.abs(_logical(p, "aux"))
+            r = oracle.gemm(p, act="relu")
+            f = {"add": 1.0, "sub": 1.0, "mul": X, "div": 1.0 / X}[op]
+            assert np.allclose(r.S, S0 * f, rtol=1e-15)
+            assert np.allclose(r.z_S, S0 * (f if pos == "before" else 1.0), rtol=1e-15)
