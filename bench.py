@@ -29,7 +29,8 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f8e4m3": 5033.2, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 METRIC = "GEMM TFLOP/s and % of MI355X MFMA peak per dtype, 1 GPU"
 
-WORKLOADS = ("layer", "down", "fp16_1024_relu", "grouped64", "fp8_decode", "fp32_small")
+WORKLOADS = ("layer", "down", "fp16_1024_relu", "grouped64", "fp8_decode", "fp32_small",
+             "mx_layer", "layer_residual")
 
 
 def source_hash() -> str:
@@ -147,7 +148,58 @@ def build_fp32():
                  describe=plan.describe(p.M, p.N, p.K))], "f32"
 
 
+def build_mx_layer():
+    """The four layer GEMMs in MXFP8 (e4m3 elements, E8M0 scales per 32 K)."""
+    import torch
+    import synthetic as syn
+    import dense_gemm_epilogue_02_amd as g
+    dev = torch.device("cuda:0")
+    plan = g.Plan("f8e4m3", la="row", lb="col", lc="row")
+    items = []
+    for i, name in enumerate(("qkv", "o", "gate_up", "down")):
+        M, N, K, A, B, xa, xb = syn.mx_layer_device(name, dev, seed=i)
+        D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        shape = type("S", (), dict(M=M, N=N, K=K))
+        items.append(dict(name=name, p=shape, flops=2 * M * N * K, plan=plan,
+                          call=(lambda A=A, B=B, D=D, xa=xa, xb=xb, M=M, N=N, K=K:
+                                plan.run_mx(A, B, None, D, M, N, K, xa, xb)),
+                          bytes=M * K + K * N + M * N * 2 + (M + N) * (K // 32),
+                          describe=plan.describe(M, N, K)))
+    torch.cuda.synchronize()
+    return items, "f8e4m3"
+
+
+def build_layer_residual():
+    """O and down projections with the residual add fused as an auxiliary
+    tensor (D = A W + X, X the M x N residual stream, bf16)."""
+    import torch
+    import synthetic as syn
+    import dense_gemm_epilogue_02_amd as g
+    dev = torch.device("cuda:0")
+    plan = g.Plan("bf16", la="row", lb="col", lc="row")
+    items = []
+    for i, name in enumerate(("o", "down")):
+        p = syn.config4(name, seed=i)
+        A, B = p.A.to(dev), p.B.to(dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(100 + i)
+        X = torch.randn((p.M, p.N), generator=gen, device=dev).to(torch.bfloat16)
+        D = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev)
+        items.append(dict(name=name + "_residual", p=p, flops=p.flops, plan=plan,
+                          call=(lambda A=A, B=B, D=D, X=X, p=p:
+                                plan.run_aux(A, B, None, D, p.M, p.N, p.K, aux=X,
+                                             aux_op="add", aux_pos="before")),
+                          bytes=p.M * p.K * 2 + p.K * p.N * 2 + 2 * p.M * p.N * 2,
+                          describe=plan.describe(p.M, p.N, p.K)))
+        del p.A, p.B
+    return items, "bf16"
+
+
 def build(workload):
+    if workload == "mx_layer":
+        return build_mx_layer()
+    if workload == "layer_residual":
+        return build_layer_residual()
     if workload == "layer":
         return build_layer(["qkv", "o", "gate_up", "down"])
     if workload == "down":
@@ -268,10 +320,14 @@ def main():
                                 "fp16_1024_relu": "fp16_1024cubed_relu",
                                 "grouped64": "grouped64_fp16_seed0",
                                 "fp8_decode": "fp8_e4m3_decode_shapes",
-                                "fp32_small": "fp32_128x64x256"}[args.workload],
+                                "fp32_small": "fp32_128x64x256",
+                                "mx_layer": "llama70b_like_layer_gemms_mxfp8_m4096",
+                                "layer_residual": "o_and_down_proj_bf16_residual_add_m4096",
+                                }[args.workload],
                    "gemms": {it["name"]: [it["p"].M, it["p"].N, it["p"].K] for it in items},
                    "layout": "A RowMajor, B ColumnMajor ([N,K]), D RowMajor"
-                   if args.workload in ("layer", "down", "fp8_decode") else "all RowMajor"},
+                   if args.workload in ("layer", "down", "fp8_decode", "mx_layer",
+                                        "layer_residual") else "all RowMajor"},
         "pct_peak": round(100 * tflops / peak, 2),
         "per_gemm": per_gemm,
         "roofline": roof,

@@ -79,6 +79,11 @@ class gemm_problem(ctypes.Structure):
                 ("D", ctypes.c_void_p)]
 
 
+class gemm_config(ctypes.Structure):
+    _fields_ = [("schedule", ctypes.c_int), ("tile", ctypes.c_int), ("sk_grid", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("us", ctypes.c_float)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -109,11 +114,25 @@ def _load():
     L.gemm_plan_run_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp, vp, vp]
     L.gemm_plan_run_mx.restype = st
     L.gemm_plan_run_mx.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp, vp, vp]
+    L.gemm_plan_run_aux.restype = st
+    L.gemm_plan_run_aux.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp,
+                                    i64, i64, i64, f32, f32, vp, vp, vp]
     L.gemm_plan_run_batched.restype = st
     L.gemm_plan_run_batched.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                         i64, i64, f32, f32, vp, vp, vp]
     L.grouped_gemm_run.restype = st
     L.grouped_gemm_run.argtypes = [vp, ctypes.POINTER(gemm_problem), i32, f32, f32, vp]
+    L.gemm_plan_profile.restype = st
+    L.gemm_plan_profile.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, i32,
+                                    ctypes.POINTER(gemm_config), i32, ctypes.POINTER(i32), vp]
+    L.gemm_plan_cache_export.restype = st
+    L.gemm_plan_cache_export.argtypes = [vp, ctypes.c_char_p, i32, ctypes.POINTER(i32)]
+    L.gemm_plan_cache_import.restype = st
+    L.gemm_plan_cache_import.argtypes = [vp, ctypes.c_char_p]
+    L.gemm_plan_cache_size.restype = i32
+    L.gemm_plan_cache_size.argtypes = [vp]
+    L.gemm_plan_cache_clear.restype = st
+    L.gemm_plan_cache_clear.argtypes = [vp]
     L.gemm_plan_describe.restype = st
     L.gemm_plan_describe.argtypes = [vp, i64, i64, i64, i32, ctypes.c_char_p, i32]
     L.gemm_last_error.restype = ctypes.c_char_p
@@ -133,7 +152,10 @@ lib = _load()
 
 EXPORTED = ("gemm_plan_create", "gemm_plan_create_simple", "gemm_plan_destroy",
             "gemm_plan_set_config", "gemm_plan_run", "gemm_plan_run_scaled",
-            "gemm_plan_run_ex", "gemm_plan_run_mx", "gemm_plan_run_batched", "grouped_gemm_run", "gemm_plan_describe", "gemm_last_error",
+            "gemm_plan_run_ex", "gemm_plan_run_mx", "gemm_plan_run_aux",
+            "gemm_plan_run_batched", "grouped_gemm_run", "gemm_plan_profile",
+            "gemm_plan_cache_export", "gemm_plan_cache_import", "gemm_plan_cache_size",
+            "gemm_plan_cache_clear", "gemm_plan_describe", "gemm_last_error",
             "gemm_status_string", "gemm_supported_count", "gemm_supported_get",
             "gemm_version")
 
@@ -210,6 +232,19 @@ def gemm_plan_run_mx(plan: int, A, B, C, D, bias, M: int, N: int, K: int, alpha:
                                 _stream(stream)))
 
 
+# gemm_aux_op / gemm_aux_pos
+AUX_OP = {"add": 0, "sub": 1, "mul": 2, "div": 3}
+AUX_POS = {"before": 0, "after": 1}
+
+
+def gemm_plan_run_aux(plan: int, A, B, C, D, bias, aux, aux_op: int, aux_pos: int, aux_out,
+                      M: int, N: int, K: int, alpha: float, beta: float, scale_a=None,
+                      scale_b=None, stream=None) -> None:
+    _check(lib.gemm_plan_run_aux(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(bias), _ptr(aux),
+                                 int(aux_op), int(aux_pos), _ptr(aux_out), M, N, K, alpha, beta,
+                                 _ptr(scale_a), _ptr(scale_b), _stream(stream)))
+
+
 def gemm_plan_run_batched(plan: int, A, B, C, D, bias, M: int, N: int, K: int, batch: int,
                           stride_a: int, stride_b: int, stride_c: int, stride_d: int,
                           alpha: float, beta: float, scale_a=None, scale_b=None,
@@ -226,6 +261,39 @@ def grouped_gemm_run(plan: int, problems: Sequence[tuple], alpha: float = 1.0,
     for i, (M, N, K, A, B, C, D) in enumerate(problems):
         arr[i] = gemm_problem(M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(D))
     _check(lib.grouped_gemm_run(plan, arr, len(problems), alpha, beta, _stream(stream)))
+
+
+def gemm_plan_profile(plan: int, A, B, C, D, M: int, N: int, K: int, alpha: float = 1.0,
+                      beta: float = 0.0, iters: int = 10, max_results: int = 32,
+                      stream=None) -> list:
+    """Time every distinct launch of the plan for M x N x K; fastest first.
+    The fastest is cached in the plan for later runs of this shape."""
+    arr = (gemm_config * max(1, max_results))()
+    n = ctypes.c_int32(0)
+    _check(lib.gemm_plan_profile(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), M, N, K, alpha, beta,
+                                 iters, arr, max_results, ctypes.byref(n), _stream(stream)))
+    return [dict(schedule=Schedule(c.schedule), tile=Tile(c.tile), sk_grid=c.sk_grid,
+                 grid=c.grid, us=c.us) for c in arr[:min(n.value, max_results)]]
+
+
+def gemm_plan_cache_export(plan: int) -> str:
+    need = ctypes.c_int32(0)
+    _check(lib.gemm_plan_cache_export(plan, None, 0, ctypes.byref(need)))
+    buf = ctypes.create_string_buffer(need.value)
+    _check(lib.gemm_plan_cache_export(plan, buf, len(buf), ctypes.byref(need)))
+    return buf.value.decode()
+
+
+def gemm_plan_cache_import(plan: int, text: str) -> None:
+    _check(lib.gemm_plan_cache_import(plan, text.encode()))
+
+
+def gemm_plan_cache_size(plan: int) -> int:
+    return lib.gemm_plan_cache_size(plan)
+
+
+def gemm_plan_cache_clear(plan: int) -> None:
+    _check(lib.gemm_plan_cache_clear(plan))
 
 
 def gemm_plan_describe(plan: int, M: int, N: int, K: int, num_cus: int = 0) -> dict:
@@ -363,6 +431,43 @@ class Plan:
                 _need(bias, N, "bias", self.dcd)
         gemm_plan_run_mx(self.handle, A, B, C, D, bias, M, N, K, alpha, beta, mx_scale_a,
                          mx_scale_b, stream)
+
+    def run_aux(self, A, B, C, D, M, N, K, aux=None, aux_op="add", aux_pos="before",
+                aux_out=None, alpha=1.0, beta=0.0, scale_a=None, scale_b=None, stream=None,
+                bias=None):
+        """Auxiliary-tensor epilogue: aux (M x N, C's type and layout) combined
+        by aux_op ("add", "sub", "mul", "div") before or after the activation;
+        aux_out (M x N, D's type and layout) receives the activation's input."""
+        self.check(A, B, C, D, M, N, K, beta)
+        if M and N:
+            if bias is not None:
+                _need(bias, N, "bias", self.dcd)
+            if aux is not None:
+                _need(aux, M * N, "aux", self.dcd)
+            if aux_out is not None:
+                _need(aux_out, M * N, "aux_out", self.dcd)
+        op = AUX_OP[aux_op] if isinstance(aux_op, str) else int(aux_op)
+        pos = AUX_POS[aux_pos] if isinstance(aux_pos, str) else int(aux_pos)
+        gemm_plan_run_aux(self.handle, A, B, C, D, bias, aux, op, pos, aux_out, M, N, K, alpha,
+                          beta, scale_a, scale_b, stream)
+
+    def profile(self, A, B, C, D, M, N, K, alpha=1.0, beta=0.0, iters=10, stream=None):
+        """Time every distinct launch for this shape (fastest first) and cache the best."""
+        self.check(A, B, C, D, M, N, K, beta)
+        return gemm_plan_profile(self.handle, A, B, C, D, M, N, K, alpha, beta, iters,
+                                 stream=stream)
+
+    def cache_export(self) -> str:
+        return gemm_plan_cache_export(self.handle)
+
+    def cache_import(self, text: str) -> None:
+        gemm_plan_cache_import(self.handle, text)
+
+    def cache_size(self) -> int:
+        return gemm_plan_cache_size(self.handle)
+
+    def cache_clear(self) -> None:
+        gemm_plan_cache_clear(self.handle)
 
     def run_batched(self, A, B, C, D, M, N, K, batch, strides, alpha=1.0, beta=0.0,
                     scale_a=None, scale_b=None, stream=None, bias=None):

@@ -49,13 +49,20 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(jobs: int = 0, extra=(), verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link the shared library."""
+def build(jobs: int = 0, extra=(), verbose: bool = False, only=None) -> str:
+    """Compile every HIP source for gfx950 and link the shared library.
+    ``only`` (a list of source names) recompiles just those and links the
+    others' existing objects."""
     os.makedirs(BUILD_DIR, exist_ok=True)
+    todo = list(SOURCES) if only is None else [s for s in SOURCES if s in only]
+    objs = {s: os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES
+            if s not in todo}
+    for s, o in objs.items():
+        if not os.path.exists(o):
+            raise RuntimeError(f"no object for {s}: build it first")
     jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = {ex.submit(_compile, s, extra): s for s in SOURCES}
-        objs = {}
+        futs = {ex.submit(_compile, s, extra): s for s in todo}
         for f in cf.as_completed(futs):
             objs[futs[f]] = f.result()
             if verbose:
@@ -71,4 +78,6 @@ def build(jobs: int = 0, extra=(), verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True, extra=sys.argv[1:]))
+    args = sys.argv[1:]
+    only = [a for a in args if a in SOURCES] or None
+    print(build(verbose=True, extra=[a for a in args if a not in SOURCES], only=only))

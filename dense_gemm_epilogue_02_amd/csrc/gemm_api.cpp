@@ -16,6 +16,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
 #include <unordered_map>
@@ -140,6 +141,200 @@ int static_occupancy(const KernelEntry *e) {
     return occ > 0 ? occ : 1;
 }
 
+// ---- configuration cache: JSON text ----------------------------------------
+//
+// Written by gemm_plan_cache_export, read by gemm_plan_cache_import:
+//   {"format": "mi355-gemm-config-cache", "version": 1, "arch": "gfx950",
+//    "plan": {"a": "BF16", "b": "BF16", "c": "BF16", "d": "BF16", "acc": "F32",
+//             "layout_a": "row", "layout_b": "col", "layout_c": "row"},
+//    "entries": [{"m": 4096, "n": 8192, "k": 8192, "mx": 0,
+//                 "schedule": "data_parallel", "tile": "256x256", "sk_grid": 0,
+//                 "us": 477.8}, ...]}
+
+const char *kCacheFormat = "mi355-gemm-config-cache";
+
+const char *layout_str(gemm_layout l) { return l == GEMM_ROW_MAJOR ? "row" : "col"; }
+
+const char *tile_enum_name(gemm_tile t) {
+    switch (t) {
+    case GEMM_TILE_256x256: return "256x256";
+    case GEMM_TILE_128x128: return "128x128";
+    case GEMM_TILE_64x256: return "64x256";
+    case GEMM_TILE_32x256: return "32x256";
+    case GEMM_TILE_GENERIC: return "generic";
+    default: return "auto";
+    }
+}
+
+bool parse_tile(const std::string &s, gemm_tile *t) {
+    for (int v = GEMM_TILE_AUTO; v <= GEMM_TILE_GENERIC; ++v)
+        if (s == tile_enum_name((gemm_tile)v)) { *t = (gemm_tile)v; return true; }
+    return false;
+}
+
+const char *sched_name(gemm_schedule s);
+
+bool parse_sched(const std::string &s, gemm_schedule *out) {
+    for (int v = GEMM_SCHED_AUTO; v <= GEMM_SCHED_SPLIT_K; ++v)
+        if (s == sched_name((gemm_schedule)v)) { *out = (gemm_schedule)v; return true; }
+    return false;
+}
+
+// A JSON value (only what the cache format needs: objects, arrays, strings,
+// numbers, true/false/null).
+struct JVal {
+    enum Kind { NUL, BOOL, NUM, STR, ARR, OBJ } kind = NUL;
+    double num = 0.0;
+    bool b = false;
+    std::string str;
+    std::vector<JVal> arr;
+    std::vector<std::pair<std::string, JVal>> obj;
+    const JVal *get(const char *key) const {
+        for (const auto &kv : obj)
+            if (kv.first == key) return &kv.second;
+        return nullptr;
+    }
+};
+
+struct JParser {
+    const char *s;
+    size_t i = 0, n;
+    const char *err = nullptr;
+    int depth = 0;
+    explicit JParser(const char *t) : s(t), n(strlen(t)) {}
+    void ws() {
+        while (i < n && (s[i] == ' ' || s[i] == '\t' || s[i] == '\n' || s[i] == '\r')) ++i;
+    }
+    bool fail_at(const char *m) {
+        if (!err) err = m;
+        return false;
+    }
+    bool lit(const char *w) {
+        const size_t L = strlen(w);
+        if (n - i < L || strncmp(s + i, w, L) != 0) return fail_at("unexpected token");
+        i += L;
+        return true;
+    }
+    bool string(std::string *out) {
+        if (i >= n || s[i] != '"') return fail_at("expected a string");
+        ++i;
+        out->clear();
+        while (i < n && s[i] != '"') {
+            char c = s[i++];
+            if (c == '\\') {
+                if (i >= n) return fail_at("unterminated escape");
+                const char e = s[i++];
+                switch (e) {
+                case '"': c = '"'; break;
+                case '\\': c = '\\'; break;
+                case '/': c = '/'; break;
+                case 'n': c = '\n'; break;
+                case 't': c = '\t'; break;
+                case 'r': c = '\r'; break;
+                case 'b': c = '\b'; break;
+                case 'f': c = '\f'; break;
+                default: return fail_at("unsupported string escape");
+                }
+            } else if ((unsigned char)c < 0x20) {
+                return fail_at("control character in a string");
+            }
+            out->push_back(c);
+        }
+        if (i >= n) return fail_at("unterminated string");
+        ++i;
+        return true;
+    }
+    bool value(JVal *v) {
+        if (++depth > 16) return fail_at("nesting too deep");
+        ws();
+        bool ok_ = false;
+        if (i >= n) {
+            ok_ = fail_at("unexpected end of text");
+        } else if (s[i] == '{') {
+            v->kind = JVal::OBJ;
+            ++i;
+            ws();
+            if (i < n && s[i] == '}') {
+                ++i;
+                ok_ = true;
+            } else {
+                for (;;) {
+                    ws();
+                    std::string key;
+                    if (!string(&key)) break;
+                    ws();
+                    if (i >= n || s[i] != ':') { fail_at("expected ':'"); break; }
+                    ++i;
+                    JVal child;
+                    if (!value(&child)) break;
+                    v->obj.emplace_back(std::move(key), std::move(child));
+                    ws();
+                    if (i < n && s[i] == ',') { ++i; continue; }
+                    if (i < n && s[i] == '}') { ++i; ok_ = true; }
+                    else fail_at("expected ',' or '}'");
+                    break;
+                }
+            }
+        } else if (s[i] == '[') {
+            v->kind = JVal::ARR;
+            ++i;
+            ws();
+            if (i < n && s[i] == ']') {
+                ++i;
+                ok_ = true;
+            } else {
+                for (;;) {
+                    JVal child;
+                    if (!value(&child)) break;
+                    v->arr.push_back(std::move(child));
+                    ws();
+                    if (i < n && s[i] == ',') { ++i; continue; }
+                    if (i < n && s[i] == ']') { ++i; ok_ = true; }
+                    else fail_at("expected ',' or ']'");
+                    break;
+                }
+            }
+        } else if (s[i] == '"') {
+            v->kind = JVal::STR;
+            ok_ = string(&v->str);
+        } else if (s[i] == 't') {
+            v->kind = JVal::BOOL;
+            v->b = true;
+            ok_ = lit("true");
+        } else if (s[i] == 'f') {
+            v->kind = JVal::BOOL;
+            ok_ = lit("false");
+        } else if (s[i] == 'n') {
+            ok_ = lit("null");
+        } else {
+            char *end = nullptr;
+            v->kind = JVal::NUM;
+            v->num = strtod(s + i, &end);
+            if (end == s + i) ok_ = fail_at("unexpected character");
+            else {
+                i = (size_t)(end - s);
+                ok_ = true;
+            }
+        }
+        --depth;
+        return ok_;
+    }
+};
+
+bool json_int(const JVal *v, int64_t lo, int64_t hi, int64_t *out) {
+    if (!v || v->kind != JVal::NUM) return false;
+    if (!(v->num >= (double)lo && v->num <= (double)hi) || v->num != (double)(int64_t)v->num)
+        return false;
+    *out = (int64_t)v->num;
+    return true;
+}
+
+bool json_str(const JVal *v, std::string *out) {
+    if (!v || v->kind != JVal::STR) return false;
+    *out = v->str;
+    return true;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ plan
@@ -165,6 +360,25 @@ struct gemm_plan_s {
     bool gevent_pending;
     hipStream_t last_stream;
     bool used;
+    // Tuned configurations (from gemm_plan_profile or an imported cache),
+    // keyed by (M, N, K, MX); used when the plan has no explicit override.
+    struct TunedKey {
+        int64_t m, n, k;
+        int mx;
+        bool operator<(const TunedKey &o) const {
+            if (m != o.m) return m < o.m;
+            if (n != o.n) return n < o.n;
+            if (k != o.k) return k < o.k;
+            return mx < o.mx;
+        }
+    };
+    struct Tuned {
+        gemm_schedule sched;
+        gemm_tile tile;
+        int sk_grid;
+        float us;
+    };
+    std::map<TunedKey, Tuned> tuned;
 };
 
 namespace {
@@ -245,6 +459,24 @@ const char *sched_name(gemm_schedule s) {
 // fp32, whose 32-element k-tile already costs eight times that.
 int min_iters(int fam) { return fam == FAM_F32 ? 1 : 8; }
 
+// The schedule / tile / grid a run uses: the plan's explicit override if it
+// has one, else a tuned entry for this single (non-batched) shape, else the
+// heuristics (AUTO).
+struct Cfg {
+    gemm_schedule sched;
+    gemm_tile tile;
+    int sk_grid;
+};
+
+Cfg plan_cfg(const gemm_plan_s *pl, int64_t M, int64_t N, int64_t K, int64_t batch, bool mx) {
+    Cfg c{pl->sched, pl->tile, pl->sk_grid};
+    if (c.sched == GEMM_SCHED_AUTO && c.tile == GEMM_TILE_AUTO && c.sk_grid == 0 && batch == 1) {
+        auto it = pl->tuned.find({M, N, K, mx ? 1 : 0});
+        if (it != pl->tuned.end()) c = Cfg{it->second.sched, it->second.tile, it->second.sk_grid};
+    }
+    return c;
+}
+
 // `occ_of` gives workgroups per CU for an entry (live query or estimate).
 template <class OccFn>
 gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const void *C, const void *D,
@@ -252,6 +484,7 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
                    Decision &d, int64_t batch = 1, const void *mx_a = nullptr,
                    const void *mx_b = nullptr) {
     const int fam = mx_a ? FAM_MXF8 : pl->fam;
+    const Cfg cfg = plan_cfg(pl, M, N, K, batch, mx_a != nullptr);
     const int esz = elem_bytes(fam), osz = out_bytes(fam);
     const bool a_kc = pl->la == GEMM_ROW_MAJOR, b_kc = pl->lb == GEMM_COL_MAJOR;
     d.vec_cd = (pl->lc == GEMM_ROW_MAJOR && N % 4 == 0 &&
@@ -259,8 +492,8 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
                 (beta == 0.0f || reinterpret_cast<uintptr_t>(C) % (4 * osz) == 0) &&
                 reinterpret_cast<uintptr_t>(bias) % (4 * osz) == 0)
                    ? 1 : 0;
-    if (pl->tile != GEMM_TILE_GENERIC) {
-        gemm_tile t = pl->tile == GEMM_TILE_AUTO ? pick_tile(fam, M, N, cus) : pl->tile;
+    if (cfg.tile != GEMM_TILE_GENERIC) {
+        gemm_tile t = cfg.tile == GEMM_TILE_AUTO ? pick_tile(fam, M, N, cus) : cfg.tile;
         const KernelEntry *e = registry().find(fam, a_kc, b_kc, tile_id(t));
         if (!e) e = registry().find(fam, a_kc, b_kc, TILE_128x128);
         const char *why = nullptr;
@@ -307,8 +540,8 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
     gemm_status st = occ_of(e, &occ);
     if (st != GEMM_OK) return st;
     int G = cus * occ;
-    if (pl->sk_grid > 0 && pl->sk_grid < G) G = pl->sk_grid;
-    gemm_schedule s = pl->sched;
+    if (cfg.sk_grid > 0 && cfg.sk_grid < G) G = cfg.sk_grid;
+    gemm_schedule s = cfg.sched;
     if (d.ipt == 0) s = GEMM_SCHED_DATA_PARALLEL;
     if (s == GEMM_SCHED_AUTO) {
         if (d.total >= G) {
@@ -339,10 +572,10 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
         const int64_t kMinSkIters = min_iters(fam);
         d.sk_tiles = d.total;
         d.sk_iters = (int64_t)d.total * d.ipt;
-        int64_t g = pl->sk_grid > 0 ? d.sk_iters : d.sk_iters / kMinSkIters;
+        int64_t g = cfg.sk_grid > 0 ? d.sk_iters : d.sk_iters / kMinSkIters;
         if (g > G) g = G;
-        if (pl->sk_grid <= 0 && g > cus) g = cus;   // one stream-K workgroup per CU
-        if (g < d.total && pl->sk_grid <= 0) g = d.total < G ? d.total : G;
+        if (cfg.sk_grid <= 0 && g > cus) g = cus;   // one stream-K workgroup per CU
+        if (g < d.total && cfg.sk_grid <= 0) g = d.total < G ? d.total : G;
         d.grid = (int)(g > 0 ? g : 1);
         break;
     }
@@ -459,10 +692,14 @@ struct RunOpts {
     int64_t count = 1;
     int64_t sa = 0, sb = 0, sc = 0, sd = 0;   // element strides
     const uint8_t *mx_a = nullptr, *mx_b = nullptr;
+    // auxiliary tensors of the epilogue (single GEMMs only)
+    const void *aux = nullptr;
+    void *aux_out = nullptr;
+    int aux_op = 0, aux_after = 0;
 };
 
 EpiArgs make_epi(const gemm_plan_s *pl, float alpha, float beta, const float *sa, const float *sb,
-                 const void *bias) {
+                 const void *bias, const RunOpts &ro = RunOpts()) {
     EpiArgs e;
     e.alpha = alpha;
     e.beta = beta;
@@ -471,6 +708,10 @@ EpiArgs make_epi(const gemm_plan_s *pl, float alpha, float beta, const float *sa
     e.bias = bias;
     e.act = (int)pl->epi;
     e.lc_row = pl->lc == GEMM_ROW_MAJOR ? 1 : 0;
+    e.aux = ro.aux;
+    e.aux_out = ro.aux_out;
+    e.aux_op = ro.aux_op;
+    e.aux_after = ro.aux_after;
     return e;
 }
 
@@ -522,6 +763,10 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
                 },
                 d, bt.count, bt.mx_a, bt.mx_b);
     if (st != GEMM_OK) return st;
+    // the vector epilogue reads and writes the auxiliary tensors like C and D
+    if (reinterpret_cast<uintptr_t>(bt.aux) % (4 * osz) != 0 ||
+        reinterpret_cast<uintptr_t>(bt.aux_out) % (4 * osz) != 0)
+        d.vec_cd = 0;
     const int fam = bt.mx_a ? FAM_MXF8 : pl->fam;
     Prob p = make_prob(A, B, C, D, M, N, K, d);
     p.batch = (int)bt.count;
@@ -531,7 +776,7 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
     p.stride_d = bt.sd;
     p.mx_a = bt.mx_a;
     p.mx_b = bt.mx_b;
-    const EpiArgs ep = make_epi(pl, alpha, beta, sa, sb, bias);
+    const EpiArgs ep = make_epi(pl, alpha, beta, sa, sb, bias, bt);
     if (!d.e) {
         if (batched) {   // the scalar kernel takes one problem per launch
             for (int64_t b = 0; b < bt.count && st == GEMM_OK; ++b) {
@@ -715,6 +960,28 @@ gemm_status gemm_plan_run_mx(gemm_plan_t p, const void *A, const void *B, const 
     return run_one(p, A, B, C, D, M, N, K, alpha, beta, nullptr, nullptr, bias, stream, ro);
 }
 
+gemm_status gemm_plan_run_aux(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,
+                              const void *bias, const void *aux, gemm_aux_op aux_op,
+                              gemm_aux_pos aux_pos, void *aux_out, int64_t M, int64_t N, int64_t K,
+                              float alpha, float beta, const float *scale_a, const float *scale_b,
+                              void *stream) {
+    if (!plan_ok(p)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_run_aux: invalid plan handle");
+    if ((int)aux_op < GEMM_AUX_ADD || (int)aux_op > GEMM_AUX_DIV)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_run_aux: aux_op %d is not an elementwise op",
+                    (int)aux_op);
+    if (aux_pos != GEMM_AUX_BEFORE_ACT && aux_pos != GEMM_AUX_AFTER_ACT)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_run_aux: aux_pos %d is not a side of the "
+                    "activation", (int)aux_pos);
+    if (M > 0 && N > 0 && aux_out && aux_out == D)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_run_aux: aux_out and D are the same buffer");
+    RunOpts ro;
+    ro.aux = aux;
+    ro.aux_out = aux_out;
+    ro.aux_op = (int)aux_op;
+    ro.aux_after = aux_pos == GEMM_AUX_AFTER_ACT ? 1 : 0;
+    return run_one(p, A, B, C, D, M, N, K, alpha, beta, scale_a, scale_b, bias, stream, ro);
+}
+
 gemm_status gemm_plan_run_ex(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,
                              const void *bias, int64_t M, int64_t N, int64_t K, float alpha,
                              float beta, const float *scale_a, const float *scale_b, void *stream) {
@@ -876,6 +1143,216 @@ gemm_status gemm_plan_describe(gemm_plan_t pl, int64_t M, int64_t N, int64_t K, 
              "\"generic_reason\": \"%s\"}",
              d.e ? "tile" : "generic", tile_name(d.e), d.e ? d.e->bk : 16, d.e ? d.e->nt / 64 : 4,
              sched_name(d.sched), d.total, d.ipt, d.sk_tiles, d.split, d.grid, d.why_generic);
+    return ok();
+}
+
+gemm_status gemm_plan_profile(gemm_plan_t pl, const void *A, const void *B, const void *C, void *D,
+                              int64_t M, int64_t N, int64_t K, float alpha, float beta,
+                              int32_t iters, gemm_config *results, int32_t max_results,
+                              int32_t *n_results, void *stream) {
+    if (!plan_ok(pl)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_profile: invalid plan handle");
+    if (iters < 1 || iters > 100000)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_profile: iters = %d outside [1, 100000]", (int)iters);
+    if (max_results < 0 || (max_results > 0 && !results))
+        return fail(GEMM_INVALID_ARG, "gemm_plan_profile: results array missing");
+    gemm_status st = validate_problem(pl, A, B, C, D, M, N, K, beta, "gemm_plan_profile");
+    if (st != GEMM_OK) return st;
+    if (beta != 0.0f && C == D && M > 0 && N > 0)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_profile: D == C with beta != 0 would feed each "
+                    "timed run the previous run's output");
+    if (n_results) *n_results = 0;
+    if (M == 0 || N == 0) return ok();
+    int dev = 0, cus = 0;
+    if ((st = check_device(pl, &dev)) != GEMM_OK) return st;
+    if ((st = device_cus(dev, &cus)) != GEMM_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const Cfg saved{pl->sched, pl->tile, pl->sk_grid};
+    struct Cand {
+        gemm_config c;
+        const KernelEntry *e;
+        int sched, grid, split;
+    };
+    std::vector<Cand> done;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    hipError_t he = hipEventCreate(&ev[0]);
+    if (he == hipSuccess) he = hipEventCreate(&ev[1]);
+    if (he != hipSuccess) {
+        if (ev[0]) (void)hipEventDestroy(ev[0]);
+        return hip_fail(he, "gemm_plan_profile: hipEventCreate");
+    }
+    const gemm_tile tiles[] = {GEMM_TILE_256x256, GEMM_TILE_128x128, GEMM_TILE_64x256,
+                               GEMM_TILE_32x256, GEMM_TILE_GENERIC};
+    const gemm_schedule scheds[] = {GEMM_SCHED_DATA_PARALLEL, GEMM_SCHED_STREAM_K,
+                                    GEMM_SCHED_HYBRID, GEMM_SCHED_SPLIT_K};
+    for (gemm_tile t : tiles) {
+        for (gemm_schedule s : scheds) {
+            pl->sched = s;
+            pl->tile = t;
+            pl->sk_grid = 0;
+            // what this candidate launches; identical launches are timed once
+            Decision d;
+            st = decide(pl, A, B, beta == 0.0f ? nullptr : C, D, nullptr, M, N, K, beta, cus,
+                        [&](const KernelEntry *e, int *occ) {
+                            return kernel_occupancy(dev, e->fn_persistent, e->nt, occ);
+                        },
+                        d);
+            if (st != GEMM_OK) break;
+            bool dup = false;
+            for (const Cand &c : done)
+                dup |= c.e == d.e && c.sched == (int)d.sched && c.grid == d.grid &&
+                       c.split == d.split;
+            if (dup) continue;
+            // the resolved choice, so a cached entry reproduces this launch
+            pl->sched = d.sched;
+            pl->tile = d.e ? t : GEMM_TILE_GENERIC;
+            st = run_one(pl, A, B, C, D, M, N, K, alpha, beta, nullptr, nullptr, nullptr, stream);
+            if (st == GEMM_OK) he = hipEventRecord(ev[0], hs);
+            for (int32_t r = 0; r < iters && st == GEMM_OK && he == hipSuccess; ++r)
+                st = run_one(pl, A, B, C, D, M, N, K, alpha, beta, nullptr, nullptr, nullptr,
+                             stream);
+            if (st == GEMM_OK && he == hipSuccess) he = hipEventRecord(ev[1], hs);
+            if (st == GEMM_OK && he == hipSuccess) he = hipEventSynchronize(ev[1]);
+            float ms = 0.0f;
+            if (st == GEMM_OK && he == hipSuccess) he = hipEventElapsedTime(&ms, ev[0], ev[1]);
+            if (st != GEMM_OK || he != hipSuccess) break;
+            Cand c;
+            c.c.schedule = pl->sched;
+            c.c.tile = pl->tile;
+            c.c.sk_grid = 0;
+            c.c.grid = d.grid;
+            c.c.us = ms * 1000.0f / (float)iters;
+            c.e = d.e;
+            c.sched = (int)d.sched;
+            c.grid = d.grid;
+            c.split = d.split;
+            done.push_back(c);
+        }
+        if (st != GEMM_OK || he != hipSuccess) break;
+    }
+    pl->sched = saved.sched;
+    pl->tile = saved.tile;
+    pl->sk_grid = saved.sk_grid;
+    (void)hipEventDestroy(ev[0]);
+    (void)hipEventDestroy(ev[1]);
+    if (he != hipSuccess) return hip_fail(he, "gemm_plan_profile: timing");
+    if (st != GEMM_OK) return st;
+    std::stable_sort(done.begin(), done.end(),
+                     [](const Cand &x, const Cand &y) { return x.c.us < y.c.us; });
+    if (!done.empty()) {
+        const gemm_config &b = done.front().c;
+        pl->tuned[{M, N, K, 0}] = gemm_plan_s::Tuned{b.schedule, b.tile, b.sk_grid, b.us};
+    }
+    const int32_t n = (int32_t)std::min<size_t>(done.size(), (size_t)max_results);
+    for (int32_t i = 0; i < n; ++i) results[i] = done[i].c;
+    if (n_results) *n_results = (int32_t)done.size();
+    return ok();
+}
+
+gemm_status gemm_plan_cache_export(gemm_plan_t pl, char *buf, int32_t len, int32_t *needed) {
+    if (!plan_ok(pl)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_cache_export: invalid plan handle");
+    std::string s;
+    char tmp[512];
+    snprintf(tmp, sizeof tmp,
+             "{\"format\": \"%s\", \"version\": 1, \"arch\": \"gfx950\", \"plan\": {\"a\": \"%s\", "
+             "\"b\": \"%s\", \"c\": \"%s\", \"d\": \"%s\", \"acc\": \"%s\", \"layout_a\": \"%s\", "
+             "\"layout_b\": \"%s\", \"layout_c\": \"%s\"}, \"entries\": [",
+             kCacheFormat, dtype_name(pl->a), dtype_name(pl->b), dtype_name(pl->c),
+             dtype_name(pl->d), dtype_name(pl->acc), layout_str(pl->la), layout_str(pl->lb),
+             layout_str(pl->lc));
+    s += tmp;
+    bool first = true;
+    for (const auto &kv : pl->tuned) {
+        snprintf(tmp, sizeof tmp,
+                 "%s\n  {\"m\": %lld, \"n\": %lld, \"k\": %lld, \"mx\": %d, \"schedule\": \"%s\", "
+                 "\"tile\": \"%s\", \"sk_grid\": %d, \"us\": %.3f}",
+                 first ? "" : ",", (long long)kv.first.m, (long long)kv.first.n,
+                 (long long)kv.first.k, kv.first.mx, sched_name(kv.second.sched),
+                 tile_enum_name(kv.second.tile), kv.second.sk_grid, (double)kv.second.us);
+        s += tmp;
+        first = false;
+    }
+    s += "]}\n";
+    const int64_t need = (int64_t)s.size() + 1;
+    if (need > 0x7FFFFFFFLL) return fail(GEMM_UNSUPPORTED, "gemm_plan_cache_export: cache too large");
+    if (needed) *needed = (int32_t)need;
+    if (!buf) return ok();   // size query
+    if (len < need)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_cache_export: buffer of %d bytes, needs %lld",
+                    (int)len, (long long)need);
+    memcpy(buf, s.c_str(), (size_t)need);
+    return ok();
+}
+
+gemm_status gemm_plan_cache_import(gemm_plan_t pl, const char *json) {
+    if (!plan_ok(pl)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_cache_import: invalid plan handle");
+    if (!json) return fail(GEMM_INVALID_ARG, "gemm_plan_cache_import: text is NULL");
+    JParser jp(json);
+    JVal root;
+    if (!jp.value(&root))
+        return fail(GEMM_INVALID_ARG, "gemm_plan_cache_import: bad JSON at byte %zu: %s", jp.i,
+                    jp.err ? jp.err : "?");
+    jp.ws();
+    if (jp.i != jp.n)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_cache_import: text after the JSON value at byte %zu",
+                    jp.i);
+    std::string fmt;
+    int64_t ver = 0;
+    if (root.kind != JVal::OBJ || !json_str(root.get("format"), &fmt) || fmt != kCacheFormat ||
+        !json_int(root.get("version"), 1, 1, &ver))
+        return fail(GEMM_INVALID_ARG, "gemm_plan_cache_import: not a version-1 %s document",
+                    kCacheFormat);
+    // the cache must come from a plan with the same types and layouts
+    const JVal *plan = root.get("plan");
+    const char *want[8][2] = {{"a", dtype_name(pl->a)},          {"b", dtype_name(pl->b)},
+                              {"c", dtype_name(pl->c)},          {"d", dtype_name(pl->d)},
+                              {"acc", dtype_name(pl->acc)},      {"layout_a", layout_str(pl->la)},
+                              {"layout_b", layout_str(pl->lb)}, {"layout_c", layout_str(pl->lc)}};
+    if (!plan || plan->kind != JVal::OBJ)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_cache_import: missing \"plan\" object");
+    for (const auto &w : want) {
+        std::string v;
+        if (!json_str(plan->get(w[0]), &v) || v != w[1])
+            return fail(GEMM_UNSUPPORTED,
+                        "gemm_plan_cache_import: cache written for %s = %s, this plan has %s",
+                        w[0], v.empty() ? "(missing)" : v.c_str(), w[1]);
+    }
+    const JVal *ents = root.get("entries");
+    if (!ents || ents->kind != JVal::ARR)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_cache_import: missing \"entries\" array");
+    std::map<gemm_plan_s::TunedKey, gemm_plan_s::Tuned> add;
+    for (size_t i = 0; i < ents->arr.size(); ++i) {
+        const JVal &e = ents->arr[i];
+        int64_t m, n, k, mx = 0, skg = 0;
+        std::string ss, ts;
+        gemm_schedule sc;
+        gemm_tile tl;
+        const int64_t big = (int64_t)1 << 40;
+        const bool good = e.kind == JVal::OBJ && json_int(e.get("m"), 0, big, &m) &&
+                          json_int(e.get("n"), 0, big, &n) && json_int(e.get("k"), 0, big, &k) &&
+                          (!e.get("mx") || json_int(e.get("mx"), 0, 1, &mx)) &&
+                          (!e.get("sk_grid") || json_int(e.get("sk_grid"), 0, 1 << 20, &skg)) &&
+                          json_str(e.get("schedule"), &ss) && parse_sched(ss, &sc) &&
+                          json_str(e.get("tile"), &ts) && parse_tile(ts, &tl);
+        if (!good)
+            return fail(GEMM_INVALID_ARG, "gemm_plan_cache_import: entry %zu is malformed (needs "
+                        "integer m, n, k, a known schedule and tile)", i);
+        float us = 0.0f;
+        const JVal *u = e.get("us");
+        if (u && u->kind == JVal::NUM) us = (float)u->num;
+        add[{m, n, k, (int)mx}] = gemm_plan_s::Tuned{sc, tl, (int)skg, us};
+    }
+    for (const auto &kv : add) pl->tuned[kv.first] = kv.second;   // later entries win
+    return ok();
+}
+
+int32_t gemm_plan_cache_size(gemm_plan_t pl) {
+    if (!plan_ok(pl)) return -1;
+    return (int32_t)std::min<size_t>(pl->tuned.size(), 0x7FFFFFFF);
+}
+
+gemm_status gemm_plan_cache_clear(gemm_plan_t pl) {
+    if (!plan_ok(pl)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_cache_clear: invalid plan handle");
+    pl->tuned.clear();
     return ok();
 }
 

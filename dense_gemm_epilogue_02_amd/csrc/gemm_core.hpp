@@ -151,12 +151,21 @@ struct Prob {
 // Epilogue activations (the values of gemm_epilogue).
 enum { ACT_LINEAR = 0, ACT_RELU = 1, ACT_SIGMOID = 2, ACT_TANH = 3 };
 
+// Auxiliary-tensor elementwise ops (the values of gemm_aux_op).
+enum { AUX_ADD = 0, AUX_SUB = 1, AUX_MUL = 2, AUX_DIV = 3 };
+
 struct EpiArgs {
     float alpha, beta;
     const float *scale_a, *scale_b;   // device pointers or null (1.0)
     const void *bias;                 // N elements of the output type, or null
     int act;                          // ACT_*
     int lc_row;                       // C/D RowMajor
+    // Auxiliary tensors (M x N, output type, C/D layout), each may be null:
+    // aux is combined by aux_op before the activation (aux_after == 0) or
+    // after it; aux_out receives the activation's input.
+    const void *aux;
+    void *aux_out;
+    int aux_op, aux_after;
 };
 
 // act(v): identity, max(v, +0) (NaN -> +0), 1/(1+e^-v), tanh(v). The two
@@ -177,6 +186,43 @@ __device__ __forceinline__ float apply_act(float v, int act) {
     }
     default: return v;
     }
+}
+
+// y op x for the auxiliary tensor (fp32; the division is IEEE, correctly
+// rounded). Written as selects, not a switch: the epilogue applies it to
+// every accumulator of a fully unrolled tile, where a branch per element
+// would multiply the kernel's control flow.
+__device__ __forceinline__ float aux_apply(float y, float x, int op) {
+    const float q = y / x;
+    float r = op == AUX_SUB ? y - x : y + x;
+    r = op == AUX_MUL ? y * x : r;
+    return op == AUX_DIV ? q : r;
+}
+
+// Output value from the linear result v and the auxiliary element x (0
+// without a tensor): the op on its side of the activation; z receives the
+// activation's input. pre / post: the op applies before / after it.
+// apply_act as selects (all three candidates computed), for the same reason.
+__device__ __forceinline__ float act_select(float v, int act) {
+    const float sg = __builtin_amdgcn_rcpf(1.0f + exp_e(-v));
+    const float t = exp_e(-2.0f * __builtin_fabsf(v));
+    const float th = __builtin_copysignf((1.0f - t) * __builtin_amdgcn_rcpf(1.0f + t), v);
+    float r = act == ACT_RELU ? (v > 0.0f ? v : 0.0f) : v;
+    r = act == ACT_SIGMOID ? sg : r;
+    return act == ACT_TANH ? th : r;
+}
+
+__device__ __forceinline__ float finish_aux(float v, float x, int op, int act, bool pre, bool post,
+                                            float &z) {
+    const float r = aux_apply(v, x, op);
+    v = pre ? r : v;
+    z = v;
+    const float d = act_select(v, act);
+    const float s = aux_apply(d, x, op);
+    return post ? s : d;
+}
+__device__ __forceinline__ float finish_aux(float v, float x, const EpiArgs &e, float &z) {
+    return finish_aux(v, x, e.aux_op, e.act, e.aux && !e.aux_after, e.aux && e.aux_after, z);
 }
 
 // Persistent schedule: schedule indices [0, sk_tiles) are split stream-K
@@ -835,6 +881,20 @@ struct Tile {
         }
     }
 
+    // Four floats to consecutive output-typed elements (one RNE conversion).
+    static __device__ __forceinline__ void store4(Out *dst, int64_t idx, const float (&v)[4]) {
+        if constexpr (sizeof(Out) == 4) {
+            *reinterpret_cast<f32x4 *>(dst + idx) = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+            u32x2 t;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                t[h] = (uint32_t)__builtin_bit_cast(uint16_t, (Out)v[2 * h]) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, (Out)v[2 * h + 1]) << 16);
+            *reinterpret_cast<u32x2 *>(dst + idx) = t;
+        }
+    }
+
     template <bool BETA>
     static __device__ __forceinline__ void epi_fast(const Prob &p, const EpiArgs &e, float alpha,
                                                     int64_t m_base, int64_t n_base, const Acc &acc) {
@@ -875,16 +935,42 @@ struct Tile {
                         for (int t4 = 0; t4 < 4; ++t4)
                             v[t4] = apply_act(alpha * acc.v[i][j][q * 4 + t4] + bv[i][q][t4], act);
                     }
-                    if constexpr (sizeof(Out) == 4) {
-                        *reinterpret_cast<f32x4 *>(D + idx) = f32x4{v[0], v[1], v[2], v[3]};
-                    } else {
-                        u32x2 t;
+                    store4(D, idx, v);
+                }
+        }
+    }
+
+    // Interior tile with auxiliary tensors: the same vector accesses as
+    // epi_fast (X read like C, Z written like D), out of line, with the
+    // accumulators handed over in `vals` (the layout epi_slow takes), so the
+    // tile kernels' own code and registers stay as they are without them.
+    static __device__ __noinline__ void epi_aux(const Prob &p, const EpiArgs &e, float alpha,
+                                                int64_t m_base, int64_t n_base, const float *vals) {
+        Out *D = reinterpret_cast<Out *>(p.D);
+        const Out *C = reinterpret_cast<const Out *>(p.C);
+        const Out *bias = reinterpret_cast<const Out *>(e.bias);
+        const Out *X = reinterpret_cast<const Out *>(e.aux);
+        Out *Z = reinterpret_cast<Out *>(e.aux_out);
+        const bool pre = X && !e.aux_after, post = X && e.aux_after;
+        for (int j = 0; j < FM; ++j) {
+            const int64_t row = (m_base + j * 32) * p.N;
+            for (int i = 0; i < FN; ++i)
 #pragma unroll
-                        for (int h = 0; h < 2; ++h)
-                            t[h] = (uint32_t)__builtin_bit_cast(uint16_t, (Out)v[2 * h]) |
-                                   ((uint32_t)__builtin_bit_cast(uint16_t, (Out)v[2 * h + 1]) << 16);
-                        *reinterpret_cast<u32x2 *>(D + idx) = t;
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t idx = row + n_base + i * 32 + q * 8;
+                    float v[4], c[4] = {0.0f, 0.0f, 0.0f, 0.0f}, b[4] = {0.0f, 0.0f, 0.0f, 0.0f},
+                                x[4] = {0.0f, 0.0f, 0.0f, 0.0f}, z[4];
+                    if (e.beta != 0.0f) load4(C, idx, c);
+                    if (bias) load4(bias, n_base + i * 32 + q * 8, b);
+                    if (X) load4(X, idx, x);
+#pragma unroll
+                    for (int t4 = 0; t4 < 4; ++t4) {
+                        const float a = vals[((i * FM + j) * 4 + q) * 4 + t4];
+                        const float lin = __builtin_fmaf(alpha, a, e.beta * c[t4]) + b[t4];
+                        v[t4] = finish_aux(lin, x[t4], e.aux_op, e.act, pre, post, z[t4]);
                     }
+                    if (Z) store4(Z, idx, z);
+                    store4(D, idx, v);
                 }
         }
     }
@@ -907,7 +993,11 @@ struct Tile {
                         float v = alpha * a;
                         if (e.beta != 0.0f) v = __builtin_fmaf(alpha, a, e.beta * (float)C[idx]);
                         if (e.bias) v += (float)reinterpret_cast<const Out *>(e.bias)[n];
-                        D[idx] = (Out)apply_act(v, e.act);
+                        const float x =
+                            e.aux ? (float)reinterpret_cast<const Out *>(e.aux)[idx] : 0.0f;
+                        float z;
+                        D[idx] = (Out)finish_aux(v, x, e, z);
+                        if (e.aux_out) reinterpret_cast<Out *>(e.aux_out)[idx] = (Out)z;
                     }
         }
     }
@@ -921,7 +1011,7 @@ struct Tile {
         const int64_t n_base = (int64_t)tn * BN + wn * WTN + (lane >> 5) * 4;
         const bool interior = e.lc_row && p.vec_cd && (int64_t)(tm + 1) * BM <= p.M &&
                               (int64_t)(tn + 1) * BN <= p.N;
-        if (interior) {
+        if (interior && !e.aux && !e.aux_out) {
             if (e.beta != 0.0f) epi_fast<true>(p, e, alpha, m_base, n_base, acc);
             else epi_fast<false>(p, e, alpha, m_base, n_base, acc);
         } else {
@@ -932,7 +1022,8 @@ struct Tile {
                 for (int j = 0; j < FM; ++j)
 #pragma unroll
                     for (int x = 0; x < 16; ++x) vals[(i * FM + j) * 16 + x] = acc.v[i][j][x];
-            epi_slow(p, e, alpha, m_base, n_base, vals);
+            if (interior) epi_aux(p, e, alpha, m_base, n_base, vals);
+            else epi_slow(p, e, alpha, m_base, n_base, vals);
         }
     }
 

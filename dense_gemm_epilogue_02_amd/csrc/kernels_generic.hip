@@ -112,7 +112,10 @@ __global__ void __launch_bounds__(256) gemm_generic(GenericArgs a) {
             float v = alpha * acc[i][j];
             if (a.e.beta != 0.0f) v = __builtin_fmaf(alpha, acc[i][j], a.e.beta * (float)C[idx]);
             if (a.e.bias) v += (float)reinterpret_cast<const Out *>(a.e.bias)[n];
-            D[idx] = (Out)apply_act(v, a.e.act);
+            const float x = a.e.aux ? (float)reinterpret_cast<const Out *>(a.e.aux)[idx] : 0.0f;
+            float z;
+            D[idx] = (Out)finish_aux(v, x, a.e, z);
+            if (a.e.aux_out) reinterpret_cast<Out *>(a.e.aux_out)[idx] = (Out)z;
         }
 }
 

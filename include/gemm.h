@@ -187,6 +187,45 @@ gemm_status gemm_plan_run_mx(gemm_plan_t plan, const void *A, const void *B,
                              float beta, const uint8_t *mx_scale_a,
                              const uint8_t *mx_scale_b, void *stream);
 
+/* Elementwise op between the epilogue value and an auxiliary tensor, and
+ * the side of the activation it sits on (see gemm_plan_run_aux). */
+typedef enum {
+    GEMM_AUX_ADD = 0, /* y + X */
+    GEMM_AUX_SUB = 1, /* y - X */
+    GEMM_AUX_MUL = 2, /* y * X */
+    GEMM_AUX_DIV = 3  /* y / X (IEEE fp32 division) */
+} gemm_aux_op;
+
+typedef enum {
+    GEMM_AUX_BEFORE_ACT = 0, /* D = act(v op X)  */
+    GEMM_AUX_AFTER_ACT = 1   /* D = act(v) op X  */
+} gemm_aux_pos;
+
+/* Auxiliary-tensor epilogue ("Generating State-of-the-Art GEMMs with
+ * TorchInductor's CuteDSL backend", section 7: the epilogue-fusion kernels
+ * load and store auxiliary tensors and apply elementwise add, multiply,
+ * subtract and divide besides the ReLU / Sigmoid / Tanh activations).
+ * With v = alpha * s_A * s_B * (A B) + beta * C + bias[n] (as in
+ * gemm_plan_run_ex) and the plan's activation act:
+ *   aux_pos = GEMM_AUX_BEFORE_ACT:  z = v op aux,  D = act(z)
+ *   aux_pos = GEMM_AUX_AFTER_ACT:   z = v,         D = act(v) op aux
+ * and aux_out, if not NULL, receives z (the activation's input), rounded
+ * once to element_D. aux and aux_out are M x N in the plan's layout_C and
+ * element_C / element_D types, device memory; aux NULL means no op (D =
+ * act(v)), so aux_out alone stores the pre-activation value. All arithmetic
+ * is fp32; division is IEEE (x / 0 gives Inf or NaN, not an error).
+ * aux may be C, and aux_out may be aux (in place); aux_out equal to D gives
+ * GEMM_INVALID_ARG, any other overlap with A, B, C or D is undefined. An
+ * unknown aux_op or aux_pos gives GEMM_INVALID_ARG. Buffers stay the
+ * caller's. */
+gemm_status gemm_plan_run_aux(gemm_plan_t plan, const void *A, const void *B,
+                              const void *C, void *D, const void *bias,
+                              const void *aux, gemm_aux_op aux_op,
+                              gemm_aux_pos aux_pos, void *aux_out, int64_t M,
+                              int64_t N, int64_t K, float alpha, float beta,
+                              const float *scale_a, const float *scale_b,
+                              void *stream);
+
 /* Batched GEMM ("CUTLASS Python接口", batched GEMM: batch_count and
  * batch_stride_A/B/C): batch_count problems of one shape M x N x K; problem b
  * reads A + b*stride_a, B + b*stride_b, C + b*stride_c and writes
@@ -236,6 +275,55 @@ gemm_status grouped_gemm_run(gemm_plan_t plan, const gemm_problem *problems,
 gemm_status gemm_plan_describe(gemm_plan_t plan, int64_t M, int64_t N,
                                int64_t K, int32_t num_cus, char *buf,
                                int32_t len);
+
+/* One timed configuration of gemm_plan_profile. */
+typedef struct {
+    gemm_schedule schedule; /* as launched (never AUTO) */
+    gemm_tile tile;         /* as launched; GENERIC for the scalar-load kernel */
+    int32_t sk_grid;        /* 0: automatic grid */
+    int32_t grid;           /* workgroups launched */
+    float us;               /* mean microseconds per run */
+} gemm_config;
+
+/* Kernel profiler ("CUTLASS Python接口", GemmProfiler: for a given size and
+ * data type, run every kernel implementation of the library and report each
+ * one's execution time). Runs every distinct (tile, schedule) launch this plan
+ * can make for M x N x K on the caller's buffers and `stream`: one untimed
+ * run, then `iters` back-to-back runs between two HIP events; blocks until
+ * they finish. Writes up to max_results configurations, fastest first, to
+ * `results` and their total count to *n_results (either may be NULL/0), and
+ * records the fastest in the plan's configuration cache, which later runs of
+ * exactly this M x N x K use whenever the plan has no gemm_plan_set_config
+ * override (batched calls and MX runs keep the heuristics). D is
+ * overwritten (it holds the last run's result); D == C with beta != 0
+ * gives GEMM_INVALID_ARG. iters outside [1, 100000] gives GEMM_INVALID_ARG.
+ * Operands follow gemm_plan_run's rules. */
+gemm_status gemm_plan_profile(gemm_plan_t plan, const void *A, const void *B,
+                              const void *C, void *D, int64_t M, int64_t N,
+                              int64_t K, float alpha, float beta, int32_t iters,
+                              gemm_config *results, int32_t max_results,
+                              int32_t *n_results, void *stream);
+
+/* Exportable configuration cache ("Generating State-of-the-Art GEMMs with
+ * TorchInductor's CuteDSL backend", roadmap: a portable, human-readable
+ * format such as JSON for autotuned GEMM configurations, with import and
+ * export calls, so tuning carries across runs and environments).
+ * Export writes the plan's cache as JSON text: the format name and version,
+ * the plan's element types and layouts, and one entry per tuned shape
+ * {m, n, k, mx, schedule, tile, sk_grid, us}. *needed receives the size
+ * including the terminating NUL; buf == NULL only queries it; a buffer
+ * shorter than that gives GEMM_INVALID_ARG and writes nothing.
+ * Import merges such a text into the plan's cache (an imported entry
+ * replaces one of the same shape). Malformed text gives GEMM_INVALID_ARG, a
+ * cache written for other element types or layouts GEMM_UNSUPPORTED; on any
+ * error the cache is left unchanged. Host-only; no device call. */
+gemm_status gemm_plan_cache_export(gemm_plan_t plan, char *buf, int32_t len,
+                                   int32_t *needed);
+gemm_status gemm_plan_cache_import(gemm_plan_t plan, const char *json);
+
+/* Number of cached shapes (-1 for an invalid handle), and clearing. */
+int32_t gemm_plan_cache_size(gemm_plan_t plan);
+gemm_status gemm_plan_cache_clear(gemm_plan_t plan);
 
 /* Thread-local description of the last failure in this thread ("" if none). */
 const char *gemm_last_error(void);

@@ -317,6 +317,39 @@ def mx_integer_problem(M: int, N: int, K: int, *, la: str = ROW, lb: str = COL,
                    la, lb, lc, bias, xa, xb)
 
 
+def mx_quantize_device(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The MX conversion of mx_quantize done with torch ops on x's device
+    (for full-size benchmark inputs): logical [R, K] rows -> (e4m3 elements
+    [R, K], E8M0 codes [R, K/32] uint8); same shared-exponent rule, RNE
+    saturating element cast."""
+    R, K = x.shape
+    assert K % MX_BLOCK == 0
+    blk = x.float().reshape(R, K // MX_BLOCK, MX_BLOCK)
+    amax = blk.abs().amax(dim=2)
+    e = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax,
+                                                                  torch.ones_like(amax))))
+                    - E4M3_EMAX, torch.zeros_like(amax))
+    code = (e + 127).clamp(0, 254)
+    q = (blk / torch.exp2(code - 127).unsqueeze(2)).clamp(-E4M3_MAX, E4M3_MAX)
+    return (q.reshape(R, K).to(torch.float8_e4m3fn),
+            code.to(torch.uint8).contiguous())
+
+
+def mx_layer_device(name: str, device, seed: int = 0):
+    """MXFP8 version of a transformer-layer GEMM, drawn on ``device``:
+    A ~ N(0,1) [M, K] RowMajor, W ~ N(0, 0.02^2) stored [N, K] (ColumnMajor
+    B), both MX-quantized along K. Returns (M, N, K, A, B, scales_a, scales_b)."""
+    M, N, K = LAYER_SHAPES[name]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    a = torch.randn((M, K), generator=gen, device=device, dtype=torch.float32)
+    A, xa = mx_quantize_device(a)
+    del a
+    w = torch.randn((N, K), generator=gen, device=device, dtype=torch.float32) * 0.02
+    B, xb = mx_quantize_device(w)
+    return M, N, K, A, B, xa, xb
+
+
 # ---------------------------------------------------------------------------
 # auxiliary tensor of the epilogue
 

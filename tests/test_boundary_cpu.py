@@ -255,3 +255,136 @@ def test_mx_validation_before_any_device_call():
                       None) == g.Status.OK
     finally:
         g.gemm_plan_destroy(h)
+
+
+def test_aux_validation_before_any_device_call():
+    run_aux = g.lib.gemm_plan_run_aux
+    args = lambda h, op=0, pos=0, aux=32, out=48, D=16, M=8: (
+        h, 16, 16, None, D, None, aux, op, pos, out, M, 8, 8, 1.0, 0.0, None, None, None)
+    assert run_aux(*args(None)) == g.Status.NOT_INITIALIZED
+    h = g.gemm_plan_create_simple(g.Dtype.F16, g.Layout.ROW_MAJOR, g.Epilogue.RELU)
+    try:
+        assert run_aux(*args(h, op=4)) == g.Status.INVALID_ARG
+        assert "elementwise op" in g.gemm_last_error()
+        assert run_aux(*args(h, op=-1)) == g.Status.INVALID_ARG
+        assert run_aux(*args(h, pos=2)) == g.Status.INVALID_ARG
+        assert "side of the activation" in g.gemm_last_error()
+        assert run_aux(*args(h, out=16)) == g.Status.INVALID_ARG   # Z over D
+        assert "same buffer" in g.gemm_last_error()
+        # negative sizes fail; an empty output is a no-op
+        assert run_aux(*args(h, M=-1)) == g.Status.INVALID_ARG
+        assert run_aux(*args(h, D=None, aux=None, out=None, M=0)) == g.Status.OK
+        with pytest.raises(ValueError):   # the binding checks buffer extents too
+            g.Plan("f16").run_aux(None, None, None, None, 8, 8, 8, aux_op="mul")
+    finally:
+        g.gemm_plan_destroy(h)
+
+
+def _cache_doc(entries, a="BF16", layout_b="col"):
+    import json
+    return json.dumps({"format": "mi355-gemm-config-cache", "version": 1, "arch": "gfx950",
+                       "plan": {"a": a, "b": a, "c": a, "d": a, "acc": "F32", "layout_a": "row",
+                                "layout_b": layout_b, "layout_c": "row"},
+                       "entries": entries})
+
+
+def test_config_cache_import_export_round_trip_without_device():
+    import json
+    D, L, E = g.Dtype, g.Layout, g.Epilogue
+    mk = lambda: g.gemm_plan_create(D.BF16, D.BF16, D.BF16, D.BF16, D.F32, L.ROW_MAJOR,
+                                    L.COL_MAJOR, L.ROW_MAJOR, E.LINEAR)
+    h, h2 = mk(), mk()
+    try:
+        assert g.gemm_plan_cache_size(h) == 0
+        empty = json.loads(g.gemm_plan_cache_export(h))
+        assert empty["format"] == "mi355-gemm-config-cache" and empty["entries"] == []
+        assert empty["plan"]["layout_b"] == "col" and empty["plan"]["a"] == "BF16"
+        before = g.gemm_plan_describe(h, 4096, 8192, 8192)
+        assert before["tile"] == "256x256" and before["schedule"] == "data_parallel"
+        doc = _cache_doc([{"m": 4096, "n": 8192, "k": 8192, "mx": 0, "schedule": "stream_k",
+                           "tile": "128x128", "sk_grid": 0, "us": 500.0},
+                          {"m": 64, "n": 64, "k": 64, "schedule": "data_parallel",
+                           "tile": "generic"}])
+        g.gemm_plan_cache_import(h, doc)
+        assert g.gemm_plan_cache_size(h) == 2
+        # a cached shape changes what a run launches; other shapes do not change
+        after = g.gemm_plan_describe(h, 4096, 8192, 8192)
+        assert after["tile"] == "128x128" and after["schedule"] == "stream_k"
+        assert g.gemm_plan_describe(h, 64, 64, 64)["kernel"] == "generic"
+        assert g.gemm_plan_describe(h, 4096, 8192, 4096)["tile"] == "256x256"
+        # an explicit override wins over the cache
+        g.gemm_plan_set_config(h, g.Schedule.DATA_PARALLEL, g.Tile.T256x256, 0)
+        assert g.gemm_plan_describe(h, 4096, 8192, 8192)["schedule"] == "data_parallel"
+        g.gemm_plan_set_config(h, g.Schedule.AUTO, g.Tile.AUTO, 0)
+        # export -> import into a fresh plan reproduces the cache
+        text = g.gemm_plan_cache_export(h)
+        g.gemm_plan_cache_import(h2, text)
+        assert g.gemm_plan_cache_export(h2) == text
+        ents = json.loads(text)["entries"]
+        assert [(e["m"], e["tile"], e["schedule"]) for e in ents] == \
+            [(64, "generic", "data_parallel"), (4096, "128x128", "stream_k")]
+        g.gemm_plan_cache_clear(h2)
+        assert g.gemm_plan_cache_size(h2) == 0
+    finally:
+        g.gemm_plan_destroy(h)
+        g.gemm_plan_destroy(h2)
+
+
+def test_config_cache_import_rejects_bad_text_and_keeps_cache():
+    D, L, E = g.Dtype, g.Layout, g.Epilogue
+    h = g.gemm_plan_create(D.BF16, D.BF16, D.BF16, D.BF16, D.F32, L.ROW_MAJOR, L.COL_MAJOR,
+                           L.ROW_MAJOR, E.LINEAR)
+    imp = lambda t: g.lib.gemm_plan_cache_import(h, t.encode())
+    try:
+        good = {"m": 1, "n": 2, "k": 3, "schedule": "hybrid", "tile": "64x256"}
+        assert imp(_cache_doc([good])) == g.Status.OK
+        assert g.gemm_plan_cache_size(h) == 1
+        bad = [
+            "", "{", "[1, 2]", "{\"format\": \"x\", \"version\": 1}",
+            _cache_doc([good]) + " trailing",
+            _cache_doc([dict(good, m=-1)]),
+            _cache_doc([dict(good, m=1.5)]),
+            _cache_doc([dict(good, tile="512x512")]),
+            _cache_doc([dict(good, schedule="fastest")]),
+            _cache_doc([good, {"m": 5}]),              # a bad entry rejects the whole text
+            _cache_doc([good]).replace("\"version\": 1", "\"version\": 2"),
+        ]
+        for t in bad:
+            assert imp(t) == g.Status.INVALID_ARG, t
+            assert "gemm_plan_cache_import" in g.gemm_last_error()
+        # written for another plan's types or layouts
+        assert imp(_cache_doc([good], a="F16")) == g.Status.UNSUPPORTED
+        assert imp(_cache_doc([good], layout_b="row")) == g.Status.UNSUPPORTED
+        assert "layout_b" in g.gemm_last_error()
+        assert g.gemm_plan_cache_size(h) == 1          # unchanged by every failure
+        # a short export buffer is an error and writes nothing
+        need = ctypes.c_int32(0)
+        assert g.lib.gemm_plan_cache_export(h, None, 0, ctypes.byref(need)) == g.Status.OK
+        buf = ctypes.create_string_buffer(need.value - 1)
+        assert g.lib.gemm_plan_cache_export(h, buf, len(buf), ctypes.byref(need)) == \
+            g.Status.INVALID_ARG
+        assert buf.value == b""
+        assert g.lib.gemm_plan_cache_size(None) == -1
+        assert g.lib.gemm_plan_cache_import(None, b"{}") == g.Status.NOT_INITIALIZED
+    finally:
+        g.gemm_plan_destroy(h)
+
+
+def test_profile_validation_before_any_device_call():
+    prof = g.lib.gemm_plan_profile
+    n = ctypes.c_int32(0)
+    arr = (g.gemm_config * 4)()
+    args = lambda h, iters=5, C=None, D=16, beta=0.0, res=arr, M=8: (
+        h, 16, 16, C, D, M, 8, 8, 1.0, beta, iters, res, 4 if res is not None else 0,
+        ctypes.byref(n), None)
+    assert prof(*args(None)) == g.Status.NOT_INITIALIZED
+    h = g.gemm_plan_create_simple(g.Dtype.F16, g.Layout.ROW_MAJOR, g.Epilogue.LINEAR)
+    try:
+        assert prof(*args(h, iters=0)) == g.Status.INVALID_ARG
+        assert "iters" in g.gemm_last_error()
+        assert prof(*args(h, C=16, D=16, beta=1.0)) == g.Status.INVALID_ARG
+        assert "previous run" in g.gemm_last_error()
+        assert prof(*args(h, M=-1)) == g.Status.INVALID_ARG
+        assert prof(*args(h, D=None, M=0)) == g.Status.OK and n.value == 0
+    finally:
+        g.gemm_plan_destroy(h)
