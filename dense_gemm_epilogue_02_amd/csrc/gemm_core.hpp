@@ -221,6 +221,25 @@ __device__ __forceinline__ float finish_aux(float v, float x, int op, int act, b
     const float s = aux_apply(d, x, op);
     return post ? s : d;
 }
+// finish_aux with the op and activation chosen by (uniform) branches: only
+// the selected arithmetic runs. For the out-of-line epilogue, where the
+// branches stay few.
+__device__ __forceinline__ float aux_op_branch(float y, float x, int op) {
+    switch (op) {
+    case AUX_SUB: return y - x;
+    case AUX_MUL: return y * x;
+    case AUX_DIV: return y / x;
+    default: return y + x;
+    }
+}
+__device__ __forceinline__ float finish_aux_branch(float v, float x, int op, int act, bool pre,
+                                                   bool post, float &z) {
+    if (pre) v = aux_op_branch(v, x, op);
+    z = v;
+    float d = apply_act(v, act);
+    if (post) d = aux_op_branch(d, x, op);
+    return d;
+}
 __device__ __forceinline__ float finish_aux(float v, float x, const EpiArgs &e, float &z) {
     return finish_aux(v, x, e.aux_op, e.act, e.aux && !e.aux_after, e.aux && e.aux_after, z);
 }
@@ -941,39 +960,47 @@ struct Tile {
     }
 
     // Interior tile with auxiliary tensors: the same vector accesses as
-    // epi_fast (X read like C, Z written like D), out of line, with the
-    // accumulators handed over in `vals` (the layout epi_slow takes), so the
-    // tile kernels' own code and registers stay as they are without them.
+    // epi_fast (X read like C, Z written like D), out of line so the tile
+    // kernels' own code and registers stay as they are without them. The
+    // accumulators of fragment rows j0 .. j0+jc-1 arrive through the idle LDS:
+    // group ((jj * FN + i) * 4 + q) of thread tid at vals[group * NT + tid].
     static __device__ __noinline__ void epi_aux(const Prob &p, const EpiArgs &e, float alpha,
-                                                int64_t m_base, int64_t n_base, const float *vals) {
+                                                int64_t m_base, int64_t n_base, const f32x4 *vals,
+                                                int j0, int jc) {
         Out *D = reinterpret_cast<Out *>(p.D);
         const Out *C = reinterpret_cast<const Out *>(p.C);
         const Out *bias = reinterpret_cast<const Out *>(e.bias);
         const Out *X = reinterpret_cast<const Out *>(e.aux);
         Out *Z = reinterpret_cast<Out *>(e.aux_out);
         const bool pre = X && !e.aux_after, post = X && e.aux_after;
-        for (int j = 0; j < FM; ++j) {
-            const int64_t row = (m_base + j * 32) * p.N;
+        const int tid = threadIdx.x;
+        for (int jj = 0; jj < jc; ++jj) {
+            const int64_t row = (m_base + (j0 + jj) * 32) * p.N;
             for (int i = 0; i < FN; ++i)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int64_t idx = row + n_base + i * 32 + q * 8;
                     float v[4], c[4] = {0.0f, 0.0f, 0.0f, 0.0f}, b[4] = {0.0f, 0.0f, 0.0f, 0.0f},
                                 x[4] = {0.0f, 0.0f, 0.0f, 0.0f}, z[4];
+                    const f32x4 a = vals[((jj * FN + i) * 4 + q) * NT + tid];
                     if (e.beta != 0.0f) load4(C, idx, c);
                     if (bias) load4(bias, n_base + i * 32 + q * 8, b);
                     if (X) load4(X, idx, x);
 #pragma unroll
                     for (int t4 = 0; t4 < 4; ++t4) {
-                        const float a = vals[((i * FM + j) * 4 + q) * 4 + t4];
-                        const float lin = __builtin_fmaf(alpha, a, e.beta * c[t4]) + b[t4];
-                        v[t4] = finish_aux(lin, x[t4], e.aux_op, e.act, pre, post, z[t4]);
+                        const float lin = __builtin_fmaf(alpha, a[t4], e.beta * c[t4]) + b[t4];
+                        v[t4] = finish_aux_branch(lin, x[t4], e.aux_op, e.act, pre, post, z[t4]);
                     }
                     if (Z) store4(Z, idx, z);
                     store4(D, idx, v);
                 }
         }
     }
+
+    // Fragment rows per LDS hand-off to epi_aux: as many as the tile's LDS holds.
+    static constexpr int AUX_JC_FIT = LDS_BYTES / (NT * FN * 4 * 16);
+    static constexpr int AUX_JC = AUX_JC_FIT >= FM ? FM : AUX_JC_FIT;
+    static_assert(AUX_JC >= 1 && FM % AUX_JC == 0, "LDS hand-off of the auxiliary epilogue");
 
     // Edge tiles, ColumnMajor C/D or unaligned C/D: element by element.
     static __device__ __noinline__ void epi_slow(const Prob &p, const EpiArgs &e, float alpha,
@@ -1002,8 +1029,11 @@ struct Tile {
         }
     }
 
+    // `lds`: the tile's LDS, idle here (the main loop ends with a barrier);
+    // the auxiliary-tensor path hands the accumulators over through it and
+    // closes with a barrier before the next tile's copies may land.
     static __device__ __forceinline__ void epilogue(const Prob &p, const EpiArgs &e, int tm, int tn,
-                                                    const Acc &acc) {
+                                                    const Acc &acc, char *lds) {
         const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
         const int wm = wave / WN, wn = wave % WN;
         const float alpha = eff_alpha(e);
@@ -1011,7 +1041,25 @@ struct Tile {
         const int64_t n_base = (int64_t)tn * BN + wn * WTN + (lane >> 5) * 4;
         const bool interior = e.lc_row && p.vec_cd && (int64_t)(tm + 1) * BM <= p.M &&
                               (int64_t)(tn + 1) * BN <= p.N;
-        if (interior && !e.aux && !e.aux_out) {
+        if (interior && (e.aux || e.aux_out)) {
+            f32x4 *buf = reinterpret_cast<f32x4 *>(lds);
+            const int tid = threadIdx.x;
+#pragma unroll
+            for (int j0 = 0; j0 < FM; j0 += AUX_JC) {
+                // each thread reads back only its own slots: no barrier between
+#pragma unroll
+                for (int jj = 0; jj < AUX_JC; ++jj)
+#pragma unroll
+                    for (int i = 0; i < FN; ++i)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            buf[((jj * FN + i) * 4 + q) * NT + tid] =
+                                f32x4{acc.v[i][j0 + jj][q * 4], acc.v[i][j0 + jj][q * 4 + 1],
+                                      acc.v[i][j0 + jj][q * 4 + 2], acc.v[i][j0 + jj][q * 4 + 3]};
+                epi_aux(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
+            }
+            __syncthreads();
+        } else if (interior) {
             if (e.beta != 0.0f) epi_fast<true>(p, e, alpha, m_base, n_base, acc);
             else epi_fast<false>(p, e, alpha, m_base, n_base, acc);
         } else {
@@ -1022,8 +1070,7 @@ struct Tile {
                 for (int j = 0; j < FM; ++j)
 #pragma unroll
                     for (int x = 0; x < 16; ++x) vals[(i * FM + j) * 16 + x] = acc.v[i][j][x];
-            if (interior) epi_aux(p, e, alpha, m_base, n_base, vals);
-            else epi_slow(p, e, alpha, m_base, n_base, vals);
+            epi_slow(p, e, alpha, m_base, n_base, vals);
         }
     }
 
@@ -1204,7 +1251,7 @@ gemm_persistent(KArgs a) {
         const Prob pt = TL::tile_problem(p, t, s.group_m, tm, tn);
         TL::mainloop(pt, tm, tn, c, (p.ipt - c + S - 1) / S, S, acc, lds);
         if (S == 1) {
-            TL::epilogue(pt, a.e, tm, tn, acc);
+            TL::epilogue(pt, a.e, tm, tn, acc, lds);
             return;
         }
         const size_t slot_elems = (size_t)TL::BM * TL::BN;
@@ -1214,7 +1261,7 @@ gemm_persistent(KArgs a) {
         if (arrive_last(&s.counters[t], S - 1, lds)) {
             // sum the units in order c = 0 .. S-1 (deterministic)
             TL::add_partials([&](int u) { return s.partials + ((size_t)t * S + u) * slot_elems; }, S, acc);
-            TL::epilogue(pt, a.e, tm, tn, acc);
+            TL::epilogue(pt, a.e, tm, tn, acc, lds);
             if (threadIdx.x == 0)
                 __hip_atomic_store(&s.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -1235,7 +1282,7 @@ gemm_persistent(KArgs a) {
             const Prob pt = TL::tile_problem(p, t, s.group_m, tm, tn);
             TL::mainloop(pt, tm, tn, k0, k1 - k0, 1, acc, lds);
             if (k0 == 0 && k1 == p.ipt) {
-                TL::epilogue(pt, a.e, tm, tn, acc);
+                TL::epilogue(pt, a.e, tm, tn, acc, lds);
             } else {
                 // every contributor publishes its partial, the last to arrive
                 // sums all partials in contributor order (deterministic)
@@ -1255,7 +1302,7 @@ gemm_persistent(KArgs a) {
                             return s.partials + (size_t)(2 * u + (t == ft ? 0 : 1)) * slot_elems;
                         },
                         v1 - v0 + 1, acc);
-                    TL::epilogue(pt, a.e, tm, tn, acc);
+                    TL::epilogue(pt, a.e, tm, tn, acc, lds);
                     if (threadIdx.x == 0)
                         __hip_atomic_store(&s.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
@@ -1267,7 +1314,7 @@ gemm_persistent(KArgs a) {
     for (int t = s.sk_tiles + v; t < s.total_tiles; t += s.grid) {
         const Prob pt = TL::tile_problem(p, t, s.group_m, tm, tn);
         TL::mainloop(pt, tm, tn, 0, p.ipt, 1, acc, lds);
-        TL::epilogue(pt, a.e, tm, tn, acc);
+        TL::epilogue(pt, a.e, tm, tn, acc, lds);
     }
 }
 
@@ -1289,7 +1336,7 @@ gemm_grouped(GroupArgs g) {
         int tm, tn;
         tile_coords(t - g.desc[lo].tile_start, p.tiles_m, p.tiles_n, g.group_m, tm, tn);
         TL::mainloop(p, tm, tn, 0, p.ipt, 1, acc, lds);
-        TL::epilogue(p, g.e, tm, tn, acc);
+        TL::epilogue(p, g.e, tm, tn, acc, lds);
     }
 }
 
