@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "GEMM TFLOP/s and % of MI355X MFMA peak per dtype, 1 GPU"
 
 WORKLOADS = ("layer", "down", "fp16_1024_relu", "grouped64", "fp8_decode", "fp32_small",
-             "mx_layer", "layer_residual")
+             "mx_layer", "layer_residual", "batched16")
 
 
 def source_hash() -> str:
@@ -195,7 +195,31 @@ def build_layer_residual():
     return items, "bf16"
 
 
+def build_batched():
+    """The batched example of the CUTLASS Python page: 16 independent fp16
+    1024^3 GEMMs (A [16, M, K], B [16, K, N], D [16, M, N], RowMajor, beta 0)."""
+    import torch
+    import synthetic as syn
+    import dense_gemm_epilogue_02_amd as g
+    dev = torch.device("cuda:0")
+    bs, M, N, K = 16, 1024, 1024, 1024
+    probs = [syn.make_problem(M, N, K, dtype_ab="f16", dtype_cd="f16", seed=200 + b)
+             for b in range(bs)]
+    A = torch.stack([q.A for q in probs]).to(dev)
+    B = torch.stack([q.B for q in probs]).to(dev)
+    D = torch.empty((bs, M, N), dtype=torch.float16, device=dev)
+    plan = g.Plan("f16", la="row", lb="row", lc="row")
+    shape = type("S", (), dict(M=M, N=N, K=K))
+    return [dict(name="batched16_f16_1024", p=shape, flops=2 * bs * M * N * K, plan=plan,
+                 call=lambda: plan.run_batched(A, B, None, D, M, N, K, bs,
+                                               (M * K, K * N, 0, M * N)),
+                 bytes=2 * bs * (M * K + K * N + M * N),
+                 describe=plan.describe(M, N, K))], "f16"
+
+
 def build(workload):
+    if workload == "batched16":
+        return build_batched()
     if workload == "mx_layer":
         return build_mx_layer()
     if workload == "layer_residual":
@@ -323,6 +347,7 @@ def main():
                                 "fp32_small": "fp32_128x64x256",
                                 "mx_layer": "llama70b_like_layer_gemms_mxfp8_m4096",
                                 "layer_residual": "o_and_down_proj_bf16_residual_add_m4096",
+                                "batched16": "batched16_fp16_1024cubed",
                                 }[args.workload],
                    "gemms": {it["name"]: [it["p"].M, it["p"].N, it["p"].K] for it in items},
                    "layout": "A RowMajor, B ColumnMajor ([N,K]), D RowMajor"

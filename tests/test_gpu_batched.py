@@ -200,3 +200,29 @@ def test_batched_in_place_sixteen_entries():
     plan.close()
     outs = [logical(C[b * M * N:(b + 1) * M * N], probs[0]) for b in range(nb)]
     close_all(outs, probs, what="in place x16")
+
+
+def test_batched16_fp16_1024_full_size_sampled():
+    """The benchmark's batched configuration (16 x fp16 1024^3, strides M*K,
+    K*N, 0, M*N, beta 0, the same seeds), in the launch bench.py times;
+    64 sampled outputs per entry against the oracle."""
+    M = N = K = 1024
+    nb = 16
+    probs = [syn.make_problem(M, N, K, dtype_ab="f16", dtype_cd="f16", seed=200 + b)
+             for b in range(nb)]
+    A = torch.stack([q.A for q in probs]).to(DEV)
+    B = torch.stack([q.B for q in probs]).to(DEV)
+    D = torch.full((nb, M, N), float("nan"), dtype=torch.float16, device=DEV)
+    plan = g.Plan("f16", la="row", lb="row", lc="row")
+    print(f"[gpu] batched16 full size {plan.describe(M, N, K)}", flush=True)
+    plan.run_batched(A, B, None, D, M, N, K, nb, (M * K, K * N, 0, M * N))
+    torch.cuda.synchronize()
+    plan.close()
+    rng = np.random.default_rng(73)
+    for b in (0, 7, 15):
+        ii, jj = rng.integers(0, M, 64), rng.integers(0, N, 64)
+        ii[:2], jj[:2] = (0, M - 1), (0, N - 1)
+        r = oracle.gemm_entries(probs[b], ii, jj)
+        got = D[b].float().cpu().double().numpy()[ii, jj]
+        acceptance.check_close(got, r.ref, r.S, "f16", "f16", f"batched16 entry {b}")
+    assert bool(torch.isfinite(D).all())

@@ -130,3 +130,25 @@ def test_mx_k_zero_is_beta_c_plus_bias():
     q = dataclasses.replace(p, K=0, A=p.A[:0], B=p.B[:0], mx_a=p.mx_a[:, :0],
                             mx_b=p.mx_b[:, :0])
     exact(run_mx(q), q, what="K=0")
+
+
+def test_mx_layer_bench_inputs_sampled():
+    """The MXFP8 layer benchmark's own inputs (drawn and MX-quantized on the
+    device, QKV 4096x10240x8192, seed 0) in its launch; sampled outputs
+    against the oracle on the same bytes."""
+    M, N, K, A, B, xa, xb = syn.mx_layer_device("qkv", DEV, seed=0)
+    plan = g.Plan("f8e4m3", "bf16", "row", "col", "row")
+    D = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    print(f"[gpu] mx layer qkv {plan.describe(M, N, K)}", flush=True)
+    plan.run_mx(A, B, None, D, M, N, K, xa, xb)
+    torch.cuda.synchronize()
+    plan.close()
+    p = syn.Problem(M, N, K, A.cpu(), B.cpu(), None, 1.0, 0.0, None, None, "f8e4m3", "bf16",
+                    "row", "col", "row", None, xa.cpu(), xb.cpu())
+    rng = np.random.default_rng(101)
+    ii, jj = rng.integers(0, M, 96), rng.integers(0, N, 96)
+    ii[:2], jj[:2] = (0, M - 1), (0, N - 1)
+    r = oracle.gemm_entries(p, ii, jj)
+    got = D.float().cpu().double().numpy()[ii, jj]
+    acceptance.check_close(got, r.ref, r.S, "f8e4m3", "bf16", "mx layer qkv sampled")
+    assert bool(torch.isfinite(D).all())
