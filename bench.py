@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "GEMM TFLOP/s and % of MI355X MFMA peak per dtype, 1 GPU"
 
 WORKLOADS = ("layer", "down", "fp16_1024_relu", "grouped64", "fp8_decode", "fp32_small",
-             "mx_layer", "layer_residual", "batched16")
+             "mx_layer", "layer_residual", "batched16", "layer_nn")
 
 
 def source_hash() -> str:
@@ -57,15 +57,15 @@ def load_traffic(workload: str):
 
 # ----------------------------------------------------------------- workloads
 
-def build_layer(names):
+def build_layer(names, lb="col"):
     import torch
     import synthetic as syn
     import dense_gemm_epilogue_02_amd as g
     dev = torch.device("cuda:0")
-    plan = g.Plan("bf16", la="row", lb="col", lc="row")
+    plan = g.Plan("bf16", la="row", lb=lb, lc="row")
     items = []
     for i, name in enumerate(names):
-        p = syn.config4(name, seed=i)
+        p = syn.config4(name, seed=i, lb=lb)
         A, B = p.A.to(dev), p.B.to(dev)
         D = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev)
         items.append(dict(name=name, p=p, flops=p.flops, plan=plan,
@@ -218,6 +218,8 @@ def build_batched():
 
 
 def build(workload):
+    if workload == "layer_nn":
+        return build_layer(["qkv", "o", "gate_up", "down"], lb="row")
     if workload == "batched16":
         return build_batched()
     if workload == "mx_layer":
@@ -348,6 +350,7 @@ def main():
                                 "mx_layer": "llama70b_like_layer_gemms_mxfp8_m4096",
                                 "layer_residual": "o_and_down_proj_bf16_residual_add_m4096",
                                 "batched16": "batched16_fp16_1024cubed",
+                                "layer_nn": "llama70b_like_layer_gemms_bf16_m4096_rowmajor_b",
                                 }[args.workload],
                    "gemms": {it["name"]: [it["p"].M, it["p"].N, it["p"].K] for it in items},
                    "layout": "A RowMajor, B ColumnMajor ([N,K]), D RowMajor"
