@@ -214,7 +214,7 @@ def build_batched():
                  call=lambda: plan.run_batched(A, B, None, D, M, N, K, bs,
                                                (M * K, K * N, 0, M * N)),
                  bytes=2 * bs * (M * K + K * N + M * N),
-                 describe=plan.describe(M, N, K))], "f16"
+                 describe=plan.describe_batched(M, N, K, bs))], "f16"
 
 
 def build(workload):

@@ -135,6 +135,8 @@ def _load():
     L.gemm_plan_cache_clear.argtypes = [vp]
     L.gemm_plan_describe.restype = st
     L.gemm_plan_describe.argtypes = [vp, i64, i64, i64, i32, ctypes.c_char_p, i32]
+    L.gemm_plan_describe_batched.restype = st
+    L.gemm_plan_describe_batched.argtypes = [vp, i64, i64, i64, i64, i32, ctypes.c_char_p, i32]
     L.gemm_last_error.restype = ctypes.c_char_p
     L.gemm_last_error.argtypes = []
     L.gemm_status_string.restype = ctypes.c_char_p
@@ -155,7 +157,8 @@ EXPORTED = ("gemm_plan_create", "gemm_plan_create_simple", "gemm_plan_destroy",
             "gemm_plan_run_ex", "gemm_plan_run_mx", "gemm_plan_run_aux",
             "gemm_plan_run_batched", "grouped_gemm_run", "gemm_plan_profile",
             "gemm_plan_cache_export", "gemm_plan_cache_import", "gemm_plan_cache_size",
-            "gemm_plan_cache_clear", "gemm_plan_describe", "gemm_last_error",
+            "gemm_plan_cache_clear", "gemm_plan_describe", "gemm_plan_describe_batched",
+            "gemm_last_error",
             "gemm_status_string", "gemm_supported_count", "gemm_supported_get",
             "gemm_version")
 
@@ -303,6 +306,14 @@ def gemm_plan_describe(plan: int, M: int, N: int, K: int, num_cus: int = 0) -> d
     return json.loads(buf.value.decode())
 
 
+def gemm_plan_describe_batched(plan: int, M: int, N: int, K: int, batch: int,
+                               num_cus: int = 0) -> dict:
+    import json
+    buf = ctypes.create_string_buffer(512)
+    _check(lib.gemm_plan_describe_batched(plan, M, N, K, batch, num_cus, buf, len(buf)))
+    return json.loads(buf.value.decode())
+
+
 def gemm_last_error() -> str:
     return lib.gemm_last_error().decode()
 
@@ -386,6 +397,9 @@ class Plan:
     def set_config(self, schedule=Schedule.AUTO, tile=Tile.AUTO, sk_grid: int = 0):
         gemm_plan_set_config(self.handle, schedule, tile, sk_grid)
         return self
+
+    def describe_batched(self, M, N, K, batch, num_cus=0) -> dict:
+        return gemm_plan_describe_batched(self.handle, M, N, K, batch, num_cus)
 
     def describe(self, M, N, K, num_cus=0) -> dict:
         return gemm_plan_describe(self.handle, M, N, K, num_cus)

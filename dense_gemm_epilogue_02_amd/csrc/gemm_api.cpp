@@ -413,12 +413,15 @@ const char *operand_vec_problem(const void *ptr, bool kc, int64_t contig, int64_
     return nullptr;
 }
 
-gemm_tile pick_tile(int fam, int64_t M, int64_t N, int cus) {
+// `batch`: problems of this shape in one launch. The 256x256 tile needs a
+// full wave of them: on 16 x 1024^3 and 64 x 512^3 fp16 batches it ran
+// 1.2-1.4x faster than 128x128 tiles once the batch supplies the wave.
+gemm_tile pick_tile(int fam, int64_t M, int64_t N, int cus, int64_t batch = 1) {
     if (fam == FAM_F32) return GEMM_TILE_128x128;
     // skinny M streams B once: 64-row tiles matched or beat 32-row ones for
     // every measured M <= 64 (fewer, longer B panels per workgroup)
     if (M <= 64) return GEMM_TILE_64x256;
-    const int64_t big = cdiv(M, 256) * cdiv(N, 256);
+    const int64_t big = cdiv(M, 256) * cdiv(N, 256) * (batch > 1 ? batch : 1);
     return big >= cus ? GEMM_TILE_256x256 : GEMM_TILE_128x128;
 }
 
@@ -493,7 +496,7 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
                 reinterpret_cast<uintptr_t>(bias) % (4 * osz) == 0)
                    ? 1 : 0;
     if (cfg.tile != GEMM_TILE_GENERIC) {
-        gemm_tile t = cfg.tile == GEMM_TILE_AUTO ? pick_tile(fam, M, N, cus) : cfg.tile;
+        gemm_tile t = cfg.tile == GEMM_TILE_AUTO ? pick_tile(fam, M, N, cus, batch) : cfg.tile;
         const KernelEntry *e = registry().find(fam, a_kc, b_kc, tile_id(t));
         if (!e) e = registry().find(fam, a_kc, b_kc, TILE_128x128);
         const char *why = nullptr;
@@ -1123,9 +1126,17 @@ gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32
 
 gemm_status gemm_plan_describe(gemm_plan_t pl, int64_t M, int64_t N, int64_t K, int32_t num_cus, char *buf,
                                int32_t len) {
+    return gemm_plan_describe_batched(pl, M, N, K, 1, num_cus, buf, len);
+}
+
+gemm_status gemm_plan_describe_batched(gemm_plan_t pl, int64_t M, int64_t N, int64_t K,
+                                       int64_t batch_count, int32_t num_cus, char *buf,
+                                       int32_t len) {
     if (!plan_ok(pl)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_describe: invalid plan handle");
     if (!buf || len <= 0) return fail(GEMM_INVALID_ARG, "gemm_plan_describe: empty buffer");
     if (M < 0 || N < 0 || K < 0) return fail(GEMM_INVALID_ARG, "gemm_plan_describe: negative size");
+    if (batch_count < 1 || batch_count > 0x7FFFFFFFLL)
+        return fail(GEMM_INVALID_ARG, "gemm_plan_describe: batch_count outside [1, 2^31)");
     const int cus = num_cus > 0 ? num_cus : 256;
     // aligned stand-in pointers: describes the vector-load path
     const void *fake = reinterpret_cast<const void *>(uintptr_t(1) << 20);
@@ -1135,7 +1146,7 @@ gemm_status gemm_plan_describe(gemm_plan_t pl, int64_t M, int64_t N, int64_t K, 
                                 *occ = static_occupancy(e);
                                 return GEMM_OK;
                             },
-                            d);
+                            d, batch_count);
     if (st != GEMM_OK) return st;
     snprintf(buf, (size_t)len,
              "{\"kernel\": \"%s\", \"tile\": \"%s\", \"bk\": %d, \"waves\": %d, \"schedule\": \"%s\", "

@@ -325,6 +325,14 @@ gemm_status gemm_plan_cache_import(gemm_plan_t plan, const char *json);
 int32_t gemm_plan_cache_size(gemm_plan_t plan);
 gemm_status gemm_plan_cache_clear(gemm_plan_t plan);
 
+/* gemm_plan_describe for a gemm_plan_run_batched call of batch_count
+ * problems of this shape (batch_count = 1 is gemm_plan_describe); "tiles"
+ * then counts the tiles of the whole batch. batch_count outside [1, 2^31)
+ * gives GEMM_INVALID_ARG. */
+gemm_status gemm_plan_describe_batched(gemm_plan_t plan, int64_t M, int64_t N,
+                                       int64_t K, int64_t batch_count,
+                                       int32_t num_cus, char *buf, int32_t len);
+
 /* Thread-local description of the last failure in this thread ("" if none). */
 const char *gemm_last_error(void);
 

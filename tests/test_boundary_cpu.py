@@ -388,3 +388,21 @@ def test_profile_validation_before_any_device_call():
         assert prof(*args(h, D=None, M=0)) == g.Status.OK and n.value == 0
     finally:
         g.gemm_plan_destroy(h)
+
+
+def test_describe_batched_tile_choice():
+    """A batch that supplies a full wave of 256x256 tiles gets them (the
+    single 1024^3 problem does not), and the tile count covers the batch."""
+    h = g.gemm_plan_create_simple(g.Dtype.F16, g.Layout.ROW_MAJOR, g.Epilogue.LINEAR)
+    try:
+        one = g.gemm_plan_describe_batched(h, 1024, 1024, 1024, 1)
+        assert one == g.gemm_plan_describe(h, 1024, 1024, 1024)
+        assert one["tile"] == "128x128"
+        b16 = g.gemm_plan_describe_batched(h, 1024, 1024, 1024, 16)
+        assert b16["tile"] == "256x256" and b16["tiles"] == 256
+        assert b16["schedule"] == "data_parallel"
+        assert g.gemm_plan_describe_batched(h, 64, 1024, 1024, 64)["tile"] == "64x256"
+        assert g.lib.gemm_plan_describe_batched(h, 8, 8, 8, 0, 0, ctypes.create_string_buffer(64),
+                                                64) == g.Status.INVALID_ARG
+    finally:
+        g.gemm_plan_destroy(h)
