@@ -1207,6 +1207,10 @@ gemm_status gemm_plan_profile(gemm_plan_t pl, const void *A, const void *B, cons
                             return kernel_occupancy(dev, e->fn_persistent, e->nt, occ);
                         },
                         d);
+            if (st == GEMM_UNSUPPORTED) {   // e.g. too many tiles of this shape: skip it
+                st = GEMM_OK;
+                continue;
+            }
             if (st != GEMM_OK) break;
             bool dup = false;
             for (const Cand &c : done)
