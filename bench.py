@@ -88,6 +88,7 @@ def build_fp16_relu():
     D = torch.empty_like(C)
     return [dict(name="fp16_1024_relu", p=p, flops=p.flops, plan=plan,
                  call=lambda: plan.run(A, B, C, D, p.M, p.N, p.K, 1.0, 1.0),
+                 tune=lambda: plan.profile(A, B, C, D, p.M, p.N, p.K, 1.0, 1.0, iters=20),
                  bytes=3 * 1024 * 1024 * 2 + 1024 * 1024 * 2,
                  describe=plan.describe(p.M, p.N, p.K))], "f16"
 
@@ -128,6 +129,9 @@ def build_fp8():
             items.append(dict(name=f"fp8_{M}x{N}x{K}", p=p, flops=p.flops, plan=plan,
                               call=(lambda A=A, B=B, D=D, sa=sa, sb=sb, p=p:
                                     plan.run(A, B, None, D, p.M, p.N, p.K, 1.0, 0.0, sa, sb)),
+                              tune=(lambda A=A, B=B, D=D, p=p:
+                                    plan.profile(A, B, None, D, p.M, p.N, p.K, 1.0, 0.0,
+                                                 iters=10)),
                               bytes=M * K + K * N + M * N * 2,
                               describe=plan.describe(M, N, K)))
     return items, "f8e4m3"
@@ -144,6 +148,7 @@ def build_fp32():
     D = torch.empty_like(C)
     return [dict(name="fp32_128x64x256", p=p, flops=p.flops, plan=plan,
                  call=lambda: plan.run(A, B, C, D, p.M, p.N, p.K, 1.0, 1.0),
+                 tune=lambda: plan.profile(A, B, C, D, p.M, p.N, p.K, 1.0, 1.0, iters=50),
                  bytes=4 * (128 * 256 + 256 * 64 + 2 * 128 * 64),
                  describe=plan.describe(p.M, p.N, p.K))], "f32"
 
@@ -301,6 +306,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="layer", choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tune", action="store_true",
+                    help="skip the profiler step of the small / skinny workloads")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -311,6 +318,15 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     items, dtype = build(args.workload)
+    if not args.no_tune:
+        # the library's profiler times every launch of each shape and caches
+        # the fastest in the plan (untimed; the workloads without a tune step
+        # keep the heuristics, which the profiler ranks first on them)
+        for it in items:
+            if "tune" in it:
+                it["tune"]()
+                it["describe"] = it["plan"].describe(it["p"].M, it["p"].N, it["p"].K)
+                it["describe"]["tuned"] = True
     print(f"[bench] workload {args.workload}: {len(items)} launches per step; "
           f"{[it['describe'] for it in items]}", file=sys.stderr, flush=True)
     ms, per, wall = time_steps(items, args.steps, args.warmup)
@@ -323,7 +339,8 @@ def main():
             "us": round(d * 1e3, 2), "tflops": round(it["flops"] / (d * 1e-3) / 1e12, 1),
             "pct_peak": round(100 * it["flops"] / (d * 1e-3) / 1e12 / peak, 1),
             "hbm_gbs": round(it["bytes"] / (d * 1e-3) / 1e9, 1),
-            "schedule": it["describe"].get("schedule"), "tile": it["describe"].get("tile")}
+            "schedule": it["describe"].get("schedule"), "tile": it["describe"].get("tile"),
+            "tuned": bool(it["describe"].get("tuned", False))}
     # dominant kernel: every launch of the default workload is the same kernel
     launch_flops = flops / len(items)
     launch_s = sum(per) / len(per) * 1e-3

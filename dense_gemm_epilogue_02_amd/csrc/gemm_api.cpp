@@ -425,6 +425,16 @@ gemm_tile pick_tile(int fam, int64_t M, int64_t N, int cus, int64_t batch = 1) {
     return big >= cus ? GEMM_TILE_256x256 : GEMM_TILE_128x128;
 }
 
+gemm_tile tile_enum(int id) {
+    switch (id) {
+    case TILE_256x256: return GEMM_TILE_256x256;
+    case TILE_128x128: return GEMM_TILE_128x128;
+    case TILE_64x256: return GEMM_TILE_64x256;
+    case TILE_32x256: return GEMM_TILE_32x256;
+    default: return GEMM_TILE_GENERIC;
+    }
+}
+
 int tile_id(gemm_tile t) {
     switch (t) {
     case GEMM_TILE_256x256: return TILE_256x256;
@@ -1217,9 +1227,11 @@ gemm_status gemm_plan_profile(gemm_plan_t pl, const void *A, const void *B, cons
                 dup |= c.e == d.e && c.sched == (int)d.sched && c.grid == d.grid &&
                        c.split == d.split;
             if (dup) continue;
-            // the resolved choice, so a cached entry reproduces this launch
+            // the resolved choice (the registry may fall back to another
+            // tile), so the report names what ran and a cached entry
+            // reproduces this launch
             pl->sched = d.sched;
-            pl->tile = d.e ? t : GEMM_TILE_GENERIC;
+            pl->tile = d.e ? tile_enum(d.e->tile) : GEMM_TILE_GENERIC;
             st = run_one(pl, A, B, C, D, M, N, K, alpha, beta, nullptr, nullptr, nullptr, stream);
             if (st == GEMM_OK) he = hipEventRecord(ev[0], hs);
             for (int32_t r = 0; r < iters && st == GEMM_OK && he == hipSuccess; ++r)

@@ -74,3 +74,49 @@ def test_imported_cache_drives_runs_and_results_stay_exact():
     torch.cuda.synchronize()
     acceptance.check_exact(D.float().cpu().double().numpy(), oracle.gemm(p).d_exact, "cached")
     plan.close()
+
+
+@pytest.mark.parametrize("which", ["fp32_128x64x256", "fp16_1024_relu", "fp8_16x8192x28672",
+                                   "bf16_16x8192x28672"])
+def test_tuned_configuration_matches_oracle(which):
+    """The benchmark tunes these shapes with the profiler before timing; the
+    configuration it caches must pass the same parity bar (full output for
+    the small ones, sampled for the skinny ones)."""
+    relu = which == "fp16_1024_relu"
+    if which == "fp32_128x64x256":
+        p = syn.config1()
+    elif which == "fp16_1024_relu":
+        p = syn.config2()
+    elif which.startswith("fp8"):
+        p = syn.config5(16, 8192, 28672)
+    else:
+        p = syn.make_problem(16, 8192, 28672, dtype_ab="bf16", dtype_cd="bf16", lb="col",
+                             std_b=0.02, seed=152)
+    plan = g.Plan(p.dtype_ab, p.dtype_cd, p.la, p.lb, p.lc, relu=relu)
+    A, B = p.A.to(DEV), p.B.to(DEV)
+    C = p.C.to(DEV) if p.C is not None else None
+    D = torch.empty((p.M, p.N) if p.lc == "row" else (p.N, p.M),
+                    dtype=syn.TORCH_DTYPE[p.dtype_cd], device=DEV)
+    sa = sb = None
+    if p.dtype_ab == "f8e4m3":
+        sa = torch.tensor([p.scale_a], dtype=torch.float32, device=DEV)
+        sb = torch.tensor([p.scale_b], dtype=torch.float32, device=DEV)
+    print(f"[gpu] tune {which}", flush=True)
+    res = plan.profile(A, B, C, D, p.M, p.N, p.K, p.alpha, p.beta, iters=5)
+    best = res[0]
+    print(f"[gpu] tuned {which}: {best} -> {plan.describe(p.M, p.N, p.K)}", flush=True)
+    D.fill_(float("nan"))
+    plan.run(A, B, C, D, p.M, p.N, p.K, p.alpha, p.beta, sa, sb)
+    torch.cuda.synchronize()
+    got = D.float().cpu().double().numpy()
+    plan.close()
+    if p.M * p.N <= 1 << 20:
+        r = oracle.gemm(p, relu=relu)
+        acceptance.check_close(got, r.ref, r.S, p.dtype_ab, p.dtype_cd, which)
+    else:
+        rng = np.random.default_rng(153)
+        ii, jj = rng.integers(0, p.M, 96), rng.integers(0, p.N, 96)
+        ii[:2], jj[:2] = (0, p.M - 1), (0, p.N - 1)
+        r = oracle.gemm_entries(p, ii, jj, relu=relu)
+        acceptance.check_close(got[ii, jj], r.ref, r.S, p.dtype_ab, p.dtype_cd, which)
+    assert np.isfinite(got).all()
