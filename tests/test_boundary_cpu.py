@@ -406,3 +406,14 @@ def test_describe_batched_tile_choice():
                                                 64) == g.Status.INVALID_ARG
     finally:
         g.gemm_plan_destroy(h)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU; --gpus N > 1 exits with a message
+    (before touching any device)."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
