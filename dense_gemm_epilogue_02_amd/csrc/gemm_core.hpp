@@ -1023,7 +1023,9 @@ struct Tile {
                         const float x =
                             e.aux ? (float)reinterpret_cast<const Out *>(e.aux)[idx] : 0.0f;
                         float z;
-                        D[idx] = (Out)finish_aux(v, x, e, z);
+                        D[idx] = (Out)finish_aux_branch(v, x, e.aux_op, e.act,
+                                                        e.aux && !e.aux_after,
+                                                        e.aux && e.aux_after, z);
                         if (e.aux_out) reinterpret_cast<Out *>(e.aux_out)[idx] = (Out)z;
                     }
         }
