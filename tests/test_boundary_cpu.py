@@ -417,3 +417,48 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_config_cache_import_survives_random_mutations():
+    """Random byte edits, truncations and duplications of a valid cache text:
+    the importer returns OK, INVALID_ARG or UNSUPPORTED and never crashes; a
+    failed import leaves the cache as it was."""
+    import random
+    D, L, E = g.Dtype, g.Layout, g.Epilogue
+    h = g.gemm_plan_create(D.BF16, D.BF16, D.BF16, D.BF16, D.F32, L.ROW_MAJOR, L.COL_MAJOR,
+                           L.ROW_MAJOR, E.LINEAR)
+    try:
+        base = _cache_doc([{"m": 4096, "n": 8192, "k": 8192, "mx": 0, "schedule": "stream_k",
+                            "tile": "128x128", "sk_grid": 0, "us": 500.0},
+                           {"m": 1, "n": 2, "k": 3, "schedule": "hybrid", "tile": "64x256"}])
+        rng = random.Random(9)
+        alphabet = '{}[]:,"\\0123456789.eE+-truefalsn x\t\n'
+        ok = bad = 0
+        for trial in range(3000):
+            s = list(base)
+            for _ in range(rng.randint(1, 4)):
+                kind = rng.randrange(4)
+                pos = rng.randrange(len(s) + 1)
+                if kind == 0 and s:
+                    s[min(pos, len(s) - 1)] = rng.choice(alphabet)
+                elif kind == 1:
+                    s.insert(pos, rng.choice(alphabet))
+                elif kind == 2 and s:
+                    del s[min(pos, len(s) - 1)]
+                else:
+                    s = s[:pos]
+            text = "".join(s)
+            before = g.gemm_plan_cache_export(h)
+            st = g.lib.gemm_plan_cache_import(h, text.encode())
+            assert st in (g.Status.OK, g.Status.INVALID_ARG, g.Status.UNSUPPORTED), (st, text)
+            if st == g.Status.OK:
+                ok += 1
+                g.gemm_plan_cache_clear(h)
+            else:
+                bad += 1
+                assert g.gemm_plan_cache_export(h) == before
+        assert bad > 0
+        # deeply nested input is rejected, not recursed into without bound
+        assert g.lib.gemm_plan_cache_import(h, ("[" * 100000).encode()) == g.Status.INVALID_ARG
+    finally:
+        g.gemm_plan_destroy(h)
