@@ -6,7 +6,8 @@
 // D = alpha*A*B + beta*C with an fp32 accumulator; section 7.2: misaligned
 // data still works, only slower): each element is loaded on its own (64-bit
 // addressing), decoded to fp32, staged in LDS, and accumulated with fp32 FMA
-// in increasing k.
+// in increasing k. The raw loads of the next few k-steps stay in flight while
+// one is multiplied.
 #include "kernels.hpp"
 
 namespace mg {
@@ -16,20 +17,8 @@ namespace {
 constexpr int GT = 64;    // output tile edge
 constexpr int GK = 16;    // k per step
 
-template <int FAM> __device__ __forceinline__ float ld_elem(const char *base, int64_t idx);
-
-template <> __device__ __forceinline__ float ld_elem<FAM_F32>(const char *base, int64_t idx) {
-    return reinterpret_cast<const float *>(base)[idx];
-}
-template <> __device__ __forceinline__ float ld_elem<FAM_F16>(const char *base, int64_t idx) {
-    return (float)reinterpret_cast<const _Float16 *>(base)[idx];
-}
-template <> __device__ __forceinline__ float ld_elem<FAM_BF16>(const char *base, int64_t idx) {
-    return (float)reinterpret_cast<const __bf16 *>(base)[idx];
-}
 // OCP E4M3: sign, 4-bit exponent (bias 7), 3-bit fraction, S.1111.111 = NaN.
-template <> __device__ __forceinline__ float ld_elem<FAM_F8>(const char *base, int64_t idx) {
-    const uint32_t u = reinterpret_cast<const uint8_t *>(base)[idx];
+__device__ __forceinline__ float decode_e4m3(uint32_t u) {
     const uint32_t s = (u & 0x80u) << 24, e = (u >> 3) & 15u, m = u & 7u;
     if (e == 15u && m == 7u) return __builtin_nanf("");
     float v;
@@ -37,7 +26,6 @@ template <> __device__ __forceinline__ float ld_elem<FAM_F8>(const char *base, i
     else v = __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
     return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) | s);
 }
-
 // OCP MX E8M0 scale: 2^(c-127); c = 0 is the fp32 subnormal 2^-127, 255 is NaN.
 __device__ __forceinline__ float e8m0(uint32_t c) {
     if (c == 255u) return __builtin_nanf("");
@@ -51,9 +39,36 @@ template <> struct OutT<FAM_BF16> { using T = __bf16; };
 template <> struct OutT<FAM_F8> { using T = __bf16; };
 template <> struct OutT<FAM_MXF8> { using T = __bf16; };
 
+// Raw storage bits of one element (decoded only when staged into LDS, so
+// the loads of several k-steps can be in flight at once).
+template <int FAM> struct RawT;
+template <> struct RawT<FAM_F32> { using T = uint32_t; };
+template <> struct RawT<FAM_F16> { using T = uint16_t; };
+template <> struct RawT<FAM_BF16> { using T = uint16_t; };
+template <> struct RawT<FAM_F8> { using T = uint8_t; };
+
+template <int FAM> __device__ __forceinline__ float decode_raw(uint32_t bits);
+template <> __device__ __forceinline__ float decode_raw<FAM_F32>(uint32_t b) {
+    return __builtin_bit_cast(float, b);
+}
+template <> __device__ __forceinline__ float decode_raw<FAM_F16>(uint32_t b) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+template <> __device__ __forceinline__ float decode_raw<FAM_BF16>(uint32_t b) {
+    return __builtin_bit_cast(float, b << 16);
+}
+template <> __device__ __forceinline__ float decode_raw<FAM_F8>(uint32_t b) {
+    return decode_e4m3(b & 0xFFu);
+}
+
+// k-steps whose loads are in flight ahead of the one being multiplied.
+constexpr int GPF = 4;
+
 template <int FAM>
 __global__ void __launch_bounds__(256) gemm_generic(GenericArgs a) {
     using Out = typename OutT<FAM>::T;
+    constexpr int LF = FAM == FAM_MXF8 ? FAM_F8 : FAM;   // element decoder
+    using Raw = typename RawT<LF>::T;
     __shared__ float As[GK][GT + 1];
     __shared__ float Bs[GK][GT + 1];
     const Prob &p = a.p;
@@ -61,41 +76,69 @@ __global__ void __launch_bounds__(256) gemm_generic(GenericArgs a) {
     const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * GT;
     const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * GT;
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const Raw *Ar = reinterpret_cast<const Raw *>(p.A);
+    const Raw *Br = reinterpret_cast<const Raw *>(p.B);
     float acc[4][4] = {};
-    for (int64_t k0 = 0; k0 < p.K; k0 += GK) {
+    // ring of GPF k-steps of raw operand bits (and MX block-scale codes):
+    // slot u holds step s with s % GPF == u; out-of-range elements are 0
+    uint32_t ra[GPF][4], rb[GPF][4], xa[GPF][4], xb[GPF][4];
+    auto fetch = [&](int64_t k0, uint32_t (&va)[4], uint32_t (&vb)[4], uint32_t (&sa)[4],
+                     uint32_t (&sb)[4]) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int e = tid + u * 256;      // 0 .. 1023
             const int kk = e / GT, rr = e % GT;
             const int64_t k = k0 + kk;
             const int64_t m = m0 + rr, n = n0 + rr;
-            float av = 0.0f, bv = 0.0f;
-            constexpr int LF = FAM == FAM_MXF8 ? FAM_F8 : FAM;   // element decoder
-            if (k < p.K && m < p.M) av = ld_elem<LF>(p.A, a.la_row ? m * p.K + k : m + k * p.M);
-            if (k < p.K && n < p.N) bv = ld_elem<LF>(p.B, a.lb_row ? k * p.N + n : k + n * p.K);
+            const bool ina = k < p.K && m < p.M, inb = k < p.K && n < p.N;
+            va[u] = ina ? (uint32_t)Ar[a.la_row ? m * p.K + k : m + k * p.M] : 0u;
+            vb[u] = inb ? (uint32_t)Br[a.lb_row ? k * p.N + n : k + n * p.K] : 0u;
             if constexpr (FAM == FAM_MXF8) {
-                // block scales of A's row m and B's column n (K % 32 == 0);
-                // a power of two, so the scaled element is exact
-                if (k < p.K && m < p.M) av *= e8m0(p.mx_a[m * (p.K >> 5) + (k >> 5)]);
-                if (k < p.K && n < p.N) bv *= e8m0(p.mx_b[n * (p.K >> 5) + (k >> 5)]);
+                sa[u] = ina ? (uint32_t)p.mx_a[m * (p.K >> 5) + (k >> 5)] : 127u;
+                sb[u] = inb ? (uint32_t)p.mx_b[n * (p.K >> 5) + (k >> 5)] : 127u;
             }
-            As[kk][rr] = av;
-            Bs[kk][rr] = bv;
         }
-        __syncthreads();
+    };
+    const int64_t steps = (p.K + GK - 1) / GK;
 #pragma unroll
-        for (int kk = 0; kk < GK; ++kk) {
-            float x[4], y[4];
+    for (int u = 0; u < GPF; ++u)
+        if (u < steps) fetch((int64_t)u * GK, ra[u], rb[u], xa[u], xb[u]);
+    for (int64_t s0 = 0; s0 < steps; s0 += GPF) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = As[kk][ty * 4 + i];
+        for (int u = 0; u < GPF; ++u) {
+            const int64_t s = s0 + u;
+            if (s >= steps) break;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) y[j] = Bs[kk][tx * 4 + j];
+            for (int w = 0; w < 4; ++w) {
+                const int e = tid + w * 256;
+                const int kk = e / GT, rr = e % GT;
+                float av = decode_raw<LF>(ra[u][w]), bv = decode_raw<LF>(rb[u][w]);
+                if constexpr (FAM == FAM_MXF8) {
+                    // block scales of A's row and B's column (K % 32 == 0); a
+                    // power of two, so the scaled element is exact
+                    av *= e8m0(xa[u][w]);
+                    bv *= e8m0(xb[u][w]);
+                }
+                As[kk][rr] = av;
+                Bs[kk][rr] = bv;
+            }
+            __syncthreads();
+            // refill this slot with step s + GPF while step s is multiplied
+            if (s + GPF < steps) fetch((s + GPF) * GK, ra[u], rb[u], xa[u], xb[u]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int kk = 0; kk < GK; ++kk) {
+                float x[4], y[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(x[i], y[j], acc[i][j]);
+                for (int i = 0; i < 4; ++i) x[i] = As[kk][ty * 4 + i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) y[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(x[i], y[j], acc[i][j]);
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
     float alpha = a.e.alpha;
     if (a.e.scale_a) alpha *= *a.e.scale_a;
