@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -393,6 +394,7 @@ struct Decision {
     gemm_schedule sched = GEMM_SCHED_DATA_PARALLEL;
     int tiles_m = 0, tiles_n = 0, ipt = 0, total = 0, grid = 0, sk_tiles = 0, split = 0;
     int64_t sk_iters = 0;
+    int sk_grid = 0;   // workgroups sharing the stream-K iterations (<= grid, <= sk_iters)
     int group_m = 4;
     int vec_cd = 0;
     const char *why_generic = "";
@@ -590,6 +592,7 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
         if (cfg.sk_grid <= 0 && g > cus) g = cus;   // one stream-K workgroup per CU
         if (g < d.total && cfg.sk_grid <= 0) g = d.total < G ? d.total : G;
         d.grid = (int)(g > 0 ? g : 1);
+        d.sk_grid = d.grid;   // g <= sk_iters in every branch above
         break;
     }
     case GEMM_SCHED_SPLIT_K: {
@@ -606,8 +609,16 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
         d.sk_tiles = d.total % G;
         d.sk_iters = (int64_t)d.sk_tiles * d.ipt;
         d.grid = G;
+        // the remainder's iterations may be fewer than the grid: only as many
+        // workgroups as there are iterations share them, so none holds an
+        // empty range that its tile's arrival count would wait for
+        d.sk_grid = (int)(d.sk_iters < G ? d.sk_iters : G);
         break;
     }
+    if (d.sk_tiles > 0 && d.split == 0 &&
+        (d.sk_grid < 1 || d.sk_grid > d.grid || (int64_t)d.sk_grid > d.sk_iters))
+        return fail(GEMM_HIP_ERROR, "internal: stream-K grid %d outside [1, min(grid %d, iterations %lld)]",
+                    d.sk_grid, d.grid, (long long)d.sk_iters);
     return GEMM_OK;
 }
 
@@ -812,6 +823,7 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
     a.s.total_tiles = d.total;
     a.s.sk_tiles = d.sk_tiles;
     a.s.sk_iters = d.sk_iters;
+    a.s.sk_grid = d.sk_grid;
     a.s.group_m = d.group_m;
     a.s.xcd_remap = 1;
     a.s.split = d.split;
@@ -827,6 +839,63 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
     if (e != hipSuccess) return hip_fail(e, "tile kernel launch");
     note_stream(pl, hs);
     return ok();
+}
+
+// Output element (kind 0: fp32, 1: fp16, 2: bf16) as a double.
+double out_value(const uint8_t *p, int kind) {
+    if (kind == 0) {
+        float f;
+        memcpy(&f, p, 4);
+        return f;
+    }
+    uint16_t h;
+    memcpy(&h, p, 2);
+    if (kind == 2) {
+        const uint32_t w = (uint32_t)h << 16;
+        float f;
+        memcpy(&f, &w, 4);
+        return f;
+    }
+    const int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v = e == 0 ? std::ldexp((double)m, -24)
+               : e == 31 ? (m ? NAN : INFINITY)
+                         : std::ldexp((double)(m | 1024), e - 25);
+    return sign ? -v : v;
+}
+
+// Two launches' outputs agree up to the order of the fp32 sums: the same
+// elements are non-finite, and the finite ones differ by at most 4 units of
+// the output's precision plus 1 % of the reference's root mean square (a
+// stream-K partial that is lost or added twice moves an element by the size
+// of a whole k-range's contribution, far beyond that). *bad: first mismatch.
+bool outputs_agree(const std::vector<uint8_t> &ref, const std::vector<uint8_t> &got, int kind,
+                   int64_t *bad) {
+    const int sz = kind == 0 ? 4 : 2;
+    const int64_t n = (int64_t)(ref.size() / sz);
+    const double rel = kind == 0 ? 0x1p-22 : kind == 1 ? 0x1p-9 : 0x1p-6;   // 4 ulp (relative)
+    double ss = 0.0;
+    int64_t nf = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const double r = out_value(&ref[(size_t)i * sz], kind);
+        if (std::isfinite(r)) {
+            ss += r * r;
+            ++nf;
+        }
+    }
+    const double tol_abs = nf ? 0.01 * std::sqrt(ss / (double)nf) : 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        const double r = out_value(&ref[(size_t)i * sz], kind);
+        const double g = out_value(&got[(size_t)i * sz], kind);
+        const bool fr = std::isfinite(r), fg = std::isfinite(g);
+        bool okv = fr == fg;
+        if (okv && fr) okv = std::fabs(g - r) <= rel * std::fabs(r) + tol_abs;
+        if (okv && !fr) okv = std::isnan(r) == std::isnan(g) && (std::isnan(r) || r == g);
+        if (!okv) {
+            *bad = i;
+            return false;
+        }
+    }
+    return true;
 }
 
 }  // namespace
@@ -1161,9 +1230,10 @@ gemm_status gemm_plan_describe_batched(gemm_plan_t pl, int64_t M, int64_t N, int
     snprintf(buf, (size_t)len,
              "{\"kernel\": \"%s\", \"tile\": \"%s\", \"bk\": %d, \"waves\": %d, \"schedule\": \"%s\", "
              "\"tiles\": %d, \"ipt\": %d, \"sk_tiles\": %d, \"split\": %d, \"grid\": %d, "
-             "\"generic_reason\": \"%s\"}",
+             "\"sk_grid\": %d, \"sk_iters\": %lld, \"generic_reason\": \"%s\"}",
              d.e ? "tile" : "generic", tile_name(d.e), d.e ? d.e->bk : 16, d.e ? d.e->nt / 64 : 4,
-             sched_name(d.sched), d.total, d.ipt, d.sk_tiles, d.split, d.grid, d.why_generic);
+             sched_name(d.sched), d.total, d.ipt, d.sk_tiles, d.split, d.grid, d.sk_grid,
+             (long long)d.sk_iters, d.why_generic);
     return ok();
 }
 
@@ -1201,6 +1271,8 @@ gemm_status gemm_plan_profile(gemm_plan_t pl, const void *A, const void *B, cons
         if (ev[0]) (void)hipEventDestroy(ev[0]);
         return hip_fail(he, "gemm_plan_profile: hipEventCreate");
     }
+    const int osz = out_bytes(pl->fam);
+    std::vector<uint8_t> ref((size_t)(M * N) * osz), got((size_t)(M * N) * osz);
     const gemm_tile tiles[] = {GEMM_TILE_256x256, GEMM_TILE_128x128, GEMM_TILE_64x256,
                                GEMM_TILE_32x256, GEMM_TILE_GENERIC};
     const gemm_schedule scheds[] = {GEMM_SCHED_DATA_PARALLEL, GEMM_SCHED_STREAM_K,
@@ -1232,7 +1304,31 @@ gemm_status gemm_plan_profile(gemm_plan_t pl, const void *A, const void *B, cons
             // reproduces this launch
             pl->sched = d.sched;
             pl->tile = d.e ? tile_enum(d.e->tile) : GEMM_TILE_GENERIC;
+            // the untimed run writes into a NaN-filled D, and its result must
+            // match the first candidate's (up to summation order) before this
+            // launch may be timed and cached: an output the launch fails to
+            // write, or gets wrong, fails loudly instead of timing fast
+            he = hipMemsetAsync(D, 0xFF, (size_t)(M * N) * osz, hs);
+            if (he != hipSuccess) break;
             st = run_one(pl, A, B, C, D, M, N, K, alpha, beta, nullptr, nullptr, nullptr, stream);
+            if (st == GEMM_OK) {
+                he = hipMemcpyAsync(done.empty() ? ref.data() : got.data(), D, (size_t)(M * N) * osz,
+                                    hipMemcpyDeviceToHost, hs);
+                if (he == hipSuccess) he = hipStreamSynchronize(hs);
+                if (he != hipSuccess) break;
+                if (!done.empty()) {
+                    int64_t bad = -1;
+                    if (!outputs_agree(ref, got, osz == 4 ? 0 : pl->d == GEMM_F16 ? 1 : 2, &bad)) {
+                        const int64_t i = pl->lc == GEMM_ROW_MAJOR ? bad / N : bad % M;
+                        const int64_t j = pl->lc == GEMM_ROW_MAJOR ? bad % N : bad / M;
+                        st = fail(GEMM_HIP_ERROR,
+                                  "gemm_plan_profile: %s %s (grid %d) disagrees with %s %s at D[%lld][%lld]",
+                                  tile_name(d.e), sched_name(d.sched), d.grid, tile_name(done[0].e),
+                                  sched_name((gemm_schedule)done[0].sched), (long long)i, (long long)j);
+                        break;
+                    }
+                }
+            }
             if (st == GEMM_OK) he = hipEventRecord(ev[0], hs);
             for (int32_t r = 0; r < iters && st == GEMM_OK && he == hipSuccess; ++r)
                 st = run_one(pl, A, B, C, D, M, N, K, alpha, beta, nullptr, nullptr, nullptr,

@@ -256,6 +256,12 @@ struct Sched {
     int total_tiles;
     int sk_tiles;
     int64_t sk_iters;       // sk_tiles * ipt
+    // Workgroups that share the stream-K iterations: virtual ids [0, sk_grid),
+    // with 1 <= sk_grid <= min(grid, sk_iters) so that every one of them owns a
+    // non-empty range (a tile's expected arrivals count every id between the
+    // owners of its first and last iteration). Ids >= sk_grid go straight to
+    // the data-parallel tiles.
+    int sk_grid;
     int group_m;            // raster: tile rows per swizzle group
     int xcd_remap;          // map consecutive virtual ids onto one XCD
     int split;              // > 0: interleaved split-K, `split` units per tile
@@ -1270,9 +1276,9 @@ gemm_persistent(KArgs a) {
         return;
     }
 
-    if (s.sk_tiles > 0 && p.ipt > 0) {
+    if (s.sk_tiles > 0 && p.ipt > 0 && v < s.sk_grid) {
         const int64_t T = s.sk_iters;
-        const int G = s.grid;
+        const int G = s.sk_grid;
         int64_t it = (int64_t)v * T / G;
         const int64_t end = (int64_t)(v + 1) * T / G;
         const int first_tile = (int)(it / p.ipt);

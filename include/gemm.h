@@ -43,6 +43,13 @@
  *   - Any pointer alignment and any size are accepted; operands whose base
  *     address or contiguous extent do not allow 16-byte vector loads run on a
  *     slower, scalar-load kernel with the same arithmetic contract.
+ *   - A plan owns one device workspace (stream-K / split-K partial tiles and
+ *     their arrival counters, the grouped descriptor table) that every run
+ *     call of the plan shares. A plan must therefore not run on two streams
+ *     at once, for any run call: two overlapping runs of one plan race on
+ *     the workspace (wrong D, counters left dirty). Create one plan per
+ *     stream for concurrent work. Consecutive runs on one stream, or on
+ *     different streams ordered by events, are fine.
  */
 #ifndef MI355_GEMM_H
 #define MI355_GEMM_H
@@ -294,7 +301,14 @@ typedef struct {
  * `results` and their total count to *n_results (either may be NULL/0), and
  * records the fastest in the plan's configuration cache, which later runs of
  * exactly this M x N x K use whenever the plan has no gemm_plan_set_config
- * override (batched calls and MX runs keep the heuristics). D is
+ * override (batched calls and MX runs keep the heuristics). Before a
+ * launch is timed, its untimed run writes into a NaN-filled D whose copy is
+ * compared with the first launch's result: the same elements non-finite,
+ * the finite ones within 4 output ulp plus 1 % of the result's root mean
+ * square (the launches differ only in the order of their fp32 sums). A
+ * launch that disagrees makes the call fail with GEMM_HIP_ERROR naming it
+ * and the first differing element, and nothing is cached. The check copies
+ * D to host memory (2 * M * N output elements of host buffers). D is
  * overwritten (it holds the last run's result); D == C with beta != 0
  * gives GEMM_INVALID_ARG. iters outside [1, 100000] gives GEMM_INVALID_ARG.
  * Operands follow gemm_plan_run's rules. */

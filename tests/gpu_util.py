@@ -93,3 +93,50 @@ def run(p, relu=False, schedule=g.Schedule.AUTO, tile=g.Tile.AUTO, sk_grid=0, pl
     if own:
         plan.close()
     return out
+
+
+def block_samples(M, N, seed, block=32):
+    """One output entry inside every block x block block of an M x N output
+    (a uniformly random position, clipped to the ragged edge), plus the four
+    corners of D. 32 x 32 is the MFMA block every tile shape is built from,
+    so every tile of every schedule, and every wave's fragment of it, is
+    sampled. Returns (ii, jj) index arrays."""
+    rng = np.random.default_rng(seed)
+    bi = np.arange(0, M, block)
+    bj = np.arange(0, N, block)
+    I0, J0 = np.meshgrid(bi, bj, indexing="ij")
+    hi_i = np.minimum(block, M - I0)
+    hi_j = np.minimum(block, N - J0)
+    ii = (I0 + (rng.random(I0.shape) * hi_i).astype(np.int64)).ravel()
+    jj = (J0 + (rng.random(J0.shape) * hi_j).astype(np.int64)).ravel()
+    ii = np.concatenate([ii, [0, 0, M - 1, M - 1]])
+    jj = np.concatenate([jj, [0, N - 1, 0, N - 1]])
+    return ii, jj
+
+
+def tile_corner_samples(M, N, bm, bn):
+    """The four corners of every bm x bn output tile (the first and last
+    rows and columns a tile's waves write)."""
+    ti = np.arange(0, M, bm)
+    tj = np.arange(0, N, bn)
+    rows = np.stack([ti, np.minimum(ti + bm, M) - 1], 1)
+    cols = np.stack([tj, np.minimum(tj + bn, N) - 1], 1)
+    ii, jj = [], []
+    for a in range(2):
+        for b in range(2):
+            I, J = np.meshgrid(rows[:, a], cols[:, b], indexing="ij")
+            ii.append(I.ravel())
+            jj.append(J.ravel())
+    return np.concatenate(ii), np.concatenate(jj)
+
+
+def full_size_samples(M, N, seed, describe=None):
+    """block_samples plus the corners of every tile of the launch that
+    `describe` names (a gemm_plan_describe dict)."""
+    ii, jj = block_samples(M, N, seed)
+    if describe and describe.get("kernel") == "tile":
+        bm, bn = (int(x) for x in describe["tile"].split("x"))
+        ci, cj = tile_corner_samples(M, N, bm, bn)
+        ii = np.concatenate([ii, ci])
+        jj = np.concatenate([jj, cj])
+    return ii, jj

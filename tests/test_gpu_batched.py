@@ -17,7 +17,7 @@ import dense_gemm_epilogue_02_amd as g
 import oracle
 from oracle import acceptance
 import synthetic as syn
-from gpu_util import DEV, SENTINEL, logical, scales
+from gpu_util import DEV, SENTINEL, full_size_samples, logical, scales
 
 pytestmark = pytest.mark.gpu
 S, T = g.Schedule, g.Tile
@@ -202,10 +202,11 @@ def test_batched_in_place_sixteen_entries():
     close_all(outs, probs, what="in place x16")
 
 
-def test_batched16_fp16_1024_full_size_sampled():
+def test_batched16_fp16_1024_full_size_every_block():
     """The benchmark's batched configuration (16 x fp16 1024^3, strides M*K,
-    K*N, 0, M*N, beta 0, the same seeds), in the launch bench.py times;
-    64 sampled outputs per entry against the oracle."""
+    K*N, 0, M*N, beta 0, the same seeds), in the launch bench.py times: every
+    entry fully written, and one oracle entry in every 32 x 32 block of every
+    entry plus the corners of every tile."""
     M = N = K = 1024
     nb = 16
     probs = [syn.make_problem(M, N, K, dtype_ab="f16", dtype_cd="f16", seed=200 + b)
@@ -214,15 +215,14 @@ def test_batched16_fp16_1024_full_size_sampled():
     B = torch.stack([q.B for q in probs]).to(DEV)
     D = torch.full((nb, M, N), float("nan"), dtype=torch.float16, device=DEV)
     plan = g.Plan("f16", la="row", lb="row", lc="row")
-    print(f"[gpu] batched16 full size {plan.describe(M, N, K)}", flush=True)
+    d = plan.describe_batched(M, N, K, nb)
+    print(f"[gpu] batched16 full size {d}", flush=True)
     plan.run_batched(A, B, None, D, M, N, K, nb, (M * K, K * N, 0, M * N))
     torch.cuda.synchronize()
     plan.close()
-    rng = np.random.default_rng(73)
-    for b in (0, 7, 15):
-        ii, jj = rng.integers(0, M, 64), rng.integers(0, N, 64)
-        ii[:2], jj[:2] = (0, M - 1), (0, N - 1)
+    assert bool(torch.isfinite(D).all())
+    for b in range(nb):
+        ii, jj = full_size_samples(M, N, 73 + b, d)
         r = oracle.gemm_entries(probs[b], ii, jj)
         got = D[b].float().cpu().double().numpy()[ii, jj]
         acceptance.check_close(got, r.ref, r.S, "f16", "f16", f"batched16 entry {b}")
-    assert bool(torch.isfinite(D).all())

@@ -13,7 +13,7 @@ import dense_gemm_epilogue_02_amd as g
 import oracle
 from oracle import acceptance
 import synthetic as syn
-from gpu_util import DEV, check_guards, logical, make_out
+from gpu_util import DEV, check_guards, full_size_samples, logical, make_out
 
 pytestmark = pytest.mark.gpu
 S, T = g.Schedule, g.Tile
@@ -105,13 +105,13 @@ def test_mx_wide_scale_range_close():
 def test_mx_full_size_sampled(M, N, K):
     p = syn.make_mx_problem(M, N, K, seed=97, std_b=0.02)
     got = run_mx(p)
-    rng = np.random.default_rng(98)
-    ii = rng.integers(0, M, 64)
-    jj = rng.integers(0, N, 64)
-    ii[:2], jj[:2] = (0, M - 1), (0, N - 1)
-    r = oracle.gemm_entries(p, ii, jj)
-    acceptance.check_close(got[ii, jj], r.ref, r.S, "f8e4m3", "bf16", f"{M}x{N}x{K} sampled")
     assert np.isfinite(got).all()
+    plan = g.Plan("f8e4m3", "bf16", "row", "col", "row")
+    d = plan.describe(M, N, K)
+    plan.close()
+    ii, jj = full_size_samples(M, N, 98, d)
+    r = oracle.gemm_entries(p, ii, jj)
+    acceptance.check_close(got[ii, jj], r.ref, r.S, "f8e4m3", "bf16", f"{M}x{N}x{K} every block")
 
 
 def test_mx_nan_scale_gives_nan_row_and_column():
@@ -145,10 +145,11 @@ def test_mx_layer_bench_inputs_sampled():
     plan.close()
     p = syn.Problem(M, N, K, A.cpu(), B.cpu(), None, 1.0, 0.0, None, None, "f8e4m3", "bf16",
                     "row", "col", "row", None, xa.cpu(), xb.cpu())
-    rng = np.random.default_rng(101)
-    ii, jj = rng.integers(0, M, 96), rng.integers(0, N, 96)
-    ii[:2], jj[:2] = (0, M - 1), (0, N - 1)
+    assert bool(torch.isfinite(D).all())
+    plan = g.Plan("f8e4m3", "bf16", "row", "col", "row")
+    d = plan.describe(M, N, K)
+    plan.close()
+    ii, jj = full_size_samples(M, N, 101, d)
     r = oracle.gemm_entries(p, ii, jj)
     got = D.float().cpu().double().numpy()[ii, jj]
-    acceptance.check_close(got, r.ref, r.S, "f8e4m3", "bf16", "mx layer qkv sampled")
-    assert bool(torch.isfinite(D).all())
+    acceptance.check_close(got, r.ref, r.S, "f8e4m3", "bf16", "mx layer qkv every block")

@@ -16,7 +16,7 @@ import dense_gemm_epilogue_02_amd as g
 import oracle
 from oracle import acceptance
 import synthetic as syn
-from gpu_util import DEV, device_operands, logical, make_out, run, scales
+from gpu_util import (DEV, device_operands, full_size_samples, logical, make_out, run, scales)
 
 pytestmark = pytest.mark.gpu
 
@@ -87,44 +87,46 @@ def test_config2_schedules(sched):
     close(run(p, relu=True, schedule=sched), p, relu=True, what=f"fp16 512^3 {sched.name}")
 
 
-def _sample(M, N, n, seed):
-    rng = np.random.default_rng(seed)
-    ii = rng.integers(0, M, n)
-    jj = rng.integers(0, N, n)
-    # always include the four corners (first/last tiles, ragged edges)
-    ii = np.concatenate([ii, [0, 0, M - 1, M - 1]])
-    jj = np.concatenate([jj, [0, N - 1, 0, N - 1]])
-    return ii, jj
+def describe_of(p, relu=False):
+    """What a run of p would launch (host-only; the heuristics' choice)."""
+    plan = g.Plan(p.dtype_ab, p.dtype_cd, p.la, p.lb, p.lc, relu)
+    try:
+        return plan.describe(p.M, p.N, p.K)
+    finally:
+        plan.close()
+
+
+def check_full_size(got, p, seed, what):
+    """Every output written (D starts as NaN), and one oracle entry in every
+    32 x 32 block plus the corners of every tile compared."""
+    assert np.isfinite(got).all(), f"{what}: unwritten (NaN) outputs"
+    ii, jj = full_size_samples(p.M, p.N, seed, describe_of(p))
+    r = oracle.gemm_entries(p, ii, jj)
+    acceptance.check_close(got[ii, jj], r.ref, r.S, p.dtype_ab, p.dtype_cd, what)
+    return len(ii)
 
 
 @pytest.mark.parametrize("name", ["qkv", "o", "down", "gate_up"])
-def test_config4_layer_gemm_sampled(name):
+def test_config4_layer_gemm_every_block(name):
     p = syn.config4(name)
     got = run(p)
-    assert np.isfinite(got).all()
-    ii, jj = _sample(p.M, p.N, 256, 1)
-    r = oracle.gemm_entries(p, ii, jj)
-    acceptance.check_close(got[ii, jj], r.ref, r.S, "bf16", "bf16", f"layer {name}")
+    n = check_full_size(got, p, 1, f"layer {name}")
+    assert n >= (p.M // 32) * (p.N // 32)
 
 
-def test_config4_row_major_b_sampled():
+def test_config4_row_major_b_every_block():
     p = syn.config4("o", lb="row")
     got = run(p)
-    ii, jj = _sample(p.M, p.N, 256, 2)
-    r = oracle.gemm_entries(p, ii, jj)
-    acceptance.check_close(got[ii, jj], r.ref, r.S, "bf16", "bf16", "layer o, RowMajor B")
+    check_full_size(got, p, 2, "layer o, RowMajor B")
 
 
 @pytest.mark.parametrize("M", syn.DECODE_MS)
 @pytest.mark.parametrize("NK", syn.DECODE_NK)
-def test_config5_fp8_sampled(M, NK):
+def test_config5_fp8_every_block(M, NK):
     N, K = NK
     p = syn.config5(M, N, K)
     got = run(p)
-    assert np.isfinite(got).all()
-    ii, jj = _sample(M, N, 256, 3)
-    r = oracle.gemm_entries(p, ii, jj)
-    acceptance.check_close(got[ii, jj], r.ref, r.S, "f8e4m3", "bf16", f"fp8 {M}x{N}x{K}")
+    check_full_size(got, p, 3, f"fp8 {M}x{N}x{K}")
 
 
 def test_config5_fp8_small_full():
@@ -187,6 +189,35 @@ def test_random_tolerance(dab, dcd, la, lb, lc):
 
 
 # ------------------------------------------------------------ stream-K
+
+@pytest.mark.parametrize("M,N,K,tile,sched,sk_grid", [
+    # AUTO resolves to hybrid with fewer stream-K iterations than workgroups
+    (4352, 4096, 256, T.AUTO, S.AUTO, 0),        # 272 tiles of 256^2: 16 stream-K, ipt 4
+    (3072, 3200, 256, T.T128x128, S.HYBRID, 0),  # 600 tiles of 128^2 over 2/CU
+    (4352, 4096, 512, T.T256x256, S.HYBRID, 0),  # ipt 8: 128 iterations
+    (2304, 2560, 256, T.T256x256, S.HYBRID, 0),  # 90 tiles < grid: resolves to stream-K
+    (1024, 1280, 384, T.T128x128, S.STREAM_K, 200),
+    (4352, 4352, 256, T.T256x256, S.HYBRID, 100),   # explicit grid, remainder of 89 tiles
+])
+def test_integer_exact_hybrid_few_iterations(M, N, K, tile, sched, sk_grid):
+    """Stream-K remainders whose iterations number fewer than the grid
+    (every workgroup must still own a non-empty range): NaN-prefilled D,
+    compared with the oracle in full, bit-exact."""
+    p = _int_problem("bf16", "bf16", "row", "col", "row", M=M, N=N, K=K, seed=M + K)
+    plan = g.Plan("bf16", la="row", lb="col", lc="row")
+    plan.set_config(sched, tile, sk_grid)
+    d = plan.describe(M, N, K)
+    if sched == S.AUTO:
+        assert d["schedule"] == "hybrid" and d["sk_iters"] < d["grid"], d
+    assert d["sk_grid"] <= max(d["sk_iters"], 1), d
+    got = run(p, plan=plan, schedule=sched, tile=tile, sk_grid=sk_grid)
+    # twice on one plan: the arrival counters must be left clean
+    got2 = run(p, plan=plan, schedule=sched, tile=tile, sk_grid=sk_grid)
+    plan.close()
+    assert np.isfinite(got).all()
+    exact(got, p, what=f"hybrid {M}x{N}x{K} {d}")
+    assert np.array_equal(got, got2)
+
 
 def test_stream_k_deterministic_and_equivalent():
     p = syn.make_problem(512, 512, 4096, dtype_ab="bf16", dtype_cd="bf16", lb="col", seed=8)
@@ -253,14 +284,22 @@ def test_grouped_small_full_oracle():
     plan.close()
 
 
-def test_grouped_config3_sampled_rows():
+def test_grouped_config3_every_block():
+    """The 64-problem grouped launch the benchmark times: every D fully
+    written, one oracle entry per 32 x 32 block of every problem, and rows 0,
+    M/2 and M-1 of every problem in full."""
     probs = syn.config3()
     plan = g.Plan("f16", la="row", lb="row", lc="row")
     outs = _grouped_run(plan, probs)
-    for p, got in zip(probs, outs):
+    for q, (p, got) in enumerate(zip(probs, outs)):
+        what = f"grouped #{q} {p.M}x{p.N}x{p.K}"
+        assert np.isfinite(got).all(), f"{what}: unwritten (NaN) outputs"
+        ii, jj = full_size_samples(p.M, p.N, 100 + q)
+        r = oracle.gemm_entries(p, ii, jj)
+        acceptance.check_close(got[ii, jj], r.ref, r.S, "f16", "f16", what)
         rows = [0, p.M // 2, p.M - 1]
         r = oracle.gemm(p, rows=rows)
-        acceptance.check_close(got[rows], r.ref, r.S, "f16", "f16", f"grouped {p.M}x{p.N}x{p.K}")
+        acceptance.check_close(got[rows], r.ref, r.S, "f16", "f16", what + " rows")
     plan.close()
 
 
