@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mg {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
@@ -515,7 +517,8 @@ template <int R, int ESZ, int NT, int CH> struct DirectStager {
 // (more than 2 only when both operands are K-contiguous).
 // PIPE: 0 = fragment reads scheduled by the compiler; 3 = the fragments of
 // substep s+1 are read (as one burst) before the MFMAs of substep s, with
-// scheduling fences.
+// scheduling fences; 7 = the register-streamed pipeline (mainloop_rs: both
+// operands K-contiguous, one wave per SIMD).
 // COPY_WAVES: how many waves issue the LDS-DMA copies (0 = all). With half
 // of them (one per SIMD), the other wave of every SIMD starts its MFMAs right
 // after the barrier while its partner waits on the CU's copy queue, which
@@ -537,6 +540,8 @@ struct Tile {
     static constexpr bool MX = F::MX;
     static_assert(!MX || (CH == 8 && STAGES == 2 && PIPE == 0),
                   "MX tiles: 128-byte rows (four scale blocks per k-tile), two stages");
+    static_assert(PIPE != 7 || (A_KC && B_KC && CH == 8 && STAGES == 2 && COPY_WAVES == 0),
+                  "register-streamed pipeline: K-contiguous operands, 128-byte rows, two stages");
     // LDS: [A stage 0 .. A stage S-1 | B stage 0 .. B stage S-1]
     static constexpr int A_BYTES = BM * KB, B_BYTES = BN * KB;
     static constexpr int B_OFF = STAGES * A_BYTES;
@@ -829,6 +834,10 @@ struct Tile {
         const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
         const int wm = wave / WN, wn = wave % WN;
         const int kt0 = uniform(kt0_), n = uniform(n_), stride = uniform(stride_);
+        if constexpr (PIPE == 7) {
+            mainloop_rs(p, tm, tn, kt0, n, stride, acc, lds);
+            return;
+        }
         zero(acc);
         if (n <= 0) return;
         // valid k of the last k-tile of K (the only one that can be partial)
@@ -877,6 +886,231 @@ struct Tile {
         __syncthreads();
     }
 
+    // ---- register-streamed pipeline (PIPE == 7) -------------------------------
+    //
+    // One wave per SIMD (2 x 2 waves of 128 x 128 on the 256 x 256 tile). Each
+    // thread streams its 16-byte chunks of every k-tile through registers:
+    // chunk u of k-tile t+2 is fetched right after chunk u of k-tile t+1 has
+    // been written to LDS, so a whole k-tile of loads is always in flight --
+    // the registers are the third buffer that two 64 KiB LDS stages leave no
+    // room for -- and no barrier ever waits for the memory pipe to drain.
+    // Inside a k-tile, the LDS writes of the next k-tile and the fragment
+    // reads of the next substep sit between the MFMAs of the current substep;
+    // one barrier, before the last substep, publishes the next k-tile's stage
+    // and releases the previous one for the writes that follow.
+    static constexpr int RS_UA = BM * CH / NT, RS_UB = BN * CH / NT;   // chunks per thread
+    static constexpr int RS_OPS = RS_UA + RS_UB;
+    static constexpr int RS_RSTEP = NT / CH;   // rows between one thread's chunks
+    // Pipeline shape: RS_DEPTH k-tiles of loads in flight in registers (one
+    // register set each); the LDS writes of a k-tile spread over substeps
+    // [0, RS_WSUB), which all precede the barrier; the global loads over
+    // substeps [0, RS_LSUB), each after the write that frees its registers.
+    static constexpr int RS_DEPTH = 1;
+    static constexpr int RS_WSUB = SUBSTEPS - 1;
+    static constexpr int RS_LSUB = SUBSTEPS;
+    static_assert(RS_DEPTH == 1 || RS_DEPTH == 2, "register stages");
+    static_assert(RS_WSUB >= 1 && RS_WSUB <= SUBSTEPS - 1 && RS_LSUB >= 1 && RS_LSUB <= SUBSTEPS,
+                  "copy distribution");
+    // substep of op o's LDS write and of its global load
+    static constexpr int rs_ws(int o) { return o * RS_WSUB / RS_OPS; }
+    static constexpr int rs_ls(int o) {
+        return o * RS_LSUB / RS_OPS > rs_ws(o) ? o * RS_LSUB / RS_OPS : rs_ws(o);
+    }
+    static constexpr int rs_count_w(int S) {
+        int c = 0;
+        for (int o = 0; o < RS_OPS; ++o) c += rs_ws(o) == S;
+        return c;
+    }
+    static constexpr int rs_count_l(int S) {
+        int c = 0;
+        for (int o = 0; o < RS_OPS; ++o) c += rs_ls(o) == S;
+        return c;
+    }
+
+    template <int U> struct RsStream {
+        const char *base;   // operand element (first row of the tile, k = 0), wave-uniform
+        uint32_t voff;      // this lane's byte offset in the tile's first row step
+        uint32_t step;      // bytes between a thread's consecutive chunks (32 rows), uniform
+        int nval;           // chunks of this thread whose rows lie inside the operand
+        uint32_t lo[2];     // LDS byte offsets of chunk 0 and of chunk 1 minus one row step
+        u32x4 r[RS_DEPTH][U];
+
+        __device__ __forceinline__ void init(const char *tile_base, uint32_t ld, int r_left, int tid) {
+            static_assert(RS_RSTEP == 32, "register stream: 256 threads, 128-byte rows");
+            base = static_cast<const char *>(uniform_ptr(tile_base));
+            const int row0 = tid >> 3, c = tid & 7;
+            voff = (uint32_t)row0 * ld + (uint32_t)(c << 4);
+            step = (uint32_t)uniform((int)(ld * RS_RSTEP));
+            nval = r_left > row0 ? (r_left - row0 + RS_RSTEP - 1) / RS_RSTEP : 0;
+            // rows row0 + 32u: the row swizzle repeats with period 2 in u
+            lo[0] = lds_off<8>(row0, c);
+            lo[1] = lds_off<8>(row0 + RS_RSTEP, c) - RS_RSTEP * KB;
+        }
+        // chunk u of the k-tile whose resource starts at its first byte, into
+        // register set Q; kin: this thread's chunk lies inside K. The row
+        // step goes in the scalar offset; a lane outside the operand reads
+        // zeros (offset past the records).
+        template <int Q>
+        __device__ __forceinline__ void load(int u, __amdgpu_buffer_rsrc_t rs, bool kin) {
+            r[Q][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, kin && u < nval ? voff : OOB_OFFSET,
+                                                            u * step, 0);
+        }
+        template <int Q> __device__ __forceinline__ void store(int u, char *stage) const {
+            *reinterpret_cast<u32x4 *>(stage + lo[u & 1] + u * RS_RSTEP * KB) = r[Q][u];
+        }
+    };
+
+    // fragments of substep s of one stage
+    static __device__ __forceinline__ void rs_frags(const char *sA, const char *sB, int s, Frags &f,
+                                                    int lane, int wm, int wn) {
+        const int g = lane >> 5, r = lane & 31;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                f.x[i][c] = *reinterpret_cast<const u32x4 *>(
+                    sB + lds_off<CH>(wn * WTN + i * 32 + r, frag_chunk(s, g, c)));
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                f.y[j][c] = *reinterpret_cast<const u32x4 *>(
+                    sA + lds_off<CH>(wm * WTM + j * 32 + r, frag_chunk(s, g, c)));
+    }
+
+    // Scheduling pattern of one substep: the fragment reads ride on the
+    // first half of its MFMAs; the LDS writes, then the global loads, on the
+    // second half (the writes go to the other stage, but the compiler cannot
+    // prove that, so they stay behind the reads), spread evenly, so the
+    // memory instructions issue in the MFMAs' shadow.
+    template <int NREAD, int NW, int NL, int Q = 0>
+    static __device__ __forceinline__ void rs_sched() {
+        constexpr int NMMA = FN * FM;
+        constexpr int H = NMMA / 2;
+        if constexpr (Q < NMMA) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            if constexpr (Q < H) {
+                constexpr int NR = (Q + 1) * NREAD / H - Q * NREAD / H;
+                if constexpr (NR > 0) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);   // DS read
+            } else {
+                constexpr int W = NMMA - H, h = Q - H, TOT = NW + NL;
+                constexpr int e0 = h * TOT / W, e1 = (h + 1) * TOT / W;
+                constexpr int nw = (e1 < NW ? e1 : NW) - (e0 < NW ? e0 : NW);
+                constexpr int nl = (e1 - e0) - nw;
+                if constexpr (nw > 0) __builtin_amdgcn_sched_group_barrier(0x200, nw, 0);   // DS write
+                if constexpr (nl > 0) __builtin_amdgcn_sched_group_barrier(0x020, nl, 0);   // VMEM read
+            }
+            rs_sched<NREAD, NW, NL, Q + 1>();
+        }
+    }
+
+    static __device__ __forceinline__ void mainloop_rs(const Prob &p, int tm, int tn, int kt0, int n,
+                                                       int stride, Acc &acc, char *lds) {
+        const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+        const int wm = wave / WN, wn = wave % WN;
+        zero(acc);
+        if (n <= 0) return;
+        const int last = uniform(p.ipt) - 1;
+        const int k_tail = uniform((int)(p.K - (int64_t)last * BK));
+        const int kc = (tid & 7) * VEC;   // first k of this thread's chunk within a k-tile
+        RsStream<RS_UA> sa;
+        RsStream<RS_UB> sb;
+        {
+            const char *base;
+            uint32_t ld;
+            int rl, kl;
+            a_tile(p, tm, 0, base, ld, rl, kl);
+            sa.init(base, ld, rl, tid);
+            b_tile(p, tn, 0, base, ld, rl, kl);
+            sb.init(base, ld, rl, tid);
+        }
+        // k-tile j of this work unit (j >= n: none; every chunk reads zeros)
+        auto kin = [&](int j) {
+            const int kt = kt0 + j * stride;
+            return j < n && kc < (kt == last ? k_tail : BK);
+        };
+        auto koff = [&](int j) { return (size_t)(kt0 + (j < n ? j : 0) * stride) * KB; };
+        // every chunk of k-tile j into register set Q
+        auto load_all = [&](auto qc, int j) {
+            constexpr int Q = decltype(qc)::value;
+            const bool k = kin(j);
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(sa.base + koff(j));
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(sb.base + koff(j));
+#pragma unroll
+            for (int u = 0; u < RS_UA; ++u) sa.template load<Q>(u, ra, k);
+#pragma unroll
+            for (int u = 0; u < RS_UB; ++u) sb.template load<Q>(u, rb, k);
+        };
+        constexpr int Q1 = RS_DEPTH == 2 ? 1 : 0;   // register set of k-tile 1
+
+        // prologue: k-tile 0 into stage 0; k-tiles 1 .. RS_DEPTH into registers
+        load_all(std::integral_constant<int, 0>{}, 0);
+#pragma unroll
+        for (int u = 0; u < RS_UA; ++u) sa.template store<0>(u, lds);
+#pragma unroll
+        for (int u = 0; u < RS_UB; ++u) sb.template store<0>(u, lds + B_OFF);
+        load_all(std::integral_constant<int, Q1>{}, 1);
+        if constexpr (RS_DEPTH == 2) load_all(std::integral_constant<int, 0>{}, 2);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes done
+        barrier_no_fence();
+
+        Frags f[2];
+        rs_frags(lds, lds + B_OFF, 0, f[0], lane, wm, wn);
+        // iteration i: multiply k-tile i (stage P = i & 1); write k-tile i+1
+        // from its register set into stage P^1 and refill that set with
+        // k-tile i+1+RS_DEPTH
+        auto iteration = [&](auto pc, int i) {
+            constexpr int P = decltype(pc)::value;
+            constexpr int Q = RS_DEPTH == 2 ? (P ^ 1) : 0;   // register set of k-tile i+1
+            const char *rA = lds + P * A_BYTES, *rB = lds + B_OFF + P * B_BYTES;
+            char *wA = lds + (P ^ 1) * A_BYTES, *wB = lds + B_OFF + (P ^ 1) * B_BYTES;
+            const int jn = i + 1 + RS_DEPTH;
+            const bool kn = kin(jn);
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(sa.base + koff(jn));
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(sb.base + koff(jn));
+            auto substep = [&](auto sc) {
+                constexpr int S = decltype(sc)::value;
+                // fragments for the next substep: this stage, or (after the
+                // barrier) the next k-tile's substep 0 from the other stage
+                if constexpr (S + 1 < SUBSTEPS) rs_frags(rA, rB, S + 1, f[(S + 1) & 1], lane, wm, wn);
+                else rs_frags(wA, wB, 0, f[0], lane, wm, wn);
+                mma_frags(f[S & 1], acc);
+#pragma unroll
+                for (int o = 0; o < RS_OPS; ++o) {
+                    if (rs_ws(o) != S) continue;
+                    if (o < RS_UA) sa.template store<Q>(o, wA);
+                    else sb.template store<Q>(o - RS_UA, wB);
+                }
+#pragma unroll
+                for (int o = 0; o < RS_OPS; ++o) {
+                    if (rs_ls(o) != S) continue;
+                    if (o < RS_UA) sa.template load<Q>(o, ra, kn);
+                    else sb.template load<Q>(o - RS_UA, rb, kn);
+                }
+                rs_sched<FN * CPL + FM * CPL, rs_count_w(S), rs_count_l(S)>();
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (S == SUBSTEPS - 2) {
+                    // this wave's writes of k-tile i+1 and reads of k-tile i
+                    // are done; after the barrier everyone's are
+                    __builtin_amdgcn_s_waitcnt(0xC07F);
+                    barrier_no_fence();
+                }
+            };
+            static_assert(SUBSTEPS == 2 || SUBSTEPS == 4, "substeps per k-tile");
+            substep(std::integral_constant<int, 0>{});
+            substep(std::integral_constant<int, 1>{});
+            if constexpr (SUBSTEPS == 4) {
+                substep(std::integral_constant<int, 2>{});
+                substep(std::integral_constant<int, 3>{});
+            }
+        };
+        for (int i = 0; i < n; i += 2) {
+            iteration(std::integral_constant<int, 0>{}, i);
+            if (i + 1 < n) iteration(std::integral_constant<int, 1>{}, i + 1);
+        }
+        __syncthreads();
+    }
+
     // ---- epilogue ------------------------------------------------------------
     //
     // v = alpha' * acc + beta * C (C not read when beta == 0) + bias[n],
@@ -920,49 +1154,75 @@ struct Tile {
         }
     }
 
-    template <bool BETA>
+    // The finished output tile can be staged through the (idle) LDS and
+    // written back as whole rows: OROW bytes per tile row, the 16-byte chunk
+    // k of row r at chunk k ^ (r & 15) -- the per-lane 4-element writes (two
+    // or four rows of one chunk column per bank window) and the row-wise
+    // 16-byte reads are both free of bank conflicts.
+    static constexpr int OSZ = (int)sizeof(Out);
+    static constexpr int OROW = BN * OSZ;
+    static constexpr int OCPR = OROW / 16;   // 16-byte chunks per tile row
+    static constexpr bool STAGE_OUT = BM * OROW <= LDS_BYTES && OCPR >= 16 && (BM * OCPR) % NT == 0;
+    static __device__ __forceinline__ uint32_t out_off(int r, int cbyte) {
+        return (uint32_t)(r * OROW + ((((cbyte >> 4) ^ (r & 15))) << 4) + (cbyte & 15));
+    }
+
+    // Four floats to LDS as output-typed elements (one RNE conversion).
+    static __device__ __forceinline__ void store4_lds(char *lds, uint32_t off, const float (&v)[4]) {
+        if constexpr (sizeof(Out) == 4) {
+            *reinterpret_cast<f32x4 *>(lds + off) = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+            u32x2 t;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                t[h] = (uint32_t)__builtin_bit_cast(uint16_t, (Out)v[2 * h]) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, (Out)v[2 * h + 1]) << 16);
+            *reinterpret_cast<u32x2 *>(lds + off) = t;
+        }
+    }
+
+    // Interior tile, RowMajor D, beta = 0, no bias or auxiliary tensor, a
+    // linear or ReLU epilogue, the output tile fitting the LDS: v =
+    // act(alpha acc) per lane (four
+    // consecutive n of one m for each (i, j, q)) into the LDS (idle on
+    // entry), which the workgroup then writes back as whole rows with
+    // 16-byte stores (D 16-byte aligned, rows a multiple of 16 bytes). The
+    // one inlined epilogue of a kernel, kept this small so the main loop's
+    // register allocation is unaffected; the other cases run out of line.
     static __device__ __forceinline__ void epi_fast(const Prob &p, const EpiArgs &e, float alpha,
-                                                    int64_t m_base, int64_t n_base, const Acc &acc) {
-        Out *D = reinterpret_cast<Out *>(p.D);
-        const Out *C = reinterpret_cast<const Out *>(p.C);
-        const Out *bias = reinterpret_cast<const Out *>(e.bias);
-        const int act = e.act;
-        // the bias depends on n only: one vector per (i, q), shared by every row
-        float bv[FN][4][4];
+                                                    int64_t m_base, int64_t n_base, const Acc &acc,
+                                                    char *lds, int tm, int tn) {
+        // LINEAR or RELU only, as a select (a switch per element would put
+        // every element behind its own branches); relu(NaN) = relu(-0) = +0
+        const bool relu = e.act == ACT_RELU;
+        const int tid = threadIdx.x;
+        // tile-local row / column of this lane's first group
+        const int r_loc = (int)(m_base - (int64_t)tm * BM), c_loc = (int)(n_base - (int64_t)tn * BN);
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (bias) load4(bias, n_base + i * 32 + q * 8, bv[i][q]);
-                else
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int t4 = 0; t4 < 4; ++t4) bv[i][q][t4] = 0.0f;
-            }
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const int64_t row = (m_base + j * 32) * p.N;
-#pragma unroll
-            for (int i = 0; i < FN; ++i)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t idx = row + n_base + i * 32 + q * 8;
+                for (int j = 0; j < FM; ++j) {
                     float v[4];
-                    if constexpr (BETA) {
-                        float c[4];
-                        load4(C, idx, c);
 #pragma unroll
-                        for (int t4 = 0; t4 < 4; ++t4)
-                            v[t4] = apply_act(__builtin_fmaf(alpha, acc.v[i][j][q * 4 + t4],
-                                                             e.beta * c[t4]) + bv[i][q][t4],
-                                              act);
-                    } else {
-#pragma unroll
-                        for (int t4 = 0; t4 < 4; ++t4)
-                            v[t4] = apply_act(alpha * acc.v[i][j][q * 4 + t4] + bv[i][q][t4], act);
+                    for (int t4 = 0; t4 < 4; ++t4) {
+                        const float x = alpha * acc.v[i][j][q * 4 + t4];
+                        v[t4] = (relu && !(x > 0.0f)) ? 0.0f : x;
                     }
-                    store4(D, idx, v);
+                    store4_lds(lds, out_off(r_loc + j * 32, (c_loc + i * 32 + q * 8) * OSZ), v);
                 }
+        __syncthreads();
+        char *Dt = p.D + ((int64_t)tm * BM * p.N + (int64_t)tn * BN) * OSZ;
+        const int64_t ld = p.N * OSZ;
+#pragma unroll 8
+        for (int it = 0; it < BM * OCPR / NT; ++it) {
+            const int c = tid + it * NT;
+            const int r = c / OCPR, k = c - (c / OCPR) * OCPR;
+            const u32x4 val = *reinterpret_cast<const u32x4 *>(lds + out_off(r, k * 16));
+            *reinterpret_cast<u32x4 *>(Dt + r * ld + k * 16) = val;
         }
+        __syncthreads();
     }
 
     // Interior tile with auxiliary tensors: the same vector accesses as
@@ -1008,21 +1268,26 @@ struct Tile {
     static constexpr int AUX_JC = AUX_JC_FIT >= FM ? FM : AUX_JC_FIT;
     static_assert(AUX_JC >= 1 && FM % AUX_JC == 0, "LDS hand-off of the auxiliary epilogue");
 
-    // Edge tiles, ColumnMajor C/D or unaligned C/D: element by element.
+    // Edge tiles, ColumnMajor C/D or unaligned C/D: element by element, with
+    // the accumulators of fragment rows j0 .. j0+jc-1 handed over through the
+    // idle LDS exactly as for epi_aux (no private scratch array).
     static __device__ __noinline__ void epi_slow(const Prob &p, const EpiArgs &e, float alpha,
-                                                 int64_t m_base, int64_t n_base, const float *vals) {
+                                                 int64_t m_base, int64_t n_base, const f32x4 *vals,
+                                                 int j0, int jc) {
         Out *D = reinterpret_cast<Out *>(p.D);
         const Out *C = reinterpret_cast<const Out *>(p.C);
-        for (int j = 0; j < FM; ++j) {
-            const int64_t m = m_base + j * 32;
+        const int tid = threadIdx.x;
+        for (int jj = 0; jj < jc; ++jj) {
+            const int64_t m = m_base + (j0 + jj) * 32;
             if (m >= p.M) continue;
             for (int i = 0; i < FN; ++i)
-                for (int q = 0; q < 4; ++q)
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 a4 = vals[((jj * FN + i) * 4 + q) * NT + tid];
                     for (int t4 = 0; t4 < 4; ++t4) {
                         const int64_t n = n_base + i * 32 + q * 8 + t4;
                         if (n >= p.N) continue;
                         const int64_t idx = e.lc_row ? m * p.N + n : m + n * p.M;
-                        const float a = vals[((i * FM + j) * 4 + q) * 4 + t4];
+                        const float a = a4[t4];
                         float v = alpha * a;
                         if (e.beta != 0.0f) v = __builtin_fmaf(alpha, a, e.beta * (float)C[idx]);
                         if (e.bias) v += (float)reinterpret_cast<const Out *>(e.bias)[n];
@@ -1034,12 +1299,14 @@ struct Tile {
                                                         e.aux && e.aux_after, z);
                         if (e.aux_out) reinterpret_cast<Out *>(e.aux_out)[idx] = (Out)z;
                     }
+                }
         }
     }
 
     // `lds`: the tile's LDS, idle here (the main loop ends with a barrier);
-    // the auxiliary-tensor path hands the accumulators over through it and
-    // closes with a barrier before the next tile's copies may land.
+    // every path but the interior vector one hands the accumulators over
+    // through it and closes with a barrier before the next tile's copies may
+    // land.
     static __device__ __forceinline__ void epilogue(const Prob &p, const EpiArgs &e, int tm, int tn,
                                                     const Acc &acc, char *lds) {
         const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
@@ -1049,37 +1316,31 @@ struct Tile {
         const int64_t n_base = (int64_t)tn * BN + wn * WTN + (lane >> 5) * 4;
         const bool interior = e.lc_row && p.vec_cd && (int64_t)(tm + 1) * BM <= p.M &&
                               (int64_t)(tn + 1) * BN <= p.N;
-        if (interior && (e.aux || e.aux_out)) {
-            f32x4 *buf = reinterpret_cast<f32x4 *>(lds);
-            const int tid = threadIdx.x;
-#pragma unroll
-            for (int j0 = 0; j0 < FM; j0 += AUX_JC) {
-                // each thread reads back only its own slots: no barrier between
-#pragma unroll
-                for (int jj = 0; jj < AUX_JC; ++jj)
-#pragma unroll
-                    for (int i = 0; i < FN; ++i)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            buf[((jj * FN + i) * 4 + q) * NT + tid] =
-                                f32x4{acc.v[i][j0 + jj][q * 4], acc.v[i][j0 + jj][q * 4 + 1],
-                                      acc.v[i][j0 + jj][q * 4 + 2], acc.v[i][j0 + jj][q * 4 + 3]};
-                epi_aux(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
+        if constexpr (STAGE_OUT) {
+            if (interior && !e.aux && !e.aux_out && !e.bias && e.beta == 0.0f &&
+                (e.act == ACT_LINEAR || e.act == ACT_RELU) &&
+                (reinterpret_cast<uintptr_t>(p.D) & 15) == 0 && ((p.N * OSZ) & 15) == 0) {
+                epi_fast(p, e, alpha, m_base, n_base, acc, lds, tm, tn);
+                return;
             }
-            __syncthreads();
-        } else if (interior) {
-            if (e.beta != 0.0f) epi_fast<true>(p, e, alpha, m_base, n_base, acc);
-            else epi_fast<false>(p, e, alpha, m_base, n_base, acc);
-        } else {
-            float vals[FN * FM * 16];
-#pragma unroll
-            for (int i = 0; i < FN; ++i)
-#pragma unroll
-                for (int j = 0; j < FM; ++j)
-#pragma unroll
-                    for (int x = 0; x < 16; ++x) vals[(i * FM + j) * 16 + x] = acc.v[i][j][x];
-            epi_slow(p, e, alpha, m_base, n_base, vals);
         }
+        f32x4 *buf = reinterpret_cast<f32x4 *>(lds);
+#pragma unroll
+        for (int j0 = 0; j0 < FM; j0 += AUX_JC) {
+            // each thread reads back only its own slots: no barrier between
+#pragma unroll
+            for (int jj = 0; jj < AUX_JC; ++jj)
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        buf[((jj * FN + i) * 4 + q) * NT + tid] =
+                            f32x4{acc.v[i][j0 + jj][q * 4], acc.v[i][j0 + jj][q * 4 + 1],
+                                  acc.v[i][j0 + jj][q * 4 + 2], acc.v[i][j0 + jj][q * 4 + 3]};
+            if (interior) epi_aux(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
+            else epi_slow(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
+        }
+        __syncthreads();
     }
 
     // ---- stream-K partial tiles ---------------------------------------------
@@ -1242,6 +1503,11 @@ Tile<FAM_, A_KC, B_KC, BM_, BN_, WM_, WN_, KB, STAGES, PIPE, COPY_WAVES>::tile_p
     return q;
 }
 
+// One workgroup's work, as a sequence of units (a tile and a range of its
+// k-tiles): the split-K unit, or the stream-K segments, then the
+// data-parallel tiles. The kernel has a single main-loop and a single
+// epilogue call site, which keeps its code and register allocation to one
+// copy of each.
 template <class TL>
 __global__ void __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::WAVES_PER_EU)))
 gemm_persistent(KArgs a) {
@@ -1249,80 +1515,91 @@ gemm_persistent(KArgs a) {
     const Prob &p = a.p;
     const Sched &s = a.s;
     const int v = uniform(virtual_id(blockIdx.x, s.grid, s.xcd_remap));
+    const size_t slot_elems = (size_t)TL::BM * TL::BN;
     typename TL::Acc acc;
-    int tm, tn;
 
-    if (s.split > 0) {
-        const int S = s.split;
-        if (v >= s.sk_tiles * S) return;
-        const int t = v / S, c = v - (v / S) * S;
-        const Prob pt = TL::tile_problem(p, t, s.group_m, tm, tn);
-        TL::mainloop(pt, tm, tn, c, (p.ipt - c + S - 1) / S, S, acc, lds);
-        if (S == 1) {
-            TL::epilogue(pt, a.e, tm, tn, acc, lds);
-            return;
+    // stream-K range of this workgroup (empty unless v < sk_grid)
+    const bool sk = s.split == 0 && s.sk_tiles > 0 && p.ipt > 0 && v < s.sk_grid;
+    const int64_t T = s.sk_iters;
+    const int G = s.sk_grid;
+    int64_t it = sk ? (int64_t)v * T / G : 0;
+    const int64_t end = sk ? (int64_t)(v + 1) * T / G : 0;
+    const int first_tile = sk ? (int)(it / p.ipt) : 0;
+    // split-K: this workgroup's single unit, if any
+    const int S = s.split;
+    bool split_pending = S > 0 && v < s.sk_tiles * S;
+    int dp_t = S > 0 ? s.total_tiles : s.sk_tiles + v;
+
+    for (;;) {
+        int t, kt0, n, stride;
+        int mode;   // 0: whole tile, 1: stream-K segment, 2: split-K unit
+        int c = 0, k1 = 0;
+        if (split_pending) {
+            split_pending = false;
+            t = v / S;
+            c = v - t * S;
+            kt0 = c;
+            n = (p.ipt - c + S - 1) / S;
+            stride = S;
+            mode = S == 1 ? 0 : 2;
+        } else if (it < end) {
+            t = (int)(it / p.ipt);
+            const int64_t tile_it0 = (int64_t)t * p.ipt;
+            kt0 = (int)(it - tile_it0);
+            k1 = (int)(imin64(end, tile_it0 + p.ipt) - tile_it0);
+            n = k1 - kt0;
+            stride = 1;
+            mode = (kt0 == 0 && k1 == p.ipt) ? 0 : 1;
+            it = tile_it0 + k1;
+        } else if (dp_t < s.total_tiles) {
+            t = dp_t;
+            dp_t += s.grid;
+            kt0 = 0;
+            n = p.ipt;
+            stride = 1;
+            mode = 0;
+        } else {
+            break;
         }
-        const size_t slot_elems = (size_t)TL::BM * TL::BN;
-        TL::store_partial(s.partials + (size_t)v * slot_elems, acc);
-        wait_vmcnt<0>();   // this thread's device-scope stores are complete
-        __syncthreads();   // ... and every thread's, before the arrival is counted
-        if (arrive_last(&s.counters[t], S - 1, lds)) {
-            // sum the units in order c = 0 .. S-1 (deterministic)
-            TL::add_partials([&](int u) { return s.partials + ((size_t)t * S + u) * slot_elems; }, S, acc);
+        t = uniform(t);
+        mode = uniform(mode);
+        int tm, tn;
+        const Prob pt = TL::tile_problem(p, t, s.group_m, tm, tn);
+        TL::mainloop(pt, tm, tn, kt0, n, stride, acc, lds);
+        bool finish = mode == 0;
+        int v0 = 0, v1 = 0;
+        if (mode != 0) {
+            // every contributor publishes its partial; the last to arrive
+            // sums all of them in contributor order (deterministic)
+            const int my_slot = mode == 2 ? v : 2 * v + (t == first_tile ? 0 : 1);
+            TL::store_partial(s.partials + (size_t)my_slot * slot_elems, acc);
+            wait_vmcnt<0>();   // this thread's device-scope stores are complete
+            __syncthreads();   // ... and every thread's, before the arrival is counted
+            if (mode == 2) {
+                v1 = S - 1;
+            } else {
+                const int64_t tile_it0 = (int64_t)t * p.ipt;
+                v0 = sk_owner(tile_it0, T, G);
+                v1 = sk_owner(tile_it0 + p.ipt - 1, T, G);
+            }
+            finish = arrive_last(&s.counters[t], v1 - v0, lds);
+            if (finish) {
+                TL::add_partials(
+                    [&](int k) {
+                        if (mode == 2) return s.partials + ((size_t)t * S + k) * slot_elems;
+                        const int u = v0 + k;
+                        const int ft = (int)(((int64_t)u * T / G) / p.ipt);
+                        return s.partials + (size_t)(2 * u + (t == ft ? 0 : 1)) * slot_elems;
+                    },
+                    v1 - v0 + 1, acc);
+            }
+        }
+        if (finish) {
             TL::epilogue(pt, a.e, tm, tn, acc, lds);
-            if (threadIdx.x == 0)
+            if (mode != 0 && threadIdx.x == 0)
                 __hip_atomic_store(&s.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        return;
-    }
-
-    if (s.sk_tiles > 0 && p.ipt > 0 && v < s.sk_grid) {
-        const int64_t T = s.sk_iters;
-        const int G = s.sk_grid;
-        int64_t it = (int64_t)v * T / G;
-        const int64_t end = (int64_t)(v + 1) * T / G;
-        const int first_tile = (int)(it / p.ipt);
-        while (it < end) {
-            const int t = (int)(it / p.ipt);
-            const int64_t tile_it0 = (int64_t)t * p.ipt;
-            const int k0 = (int)(it - tile_it0);
-            const int k1 = (int)(imin64(end, tile_it0 + p.ipt) - tile_it0);
-            const Prob pt = TL::tile_problem(p, t, s.group_m, tm, tn);
-            TL::mainloop(pt, tm, tn, k0, k1 - k0, 1, acc, lds);
-            if (k0 == 0 && k1 == p.ipt) {
-                TL::epilogue(pt, a.e, tm, tn, acc, lds);
-            } else {
-                // every contributor publishes its partial, the last to arrive
-                // sums all partials in contributor order (deterministic)
-                const size_t slot_elems = (size_t)TL::BM * TL::BN;
-                const int my_slot = 2 * v + (t == first_tile ? 0 : 1);
-                TL::store_partial(s.partials + my_slot * slot_elems, acc);
-                wait_vmcnt<0>();   // this thread's device-scope stores are complete
-                __syncthreads();   // ... and every thread's, before the arrival is counted
-                const int v0 = sk_owner(tile_it0, T, G);
-                const int v1 = sk_owner(tile_it0 + p.ipt - 1, T, G);
-                if (arrive_last(&s.counters[t], v1 - v0, lds)) {
-                    // every contributor's partial is complete at device scope
-                    TL::add_partials(
-                        [&](int k) {
-                            const int u = v0 + k;
-                            const int ft = (int)(((int64_t)u * T / G) / p.ipt);
-                            return s.partials + (size_t)(2 * u + (t == ft ? 0 : 1)) * slot_elems;
-                        },
-                        v1 - v0 + 1, acc);
-                    TL::epilogue(pt, a.e, tm, tn, acc, lds);
-                    if (threadIdx.x == 0)
-                        __hip_atomic_store(&s.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-                __syncthreads();
-            }
-            it = tile_it0 + k1;
-        }
-    }
-    for (int t = s.sk_tiles + v; t < s.total_tiles; t += s.grid) {
-        const Prob pt = TL::tile_problem(p, t, s.group_m, tm, tn);
-        TL::mainloop(pt, tm, tn, 0, p.ipt, 1, acc, lds);
-        TL::epilogue(pt, a.e, tm, tn, acc, lds);
+        if (mode != 0) __syncthreads();
     }
 }
 

@@ -16,6 +16,15 @@ template <int FAM, bool AKC, bool BKC, int BM, int BN, int WM, int WN> struct Ti
 template <int FAM> struct TileCfg<FAM, true, true, 256, 256, 2, 4> {
     using type = Tile<FAM, true, true, 256, 256, 2, 4, 128, 2, 0, 4>;
 };
+// 16-bit types, both operands K-contiguous: the register-streamed pipeline
+// (four waves of 128 x 128, one per SIMD; loads one k-tile ahead in
+// registers, LDS writes and fragment reads slotted between the MFMAs).
+template <> struct TileCfg<FAM_BF16, true, true, 256, 256, 2, 4> {
+    using type = Tile<FAM_BF16, true, true, 256, 256, 2, 2, 128, 2, 7>;
+};
+template <> struct TileCfg<FAM_F16, true, true, 256, 256, 2, 4> {
+    using type = Tile<FAM_F16, true, true, 256, 256, 2, 2, 128, 2, 7>;
+};
 }  // namespace mg
 
 #define MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN) \
