@@ -108,6 +108,8 @@ def _load():
     L.gemm_plan_set_config.argtypes = [vp, ctypes.c_int, ctypes.c_int, i32]
     L.gemm_plan_run.restype = st
     L.gemm_plan_run.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp]
+    L.gemm_plan_run_noalloc.restype = st
+    L.gemm_plan_run_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp]
     L.gemm_plan_run_scaled.restype = st
     L.gemm_plan_run_scaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, f32, f32, vp, vp, vp]
     L.gemm_plan_run_ex.restype = st
@@ -153,7 +155,7 @@ def _load():
 lib = _load()
 
 EXPORTED = ("gemm_plan_create", "gemm_plan_create_simple", "gemm_plan_destroy",
-            "gemm_plan_set_config", "gemm_plan_run", "gemm_plan_run_scaled",
+            "gemm_plan_set_config", "gemm_plan_run", "gemm_plan_run_noalloc", "gemm_plan_run_scaled",
             "gemm_plan_run_ex", "gemm_plan_run_mx", "gemm_plan_run_aux",
             "gemm_plan_run_batched", "grouped_gemm_run", "gemm_plan_profile",
             "gemm_plan_cache_export", "gemm_plan_cache_import", "gemm_plan_cache_size",
@@ -214,6 +216,12 @@ def gemm_plan_run(plan: int, A, B, C, D, M: int, N: int, K: int, alpha: float = 
                   beta: float = 0.0, stream=None) -> None:
     _check(lib.gemm_plan_run(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), M, N, K, alpha, beta,
                              _stream(stream)))
+
+
+def gemm_plan_run_noalloc(plan: int, A, B, C, D, M: int, N: int, K: int, alpha: float = 1.0,
+                          beta: float = 0.0, stream=None) -> None:
+    _check(lib.gemm_plan_run_noalloc(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), M, N, K, alpha,
+                                     beta, _stream(stream)))
 
 
 def gemm_plan_run_scaled(plan: int, A, B, C, D, M: int, N: int, K: int, alpha: float,
@@ -428,6 +436,12 @@ class Plan:
         else:
             gemm_plan_run_scaled(self.handle, A, B, C, D, M, N, K, alpha, beta, scale_a,
                                  scale_b, stream)
+
+    def run_noalloc(self, A, B, C, D, M, N, K, alpha=1.0, beta=0.0, stream=None):
+        """gemm_plan_run_noalloc: run() without any device allocation (the
+        stream-K / split-K workspace is the library's static one)."""
+        self.check(A, B, C, D, M, N, K, beta)
+        gemm_plan_run_noalloc(self.handle, A, B, C, D, M, N, K, alpha, beta, stream)
 
     def run_mx(self, A, B, C, D, M, N, K, mx_scale_a, mx_scale_b, alpha=1.0, beta=0.0,
                stream=None, bias=None):

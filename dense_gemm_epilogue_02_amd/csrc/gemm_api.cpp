@@ -497,7 +497,7 @@ template <class OccFn>
 gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const void *C, const void *D,
                    const void *bias, int64_t M, int64_t N, int64_t K, float beta, int cus, OccFn occ_of,
                    Decision &d, int64_t batch = 1, const void *mx_a = nullptr,
-                   const void *mx_b = nullptr) {
+                   const void *mx_b = nullptr, size_t max_ws = 0) {
     const int fam = mx_a ? FAM_MXF8 : pl->fam;
     const Cfg cfg = plan_cfg(pl, M, N, K, batch, mx_a != nullptr);
     const int esz = elem_bytes(fam), osz = out_bytes(fam);
@@ -615,6 +615,36 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
         d.sk_grid = (int)(d.sk_iters < G ? d.sk_iters : G);
         break;
     }
+    // a fixed-size workspace (max_ws bytes of partial tiles): the stream-K
+    // grid or the split-K factor shrinks until the partials fit; a hybrid
+    // remainder that would no longer spread over the grid runs data-parallel
+    if (max_ws > 0 && d.sk_tiles > 0 && d.split != 1) {
+        const size_t slot = (size_t)e->bm * e->bn * sizeof(float);
+        if (d.sched == GEMM_SCHED_SPLIT_K) {
+            int S = d.split;
+            while (S > 1 && (size_t)d.total * S * slot > max_ws) --S;
+            d.split = S;
+            d.grid = d.total * S;
+            if (S == 1) {   // one unit per tile: a plain data-parallel launch
+                d.sched = GEMM_SCHED_DATA_PARALLEL;
+                d.split = 0;
+                d.sk_tiles = 0;
+                d.grid = d.total < G ? d.total : G;
+            }
+        } else if ((size_t)2 * d.sk_grid * slot > max_ws) {
+            const int cap = (int)(max_ws / (2 * slot));
+            if (d.sched == GEMM_SCHED_HYBRID || cap < 1) {
+                d.sched = GEMM_SCHED_DATA_PARALLEL;
+                d.sk_tiles = 0;
+                d.sk_iters = 0;
+                d.sk_grid = 0;
+                d.grid = d.total < G ? d.total : G;
+            } else {
+                d.grid = cap;
+                d.sk_grid = cap;
+            }
+        }
+    }
     if (d.sk_tiles > 0 && d.split == 0 &&
         (d.sk_grid < 1 || d.sk_grid > d.grid || (int64_t)d.sk_grid > d.sk_iters))
         return fail(GEMM_HIP_ERROR, "internal: stream-K grid %d outside [1, min(grid %d, iterations %lld)]",
@@ -720,6 +750,8 @@ struct RunOpts {
     const void *aux = nullptr;
     void *aux_out = nullptr;
     int aux_op = 0, aux_after = 0;
+    // gemm_plan_run_noalloc: partials and counters from the static workspace
+    bool noalloc = false;
 };
 
 EpiArgs make_epi(const gemm_plan_s *pl, float alpha, float beta, const float *sa, const float *sb,
@@ -748,6 +780,51 @@ gemm_status run_generic(const gemm_plan_s *pl, int fam, const Prob &p, const Epi
     g.lb_row = pl->lb == GEMM_ROW_MAJOR;
     hipError_t e = launch_generic(fam, g, st);
     if (e != hipSuccess) return hip_fail(e, "generic kernel launch");
+    return GEMM_OK;
+}
+
+// ---- the static workspace of gemm_plan_run_noalloc ---------------------------
+//
+// Stream-K / split-K partial tiles followed by the arrival counters, in a
+// file-scope device array: every device the library runs on holds one copy
+// for the life of the process, so the entry point allocates nothing. In host
+// code `scratch` only names the symbol; its device address on each device
+// comes from hipGetSymbolAddress, taken once per device and kept.
+constexpr size_t kNoAllocPartialBytes = (size_t)32 << 20;
+constexpr size_t kNoAllocCounters = 16384;
+static __device__ __align__(256) unsigned char scratch[kNoAllocPartialBytes + kNoAllocCounters * sizeof(int)];
+
+std::mutex g_scratch_mu;
+std::unordered_map<int, unsigned char *> g_scratch_ptr;
+
+// The static workspace of device `dev` (current): its address, and on the
+// first call its counters cleared (the fill kernel on `st`, then a wait for
+// it, so calls on other streams find them clear); afterwards the finishing
+// workgroup of every split tile resets its counter.
+gemm_status noalloc_workspace(int dev, hipStream_t st, unsigned char **out) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it != g_scratch_ptr.end()) {
+        *out = it->second;
+        return GEMM_OK;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(GEMM_UNSUPPORTED,
+                    "gemm_plan_run_noalloc: the first call on device %d initialises the static workspace "
+                    "and must not be captured into a graph; make one uncaptured call first", dev);
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    unsigned char *base = static_cast<unsigned char *>(p);
+    e = launch_zero_u32(reinterpret_cast<uint32_t *>(base + kNoAllocPartialBytes), kNoAllocCounters, st);
+    if (e != hipSuccess) return hip_fail(e, "static workspace counter initialisation");
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize (static workspace initialisation)");
+    g_scratch_ptr.emplace(dev, base);
+    *out = base;
     return GEMM_OK;
 }
 
@@ -785,7 +862,7 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
                 [&](const KernelEntry *e, int *occ) {
                     return kernel_occupancy(dev, e->fn_persistent, e->nt, occ);
                 },
-                d, bt.count, bt.mx_a, bt.mx_b);
+                d, bt.count, bt.mx_a, bt.mx_b, bt.noalloc ? kNoAllocPartialBytes : 0);
     if (st != GEMM_OK) return st;
     // the vector epilogue reads and writes the auxiliary tensors like C and D
     if (reinterpret_cast<uintptr_t>(bt.aux) % (4 * osz) != 0 ||
@@ -831,9 +908,26 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
     a.s.counters = nullptr;
     if (d.sk_tiles > 0 && d.split != 1) {
         const size_t pbytes = (size_t)2 * d.grid * d.e->bm * d.e->bn * sizeof(float);
-        if ((st = ensure_workspace(pl, pbytes, (size_t)d.sk_tiles, hs)) != GEMM_OK) return st;
-        a.s.partials = pl->partials;
-        a.s.counters = pl->counters;
+        if (bt.noalloc) {
+            // the partials the launch writes: 2 slots per stream-K workgroup,
+            // one per split-K unit
+            const size_t slot = (size_t)d.e->bm * d.e->bn * sizeof(float);
+            const size_t need = d.split > 1 ? (size_t)d.grid * slot : (size_t)2 * d.sk_grid * slot;
+            if (need > kNoAllocPartialBytes || (size_t)d.sk_tiles > kNoAllocCounters)
+                return fail(GEMM_UNSUPPORTED,
+                            "gemm_plan_run_noalloc: %s launch needs %zu bytes of partial tiles and %d "
+                            "arrival counters; the static workspace holds %zu bytes and %zu counters "
+                            "(use gemm_plan_run, or a data-parallel schedule)",
+                            sched_name(d.sched), need, d.sk_tiles, kNoAllocPartialBytes, kNoAllocCounters);
+            unsigned char *ws = nullptr;
+            if ((st = noalloc_workspace(dev, hs, &ws)) != GEMM_OK) return st;
+            a.s.partials = reinterpret_cast<float *>(ws);
+            a.s.counters = reinterpret_cast<int *>(ws + kNoAllocPartialBytes);
+        } else {
+            if ((st = ensure_workspace(pl, pbytes, (size_t)d.sk_tiles, hs)) != GEMM_OK) return st;
+            a.s.partials = pl->partials;
+            a.s.counters = pl->counters;
+        }
     }
     hipError_t e = d.e->run(a, d.grid, hs);
     if (e != hipSuccess) return hip_fail(e, "tile kernel launch");
@@ -987,6 +1081,14 @@ gemm_status gemm_plan_set_config(gemm_plan_t p, gemm_schedule s, gemm_tile t, in
 gemm_status gemm_plan_run(gemm_plan_t p, const void *A, const void *B, const void *C, void *D, int64_t M,
                           int64_t N, int64_t K, float alpha, float beta, void *stream) {
     return run_one(p, A, B, C, D, M, N, K, alpha, beta, nullptr, nullptr, nullptr, stream);
+}
+
+gemm_status gemm_plan_run_noalloc(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,
+                                  int64_t M, int64_t N, int64_t K, float alpha, float beta,
+                                  void *stream) {
+    RunOpts ro;
+    ro.noalloc = true;
+    return run_one(p, A, B, C, D, M, N, K, alpha, beta, nullptr, nullptr, nullptr, stream, ro);
 }
 
 gemm_status gemm_plan_run_scaled(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,

@@ -149,6 +149,31 @@ gemm_status gemm_plan_run(gemm_plan_t plan, const void *A, const void *B,
                           const void *C, void *D, int64_t M, int64_t N,
                           int64_t K, float alpha, float beta, void *stream);
 
+/* gemm_plan_run for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, semantics and results contract as gemm_plan_run; it calls
+ * no hipMalloc, hipFree or other allocating routine. The stream-K / split-K
+ * partial tiles and arrival counters come from a static workspace compiled
+ * into the library (32 MiB of partials and 16384 counters per device, held
+ * by each device the library runs on until the process ends) instead of the
+ * plan's: a stream-K grid or split-K factor is reduced until its partials
+ * fit, and a hybrid schedule whose remainder would not spread over the grid
+ * runs data-parallel, so results may differ from gemm_plan_run's in the
+ * order of the fp32 sums only. A launch that still needs more partials or
+ * counters than the workspace holds returns GEMM_UNSUPPORTED, naming both
+ * sizes, and enqueues nothing.
+ * The first call on each device initialises that device's workspace (it
+ * clears the counters on `stream` and waits for them): it must not be
+ * captured into a graph (GEMM_UNSUPPORTED if it is); later calls may be.
+ * Every call on one device shares that device's workspace: two calls that
+ * overlap in time on one device (two streams, or two host threads) race on
+ * it and give wrong results. Order them, or use gemm_plan_run with one plan
+ * per stream. */
+gemm_status gemm_plan_run_noalloc(gemm_plan_t plan, const void *A, const void *B,
+                                  const void *C, void *D, int64_t M, int64_t N,
+                                  int64_t K, float alpha, float beta,
+                                  void *stream);
+
 /* FP8 with per-tensor scales ("Generating State-of-the-Art GEMMs ...",
  * section 5.1, scaled mm): D = epi(alpha * s_A * s_B * (A_q B_q) + beta * C).
  * scale_a / scale_b point to one fp32 each in device memory (NULL = 1.0);
