@@ -1195,23 +1195,40 @@ struct Tile {
         // LINEAR or RELU only, as a select (a switch per element would put
         // every element behind its own branches); relu(NaN) = relu(-0) = +0
         const bool relu = e.act == ACT_RELU;
-        const int tid = threadIdx.x;
+        // the per-lane LDS offsets below depend on the lane only; an opaque
+        // copy of the thread index keeps the compiler from hoisting all of
+        // them out of the persistent tile loop, where they would stay live
+        // (64 registers) through every main loop
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, wave = tid >> 6;
         // tile-local row / column of this lane's first group
-        const int r_loc = (int)(m_base - (int64_t)tm * BM), c_loc = (int)(n_base - (int64_t)tn * BN);
+        const int r_loc = (wave / WN) * WTM + (lane & 31), c_loc = (wave % WN) * WTN + (lane >> 5) * 4;
+        // alpha = 1 with no activation (the plain GEMM): conversion only;
+        // the choice is made once per tile, not per element
+        auto to_lds = [&](auto plain_c) {
+            constexpr bool PLAIN = decltype(plain_c)::value;
 #pragma unroll
-        for (int i = 0; i < FN; ++i)
+            for (int i = 0; i < FN; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+                for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int j = 0; j < FM; ++j) {
-                    float v[4];
+                    for (int j = 0; j < FM; ++j) {
+                        float v[4];
 #pragma unroll
-                    for (int t4 = 0; t4 < 4; ++t4) {
-                        const float x = alpha * acc.v[i][j][q * 4 + t4];
-                        v[t4] = (relu && !(x > 0.0f)) ? 0.0f : x;
+                        for (int t4 = 0; t4 < 4; ++t4) {
+                            if constexpr (PLAIN) {
+                                v[t4] = acc.v[i][j][q * 4 + t4];
+                            } else {
+                                const float x = alpha * acc.v[i][j][q * 4 + t4];
+                                v[t4] = (relu && !(x > 0.0f)) ? 0.0f : x;
+                            }
+                        }
+                        store4_lds(lds, out_off(r_loc + j * 32, (c_loc + i * 32 + q * 8) * OSZ), v);
                     }
-                    store4_lds(lds, out_off(r_loc + j * 32, (c_loc + i * 32 + q * 8) * OSZ), v);
-                }
+        };
+        if (!relu && alpha == 1.0f) to_lds(std::true_type{});
+        else to_lds(std::false_type{});
         __syncthreads();
         char *Dt = p.D + ((int64_t)tm * BM * p.N + (int64_t)tn * BN) * OSZ;
         const int64_t ld = p.N * OSZ;
