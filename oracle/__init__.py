@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-DT = {"f32": 0, "f16": 1, "bf16": 2, "f8e4m3": 3, "e8m0": 4}
+DT = {"f32": 0, "f16": 1, "bf16": 2, "f8e4m3": 3, "e8m0": 4, "f4e2m1": 5}
 LAYOUT = {"row": 0, "col": 1}
 
 _lib = None

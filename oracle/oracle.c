@@ -65,13 +65,19 @@
  * base[r + c*rows] (packed operands, leading dimension implied).
  * MX scales: X_A is [M][K/32] and X_B is [N][K/32] bytes, row-major, whatever
  * the layouts of A and B.
+ * MXFP4 ("Generating State-of-the-Art GEMMs with TorchInductor's CuteDSL
+ * backend", section 5.1 lists MXF4 beside MXFP8 in the scaled mm family): the
+ * elements are OCP FP4 E2M1 (OCP MX v1.0: sign, 2 exponent bits with bias 1,
+ * 1 fraction bit; values 0, 1/2, 1, 3/2, 2, 3, 4, 6 and their negatives), two
+ * per byte in the operand's storage order, element 2t in the low nibble of
+ * byte t; the same E8M0 block scales as MXFP8.
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F8E4M3 = 3, DT_E8M0 = 4 };
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F8E4M3 = 3, DT_E8M0 = 4, DT_F4E2M1 = 5 };
 enum { LAYOUT_ROW = 0, LAYOUT_COL = 1 };
 enum { ACT_IDENTITY = 0, ACT_RELU = 1, ACT_SIGMOID = 2, ACT_TANH = 3 };
 enum { AUX_ADD = 0, AUX_SUB = 1, AUX_MUL = 2, AUX_DIV = 3 };
@@ -116,6 +122,15 @@ static double dec_e4m3(uint32_t u) {
     return s ? -v : v;
 }
 
+/* OCP MX FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 fraction bit; exponent
+ * field 0 holds the subnormals 0 and 1/2; no infinities and no NaN, the
+ * largest magnitude is 6. */
+static double dec_e2m1(uint32_t u) {
+    int s = (u >> 3) & 1, e = (u >> 1) & 3, m = u & 1;
+    double v = (e == 0) ? ldexp((double)m, -1) : ldexp((double)(2 + m), e - 2);
+    return s ? -v : v;
+}
+
 /* OCP MX E8M0 scale: 8 exponent bits (bias 127), no sign, no fraction;
  * 0xFF is NaN, 0x00 is 2^-127. */
 static double dec_e8m0(uint32_t u) {
@@ -130,6 +145,7 @@ double oracle_decode(int dtype, uint32_t bits) {
     case DT_BF16: return dec_bf16(bits);
     case DT_F8E4M3: return dec_e4m3(bits);
     case DT_E8M0: return dec_e8m0(bits);
+    case DT_F4E2M1: return dec_e2m1(bits);
     }
     return NAN;
 }
@@ -172,6 +188,10 @@ static uint32_t load_bits(const void *base, int dtype, int64_t idx) {
     case DT_F16:
     case DT_BF16: return ((const uint16_t *)base)[idx];
     case DT_F8E4M3: return ((const uint8_t *)base)[idx];
+    case DT_F4E2M1: {   /* two per byte: element 2t in the low nibble of byte t */
+        const uint8_t b = ((const uint8_t *)base)[idx >> 1];
+        return (idx & 1) ? (uint32_t)(b >> 4) : (uint32_t)(b & 15u);
+    }
     }
     return 0;
 }
@@ -183,7 +203,7 @@ static double elem(const void *base, int dtype, int layout, int64_t rows,
     return oracle_decode(dtype, load_bits(base, dtype, idx));
 }
 
-static int valid_dtype(int d) { return d >= DT_F32 && d <= DT_F8E4M3; }
+static int valid_dtype(int d) { return (d >= DT_F32 && d <= DT_F8E4M3) || d == DT_F4E2M1; }
 
 /* MX block size along K (OCP MX v1.0). */
 #define MX_BLOCK 32
@@ -193,10 +213,12 @@ static double mx_scale(const uint8_t *x, int64_t K, int64_t r, int64_t k) {
     return x ? oracle_decode(DT_E8M0, x[r * (K / MX_BLOCK) + k / MX_BLOCK]) : 1.0;
 }
 
-/* MX needs e4m3 elements and whole blocks; both arrays or neither. */
+/* MX needs e4m3 or e2m1 elements (the same for A and B) and whole blocks;
+ * both arrays or neither. e2m1 exists only as MX elements. */
 static int mx_ok(const uint8_t *xa, const uint8_t *xb, int dtA, int dtB, int64_t K) {
-    if (!xa && !xb) return 1;
-    return xa && xb && dtA == DT_F8E4M3 && dtB == DT_F8E4M3 && K % MX_BLOCK == 0;
+    if (!xa && !xb) return dtA != DT_F4E2M1 && dtB != DT_F4E2M1;
+    return xa && xb && dtA == dtB && (dtA == DT_F8E4M3 || dtA == DT_F4E2M1) &&
+           K % MX_BLOCK == 0;
 }
 
 /* The activation of the epilogue, in fp64. */

@@ -28,13 +28,17 @@ import numpy as np
 import torch
 
 # dtype names used across the repository (they match the C enum names)
-F32, F16, BF16, F8 = "f32", "f16", "bf16", "f8e4m3"
+F32, F16, BF16, F8, F4 = "f32", "f16", "bf16", "f8e4m3", "f4e2m1"
 ROW, COL = "row", "col"
 
+# F4 operands are packed two per byte (uint8 storage, see pack_e2m1)
 TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16,
-               F8: torch.float8_e4m3fn}
+               F8: torch.float8_e4m3fn, F4: torch.uint8}
 ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, F8: 1}
 E4M3_MAX = 448.0
+# OCP FP4 E2M1 magnitudes by 3-bit code (exponent bits, fraction bit)
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+E2M1_MAX = 6.0
 
 
 def cast(x32: np.ndarray, dtype: str) -> torch.Tensor:
@@ -252,31 +256,76 @@ def config5(M: int, N: int, K: int, seed: int = 0) -> Problem:
 
 MX_BLOCK = 32
 E4M3_EMAX = 8          # largest e4m3 binade: 448 = 1.75 * 2^8
+E2M1_EMAX = 2          # largest e2m1 binade: 6 = 1.5 * 2^2
 
 
-def mx_quantize(x32: np.ndarray) -> Tuple[np.ndarray, torch.Tensor]:
+def e2m1_codes(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even cast of values to OCP FP4 E2M1 codes (sign in
+    bit 3; magnitudes beyond 6 saturate to 6): the storage cast of the MXFP4
+    elements. A tie goes to the code with a zero fraction bit."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E2M1_MAX)
+    lo = np.clip(np.searchsorted(E2M1_GRID, a, side="right") - 1, 0, 7)
+    hi = np.minimum(lo + 1, 7)
+    d_lo = a - E2M1_GRID[lo]
+    d_hi = E2M1_GRID[hi] - a
+    up = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    mag = np.where(up, hi, lo).astype(np.uint8)
+    return mag | np.where(np.signbit(x) & (mag != 0), 8, 0).astype(np.uint8)
+
+
+def pack_e2m1(codes: np.ndarray) -> torch.Tensor:
+    """Storage [R, C] 4-bit codes -> [R, C/2] bytes, element 2t of a row in
+    the low nibble of byte t (C even)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    assert c.shape[-1] % 2 == 0
+    return torch.from_numpy(np.ascontiguousarray((c[..., 0::2] & 15) | ((c[..., 1::2] & 15) << 4)))
+
+
+def unpack_e2m1(packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_e2m1: [R, C/2] bytes -> [R, C] 4-bit codes."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 15
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def mx_quantize(x32: np.ndarray, emax: int = E4M3_EMAX) -> Tuple[np.ndarray, torch.Tensor]:
     """Quantize logical [R, K] fp32 rows block by block (the MX conversion):
-    shared exponent floor(log2(amax)) - 8 per 32-element block, stored as the
-    E8M0 code e + 127 (clamped to 0..254; an all-zero block gets 127), and
-    elements x / 2^e cast to e4m3 (RNE, saturating). Returns (elements as
-    logical fp32 [R, K] before the e4m3 cast, codes [R, K/32] uint8)."""
+    shared exponent floor(log2(amax)) - emax per 32-element block (emax 8 for
+    e4m3, 2 for e2m1), stored as the E8M0 code e + 127 (clamped to 0..254; an
+    all-zero block gets 127); the elements x / 2^e are then cast to the
+    element type (RNE, saturating) by the caller. Returns (elements as
+    logical fp32 [R, K] before that cast, codes [R, K/32] uint8)."""
     R, K = x32.shape
     assert K % MX_BLOCK == 0
     blk = x32.reshape(R, K // MX_BLOCK, MX_BLOCK).astype(np.float64)
     amax = np.abs(blk).max(axis=2)
     safe = np.where(amax > 0, amax, 1.0)
-    e = np.where(amax > 0, np.floor(np.log2(safe)) - E4M3_EMAX, 0.0)
+    e = np.where(amax > 0, np.floor(np.log2(safe)) - emax, 0.0)
     code = np.clip(e + 127, 0, 254).astype(np.uint8)
     q = blk / np.exp2(code.astype(np.float64) - 127)[:, :, None]
     return q.reshape(R, K).astype(np.float32), torch.from_numpy(np.ascontiguousarray(code))
 
 
+def mx_elements(q32: np.ndarray, layout: str, elem: str) -> torch.Tensor:
+    """Logical [R, K] MX elements (already divided by their block scales) ->
+    storage: e4m3 in ``layout``, or e2m1 codes packed two per byte along K
+    (A RowMajor / B ColumnMajor only)."""
+    if elem == F8:
+        return cast(to_storage(q32, layout), F8)
+    return pack_e2m1(e2m1_codes(to_storage(q32, layout)))
+
+
 def make_mx_problem(M: int, N: int, K: int, *, la: str = ROW, lb: str = COL, lc: str = ROW,
                     dist_c: Optional[str] = None, alpha: float = 1.0, beta: float = 0.0,
                     dist_bias: Optional[str] = None, std_b: float = 1.0,
-                    seed: int = 0, rng=None) -> Problem:
-    """MXFP8 problem: A, B ~ N(0,1) (B times std_b) quantized per 32-block of
-    K; bf16 C / D. Draw order A, B, C, bias as in make_problem."""
+                    seed: int = 0, rng=None, elem: str = F8) -> Problem:
+    """MXFP8 (elem f8e4m3) or MXFP4 (elem f4e2m1) problem: A, B ~ N(0,1) (B
+    times std_b) quantized per 32-block of K; bf16 C / D. Draw order A, B, C,
+    bias as in make_problem. MXFP4 elements are packed along K, so A must be
+    RowMajor and B ColumnMajor."""
     rng = np.random.default_rng(seed) if rng is None else rng
     a32 = _draw(rng, (M, K), "normal")
     b32 = _draw(rng, (K, N), "normal", std_b)
@@ -284,21 +333,26 @@ def make_mx_problem(M: int, N: int, K: int, *, la: str = ROW, lb: str = COL, lc:
     if dist_c is not None:
         c = cast(to_storage(_draw(rng, (M, N), dist_c), lc), BF16)
     bias = cast(_draw(rng, (N,), dist_bias), BF16) if dist_bias is not None else None
-    qa, xa = mx_quantize(a32)
-    qbt, xb = mx_quantize(np.ascontiguousarray(b32.T))
-    A = cast(to_storage(qa, la), F8)
-    B = cast(to_storage(np.ascontiguousarray(qbt.T), lb), F8)
-    return Problem(M, N, K, A, B, c, alpha, beta, None, None, F8, BF16, la, lb, lc, bias,
+    emax = E4M3_EMAX if elem == F8 else E2M1_EMAX
+    if elem == F4:
+        assert la == ROW and lb == COL, "MXFP4 elements are packed along K"
+    qa, xa = mx_quantize(a32, emax)
+    qbt, xb = mx_quantize(np.ascontiguousarray(b32.T), emax)
+    A = mx_elements(qa, la, elem)
+    B = mx_elements(np.ascontiguousarray(qbt.T), lb, elem) if elem == F8 else \
+        pack_e2m1(e2m1_codes(qbt))
+    return Problem(M, N, K, A, B, c, alpha, beta, None, None, elem, BF16, la, lb, lc, bias,
                    xa, xb)
 
 
 def mx_integer_problem(M: int, N: int, K: int, *, la: str = ROW, lb: str = COL,
                        lc: str = ROW, lo: int = -2, hi: int = 2, emin: int = -2,
                        emax: int = 2, with_c: bool = True, beta: float = 1.0,
-                       with_bias: bool = False, seed: int = 0) -> Problem:
+                       with_bias: bool = False, seed: int = 0, elem: str = F8) -> Problem:
     """MX problem with integer elements in [lo, hi] and scale codes
     127 + U{emin..emax}: every scaled product and partial sum is a small
-    dyadic number, exact in fp32."""
+    dyadic number, exact in fp32. For MXFP4 (elem f4e2m1) every integer in
+    [-4, 4] is an e2m1 value; A RowMajor and B ColumnMajor."""
     rng = np.random.default_rng(seed)
     a32 = rng.integers(lo, hi + 1, size=(M, K)).astype(np.float32)
     b32 = rng.integers(lo, hi + 1, size=(K, N)).astype(np.float32)
@@ -311,9 +365,11 @@ def mx_integer_problem(M: int, N: int, K: int, *, la: str = ROW, lb: str = COL,
     nb = K // MX_BLOCK
     xa = torch.from_numpy((127 + rng.integers(emin, emax + 1, size=(M, nb))).astype(np.uint8))
     xb = torch.from_numpy((127 + rng.integers(emin, emax + 1, size=(N, nb))).astype(np.uint8))
-    A = cast(to_storage(a32, la), F8)
-    B = cast(to_storage(b32, lb), F8)
-    return Problem(M, N, K, A, B, c, 1.0, beta if with_c else 0.0, None, None, F8, BF16,
+    if elem == F4:
+        assert la == ROW and lb == COL and -4 <= lo <= hi <= 4
+    A = mx_elements(a32, la, elem)
+    B = mx_elements(b32, lb, elem) if elem == F8 else pack_e2m1(e2m1_codes(np.ascontiguousarray(b32.T)))
+    return Problem(M, N, K, A, B, c, 1.0, beta if with_c else 0.0, None, None, elem, BF16,
                    la, lb, lc, bias, xa, xb)
 
 

@@ -604,6 +604,152 @@ def test_mx_quantizer_round_trips_within_e4m3_precision():
     assert ok[~sat].all()
 
 
+# ---------------------------------------------------------------- MXFP4
+# "Generating State-of-the-Art GEMMs with TorchInductor's CuteDSL backend",
+# section 5.1, lists MXF4 beside MXFP8 in the scaled mm family; the element
+# format is OCP FP4 E2M1 (OCP MX v1.0), packed two per byte along K with
+# element 2t in the low nibble of byte t, under the same E8M0 block scales.
+
+OCP_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]     # OCP MX v1.0 FP4 magnitudes
+
+
+def test_decode_e2m1_ocp_table():
+    got = oracle.decode("f4e2m1", np.arange(16, dtype=np.uint32))
+    assert list(got[:8]) == OCP_E2M1
+    assert list(-got[8:]) == OCP_E2M1 and np.signbit(got[8:]).all()
+    # every FP4 value is an FP8 E4M3 value: torch's e4m3 cast keeps each one
+    # exactly and the (already pinned) e4m3 decoder reads it back unchanged
+    e4 = torch.tensor(got, dtype=torch.float32).to(torch.float8_e4m3fn)
+    assert np.array_equal(oracle.decode("f8e4m3", syn.raw(e4)), got)
+
+
+def test_e2m1_storage_cast_is_nearest_even():
+    # the generator's RNE cast against exhaustive nearest-value search over
+    # the decoded table (ties to the code with a zero fraction bit, beyond 6
+    # saturating), on a grid holding every midpoint
+    vals = oracle.decode("f4e2m1", np.arange(16, dtype=np.uint32))
+    x = np.concatenate([np.arange(-7.0, 7.0001, 0.125), [0.3, -2.9, 5.01, -100.0]])
+    codes = syn.e2m1_codes(x)
+    for xv, c in zip(x, codes):
+        d = np.abs(vals - min(max(xv, -6.0), 6.0))
+        best = np.flatnonzero(d == d.min())
+        if len(best) > 1:                           # a tie: the even code (or +-0)
+            best = [b for b in best if b % 2 == 0]
+        assert vals[c] == vals[best[0]], (xv, c, best)
+
+
+def test_e2m1_pack_round_trip_and_nibble_order():
+    rng = np.random.default_rng(85)
+    codes = rng.integers(0, 16, size=(3, 64)).astype(np.uint8)
+    packed = syn.pack_e2m1(codes).numpy()
+    assert packed.shape == (3, 32)
+    assert np.array_equal(syn.unpack_e2m1(packed), codes)
+    assert packed[1, 5] == codes[1, 10] | (codes[1, 11] << 4)   # element 2t low
+
+
+def _mx4_logical(q):
+    """Logical fp64 [M, K] / [K, N] element values of an MXFP4 problem, read
+    with the generator's unpacking and the OCP table (not the oracle's)."""
+    grid = np.array(OCP_E2M1)
+    def val(codes):
+        return np.where(codes & 8, -1.0, 1.0) * grid[codes & 7]
+    a = val(syn.unpack_e2m1(syn.raw(q.A)))            # [M, K]
+    b = val(syn.unpack_e2m1(syn.raw(q.B))).T          # B stored [N, K]
+    return a, b
+
+
+def test_mxfp4_equals_mxfp8_of_the_same_values():
+    # every e2m1 value is an e4m3 value, so an MXFP4 problem and the MXFP8
+    # problem holding the same element values and block scales must give the
+    # same outputs bit for bit (ties the FP4 path to the pinned FP8 one)
+    import dataclasses
+    q4 = syn.mx_integer_problem(20, 28, 192, lo=-4, hi=4, seed=86, elem="f4e2m1")
+    a, b = _mx4_logical(q4)
+    q8 = dataclasses.replace(q4, A=syn.cast(a.astype(np.float32), "f8e4m3"),
+                             B=syn.cast(np.ascontiguousarray(b.T).astype(np.float32), "f8e4m3"),
+                             dtype_ab="f8e4m3")
+    r4, r8 = oracle.gemm(q4), oracle.gemm(q8)
+    assert np.array_equal(r4.ref, r8.ref) and np.array_equal(r4.S, r8.S)
+    assert np.array_equal(r4.d_bits, r8.d_bits)
+    # and the half-precision values in between: 0.5 and 1.5 elements
+    q4b = syn.make_mx_problem(12, 16, 128, seed=87, elem="f4e2m1")
+    a, b = _mx4_logical(q4b)
+    assert (np.abs(a) % 1 == 0.5).any()
+    q8b = dataclasses.replace(q4b, A=syn.cast(a.astype(np.float32), "f8e4m3"),
+                              B=syn.cast(np.ascontiguousarray(b.T).astype(np.float32), "f8e4m3"),
+                              dtype_ab="f8e4m3")
+    assert np.array_equal(oracle.gemm(q4b).ref, oracle.gemm(q8b).ref)
+
+
+@pytest.mark.parametrize("k0", [0, 1, 30, 31, 32, 63])
+def test_mxfp4_one_hot_finds_its_element(k0):
+    # A holds one nonzero element, 3 at (2, k0); B is the K x K identity
+    # (N = K): D is 3 * X_A(2, k0/32) * X_B(k0, k0/32) at (2, k0) and zero
+    # elsewhere, so a swapped nibble order or a shifted index moves it
+    import dataclasses
+    M, K = 4, 64
+    a = np.zeros((M, K))
+    a[2, k0] = 3.0
+    b = np.eye(K)                                       # logical [K, N]
+    q = syn.mx_integer_problem(M, K, K, lo=0, hi=0, seed=88, elem="f4e2m1", with_c=False)
+    q = dataclasses.replace(q, A=syn.pack_e2m1(syn.e2m1_codes(a)),
+                            B=syn.pack_e2m1(syn.e2m1_codes(np.ascontiguousarray(b.T))))
+    r = oracle.gemm(q)
+    xa = 2.0 ** (q.mx_a.numpy().astype(np.float64) - 127)
+    xb = 2.0 ** (q.mx_b.numpy().astype(np.float64) - 127)
+    want = np.zeros((M, K))
+    want[2, k0] = 3.0 * xa[2, k0 // 32] * xb[k0, k0 // 32]
+    assert np.array_equal(r.ref, want)
+
+
+def test_mxfp4_exact_rational_brute_force():
+    for seed, (M, N, K) in enumerate([(3, 5, 32), (6, 4, 64), (2, 3, 96)]):
+        q = syn.mx_integer_problem(M, N, K, lo=-4, hi=4, seed=90 + seed, elem="f4e2m1",
+                                   with_bias=True)
+        a, b = _mx4_logical(q)
+        xa = 2.0 ** (q.mx_a.numpy().astype(np.float64) - 127)
+        xb = 2.0 ** (q.mx_b.numpy().astype(np.float64) - 127)
+        c = q.C.float().numpy().astype(np.float64)
+        bias = q.bias.float().numpy().astype(np.float64)
+        r = oracle.gemm(q, relu=True)
+        for i in range(M):
+            for j in range(N):
+                acc = sum((Fraction(a[i, k]) * Fraction(xa[i, k // 32])) *
+                          (Fraction(b[k, j]) * Fraction(xb[j, k // 32])) for k in range(K))
+                v = acc + Fraction(q.beta) * Fraction(c[i, j]) + Fraction(bias[j])
+                v = v if v > 0 else Fraction(0)
+                assert Fraction(float(r.ref[i, j])) == v, (i, j)
+
+
+def test_mxfp4_needs_block_scales():
+    import dataclasses
+    q = syn.mx_integer_problem(4, 4, 64, seed=89, elem="f4e2m1")
+    with pytest.raises(ValueError):      # FP4 elements exist only under MX scales
+        oracle.gemm(dataclasses.replace(q, mx_a=None, mx_b=None))
+    with pytest.raises(ValueError):      # whole 32-element blocks
+        oracle.gemm(dataclasses.replace(q, K=48))
+
+
+def test_mxfp4_quantizer_round_trips_within_e2m1_precision():
+    # the generator's MXFP4 conversion: every block's largest magnitude lands
+    # in e2m1's top binade [4, 6]; dequantized values sit within half an
+    # e2m1 step of the draw (steps of 2^(e-1) in binade [2^e, 2^(e+1)),
+    # 1/2 below 1), or saturate at 6 * 2^x
+    rng = np.random.default_rng(91)
+    x = rng.standard_normal((8, 256)).astype(np.float32)
+    q, codes = syn.mx_quantize(x, syn.E2M1_EMAX)
+    vals = oracle.decode("f4e2m1", np.arange(16, dtype=np.uint32))
+    qe = vals[syn.e2m1_codes(q)]
+    top = np.abs(qe).reshape(8, 8, 32).max(axis=2)
+    assert ((top >= 4) & (top <= 6)).all()
+    X = np.repeat(2.0 ** (codes.numpy().astype(np.float64) - 127), 32, axis=1)
+    s = np.abs(q.astype(np.float64))
+    step = np.where(s < 2, 0.5, np.where(s < 4, 1.0, 2.0))
+    sat = s > 6
+    assert (np.abs(qe[sat]) == 6).all()
+    assert (np.abs(qe - q)[~sat] <= step[~sat] / 2).all()
+
+
 # ---------------------------------------------------------------- auxiliary tensor
 # The epilogue-fusion kernels load and store auxiliary tensors and combine
 # them by elementwise add, subtract, multiply or divide ("Generating
