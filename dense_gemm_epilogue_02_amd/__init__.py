@@ -27,6 +27,7 @@ class Dtype(IntEnum):
     F16 = 1
     BF16 = 2
     F8_E4M3 = 3
+    F4_E2M1 = 4   # packed two per byte (uint8 tensors), MX runs only
 
 
 class Layout(IntEnum):
@@ -346,14 +347,15 @@ def gemm_version() -> str:
 
 # ---- tensor conveniences ------------------------------------------------------
 
-_TORCH_DT = {"f32": Dtype.F32, "f16": Dtype.F16, "bf16": Dtype.BF16, "f8e4m3": Dtype.F8_E4M3}
+_TORCH_DT = {"f32": Dtype.F32, "f16": Dtype.F16, "bf16": Dtype.BF16, "f8e4m3": Dtype.F8_E4M3,
+             "f4e2m1": Dtype.F4_E2M1}
 _LAYOUT = {"row": Layout.ROW_MAJOR, "col": Layout.COL_MAJOR}
 
 
 def _dtype_of(t) -> Dtype:
     import torch
     m = {torch.float32: Dtype.F32, torch.float16: Dtype.F16, torch.bfloat16: Dtype.BF16,
-         torch.float8_e4m3fn: Dtype.F8_E4M3}
+         torch.float8_e4m3fn: Dtype.F8_E4M3, torch.uint8: Dtype.F4_E2M1}
     if t.dtype not in m:
         raise TypeError(f"unsupported tensor dtype {t.dtype}")
     return m[t.dtype]
@@ -368,8 +370,9 @@ def _need(t, n: int, name: str, dtype: Dtype):
         raise ValueError(f"{name} must be contiguous (packed storage)")
     if _dtype_of(t) != dtype:
         raise TypeError(f"{name} has dtype {t.dtype}, plan expects {dtype.name}")
-    if t.numel() < n:
-        raise ValueError(f"{name} holds {t.numel()} elements, needs {n}")
+    per = 2 if dtype == Dtype.F4_E2M1 else 1   # FP4: two elements per byte
+    if t.numel() * per < n:
+        raise ValueError(f"{name} holds {t.numel() * per} elements, needs {n}")
 
 
 class Plan:
@@ -380,7 +383,7 @@ class Plan:
 
     def __init__(self, dtype_ab="bf16", dtype_cd=None, la="row", lb="row", lc="row",
                  relu: bool = False, activation: Optional[str] = None):
-        dtype_cd = dtype_cd or ("bf16" if dtype_ab == "f8e4m3" else dtype_ab)
+        dtype_cd = dtype_cd or ("bf16" if dtype_ab in ("f8e4m3", "f4e2m1") else dtype_ab)
         self.dab, self.dcd = _TORCH_DT[dtype_ab], _TORCH_DT[dtype_cd]
         if activation is None:
             epi = Epilogue.RELU if relu else Epilogue.LINEAR

@@ -56,6 +56,7 @@ const char *dtype_name(int d) {
     case GEMM_F16: return "F16";
     case GEMM_BF16: return "BF16";
     case GEMM_F8_E4M3: return "F8_E4M3";
+    case GEMM_F4_E2M1: return "F4_E2M1";
     }
     return "?";
 }
@@ -69,10 +70,18 @@ const Tuple kSupported[] = {
     {GEMM_F16, GEMM_F16, GEMM_F16, GEMM_F16, GEMM_F32, FAM_F16},
     {GEMM_BF16, GEMM_BF16, GEMM_BF16, GEMM_BF16, GEMM_F32, FAM_BF16},
     {GEMM_F8_E4M3, GEMM_F8_E4M3, GEMM_BF16, GEMM_BF16, GEMM_F32, FAM_F8},
+    // FP4 elements exist only under MX block scales (gemm_plan_run_mx)
+    {GEMM_F4_E2M1, GEMM_F4_E2M1, GEMM_BF16, GEMM_BF16, GEMM_F32, FAM_MXF4},
 };
 constexpr int kNumSupported = (int)(sizeof(kSupported) / sizeof(kSupported[0]));
 
-int elem_bytes(int fam) { return fam == FAM_F32 ? 4 : (fam == FAM_F8 || fam == FAM_MXF8) ? 1 : 2; }
+// Bytes per element as the tile engine addresses operands: FP4 operands are
+// addressed in bytes (two elements each), with K counted in bytes.
+int elem_bytes(int fam) {
+    return fam == FAM_F32 ? 4 : (fam == FAM_F8 || fam == FAM_MXF8 || fam == FAM_MXF4) ? 1 : 2;
+}
+// The kernel family of an MX run on a plan of family `fam`.
+int mx_family(int fam) { return fam == FAM_MXF4 ? FAM_MXF4 : FAM_MXF8; }
 int out_bytes(int fam) { return fam == FAM_F32 ? 4 : 2; }
 
 // ------------------------------------------------------------------ registry
@@ -81,7 +90,7 @@ struct Registry {
     std::vector<KernelEntry> all;
     Registry() {
         const KernelEntry *(*tables[])(int *) = {entries_f32, entries_f16, entries_bf16, entries_f8,
-                                                 entries_mxf8};
+                                                 entries_mxf8, entries_mxf4};
         for (auto t : tables) {
             int n = 0;
             const KernelEntry *e = t(&n);
@@ -498,9 +507,12 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
                    const void *bias, int64_t M, int64_t N, int64_t K, float beta, int cus, OccFn occ_of,
                    Decision &d, int64_t batch = 1, const void *mx_a = nullptr,
                    const void *mx_b = nullptr, size_t max_ws = 0) {
-    const int fam = mx_a ? FAM_MXF8 : pl->fam;
+    const int fam = mx_a ? mx_family(pl->fam) : pl->fam;
     const Cfg cfg = plan_cfg(pl, M, N, K, batch, mx_a != nullptr);
     const int esz = elem_bytes(fam), osz = out_bytes(fam);
+    // the tile kernels count K in their storage units: bytes for FP4
+    const int64_t K_el = K;
+    if (fam == FAM_MXF4) K = K / 2;
     const bool a_kc = pl->la == GEMM_ROW_MAJOR, b_kc = pl->lb == GEMM_COL_MAJOR;
     d.vec_cd = (pl->lc == GEMM_ROW_MAJOR && N % 4 == 0 &&
                 reinterpret_cast<uintptr_t>(D) % (4 * osz) == 0 &&
@@ -517,13 +529,15 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
             why = operand_vec_problem(A, a_kc, a_kc ? K : M, e ? e->bm : 0, esz, kb);
             if (!why) why = operand_vec_problem(B, b_kc, b_kc ? K : N, e ? e->bn : 0, esz, kb);
         }
-        // MX tile kernels copy each row's four block scales of a k-tile as one
-        // word, at a 32-bit offset
+        // MX tile kernels copy each row's block scales of a k-tile (128
+        // bytes of K: four blocks of e4m3, eight of e2m1) as whole words, at
+        // 32-bit offsets
         if (!why && mx_a &&
             (K % 128 != 0 || reinterpret_cast<uintptr_t>(mx_a) % 4 != 0 ||
              reinterpret_cast<uintptr_t>(mx_b) % 4 != 0))
-            why = "MX tile kernels need K % 128 == 0 and 4-byte aligned scale arrays";
-        if (!why && mx_a && (M * (K / 32) > 0x7FFFFFFFLL || N * (K / 32) > 0x7FFFFFFFLL))
+            why = fam == FAM_MXF4 ? "MXFP4 tile kernels need K % 256 == 0 and 4-byte aligned scale arrays"
+                                  : "MX tile kernels need K % 128 == 0 and 4-byte aligned scale arrays";
+        if (!why && mx_a && (M * (K_el / 32) > 0x7FFFFFFFLL || N * (K_el / 32) > 0x7FFFFFFFLL))
             why = "MX scale arrays beyond 2^31 bytes";
         if (e && !why) d.e = e;
         else d.why_generic = why ? why : "no tile kernel for this layout";
@@ -834,6 +848,9 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
     if (!plan_ok(pl)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_run: invalid plan handle");
     gemm_status st = validate_problem(pl, A, B, C, D, M, N, K, beta, "gemm_plan_run");
     if (st != GEMM_OK) return st;
+    if (pl->fam == FAM_MXF4 && !bt.mx_a && K > 0)
+        return fail(GEMM_UNSUPPORTED, "F4_E2M1 elements are defined only under MX block scales: "
+                    "use gemm_plan_run_mx");
     if (M == 0 || N == 0 || bt.count == 0) return ok();
     if (beta == 0.0f) C = nullptr;
     const int esz = elem_bytes(pl->fam), osz = out_bytes(pl->fam);
@@ -868,7 +885,7 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
     if (reinterpret_cast<uintptr_t>(bt.aux) % (4 * osz) != 0 ||
         reinterpret_cast<uintptr_t>(bt.aux_out) % (4 * osz) != 0)
         d.vec_cd = 0;
-    const int fam = bt.mx_a ? FAM_MXF8 : pl->fam;
+    const int fam = bt.mx_a ? mx_family(pl->fam) : pl->fam;
     Prob p = make_prob(A, B, C, D, M, N, K, d);
     p.batch = (int)bt.count;
     p.stride_a = bt.sa;
@@ -895,6 +912,7 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
     }
     KArgs a;
     a.p = p;
+    if (fam == FAM_MXF4) a.p.K = K / 2;   // the tile kernels address FP4 operands in bytes
     a.e = ep;
     a.s.grid = d.grid;
     a.s.total_tiles = d.total;
@@ -1015,7 +1033,8 @@ gemm_status gemm_plan_create(gemm_plan_t *out, gemm_dtype a, gemm_dtype b, gemm_
         return fail(GEMM_UNSUPPORTED,
                     "gemm_plan_create: element tuple (A=%s, B=%s, C=%s, D=%s, accumulator=%s) is not "
                     "supported; supported: (F32,F32,F32,F32,F32), (F16,F16,F16,F16,F32), "
-                    "(BF16,BF16,BF16,BF16,F32), (F8_E4M3,F8_E4M3,BF16,BF16,F32)",
+                    "(BF16,BF16,BF16,BF16,F32), (F8_E4M3,F8_E4M3,BF16,BF16,F32), "
+                    "(F4_E2M1,F4_E2M1,BF16,BF16,F32)",
                     dtype_name(a), dtype_name(b), dtype_name(c), dtype_name(d), dtype_name(acc));
     gemm_plan_s *p = new (std::nothrow) gemm_plan_s();
     if (!p) return fail(GEMM_OUT_OF_MEMORY, "gemm_plan_create: host allocation failed");
@@ -1130,8 +1149,9 @@ gemm_status gemm_plan_run_mx(gemm_plan_t p, const void *A, const void *B, const 
                              float beta, const uint8_t *mx_scale_a, const uint8_t *mx_scale_b,
                              void *stream) {
     if (!plan_ok(p)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_run_mx: invalid plan handle");
-    if (p->fam != FAM_F8)
-        return fail(GEMM_UNSUPPORTED, "gemm_plan_run_mx: MX block scaling needs an F8_E4M3 plan");
+    if (p->fam != FAM_F8 && p->fam != FAM_MXF4)
+        return fail(GEMM_UNSUPPORTED,
+                    "gemm_plan_run_mx: MX block scaling needs an F8_E4M3 or F4_E2M1 plan");
     if (K % 32 != 0)
         return fail(GEMM_INVALID_ARG, "gemm_plan_run_mx: K = %lld is not a multiple of the "
                     "32-element MX block", (long long)K);
@@ -1176,6 +1196,9 @@ gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32
                              float beta, void *stream) {
     if (!plan_ok(pl)) return fail(GEMM_NOT_INITIALIZED, "grouped_gemm_run: invalid plan handle");
     if (count < 0) return fail(GEMM_INVALID_ARG, "grouped_gemm_run: count < 0");
+    if (pl->fam == FAM_MXF4)
+        return fail(GEMM_UNSUPPORTED, "grouped_gemm_run: F4_E2M1 needs MX block scales, which "
+                    "grouped GEMM does not take");
     if (count > 0 && !problems) return fail(GEMM_INVALID_ARG, "grouped_gemm_run: problems is NULL");
     for (int32_t i = 0; i < count; ++i) {
         const gemm_problem &q = problems[i];

@@ -47,8 +47,11 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 // FAM_MXF8: e4m3 operands with MX block scales (one E8M0 scale per 32
-// elements along K, per row of A and per column of B).
-enum Family { FAM_F32 = 0, FAM_F16 = 1, FAM_BF16 = 2, FAM_F8 = 3, FAM_MXF8 = 4 };
+// elements along K, per row of A and per column of B). FAM_MXF4: e2m1
+// operands, two per byte along K (element 2t in the low nibble of byte t),
+// under the same block scales; the tile engine addresses them as bytes (the
+// host passes K in bytes), a 16-byte chunk being one 32-element block.
+enum Family { FAM_F32 = 0, FAM_F16 = 1, FAM_BF16 = 2, FAM_F8 = 3, FAM_MXF8 = 4, FAM_MXF4 = 5 };
 
 constexpr uint32_t OOB_OFFSET = 0x80000000u;
 constexpr int NUM_RECORDS = 0x7FFFFFFF;
@@ -61,6 +64,7 @@ template <int FAM> struct Fam;
 template <> struct Fam<FAM_BF16> {
     static constexpr int ESZ = 2, CPL = 1;
     static constexpr bool MX = false;
+    static constexpr int SCW = 0;
     using Out = __bf16;
     static __device__ __forceinline__ void mma(f32x16 &c, const u32x4 *x, const u32x4 *y) {
         c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[0]),
@@ -70,6 +74,7 @@ template <> struct Fam<FAM_BF16> {
 template <> struct Fam<FAM_F16> {
     static constexpr int ESZ = 2, CPL = 1;
     static constexpr bool MX = false;
+    static constexpr int SCW = 0;
     using Out = _Float16;
     static __device__ __forceinline__ void mma(f32x16 &c, const u32x4 *x, const u32x4 *y) {
         c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x[0]),
@@ -79,6 +84,7 @@ template <> struct Fam<FAM_F16> {
 template <> struct Fam<FAM_F32> {
     static constexpr int ESZ = 4, CPL = 1;
     static constexpr bool MX = false;
+    static constexpr int SCW = 0;
     using Out = float;
     static __device__ __forceinline__ void mma(f32x16 &c, const u32x4 *x, const u32x4 *y) {
         const f32x4 xv = __builtin_bit_cast(f32x4, x[0]);
@@ -92,6 +98,7 @@ template <> struct Fam<FAM_F32> {
 template <> struct Fam<FAM_F8> {
     static constexpr int ESZ = 1, CPL = 2;
     static constexpr bool MX = false;
+    static constexpr int SCW = 0;
     using Out = __bf16;
     static __device__ __forceinline__ void mma(f32x16 &c, const u32x4 *x, const u32x4 *y) {
         i32x8 a, b;
@@ -113,6 +120,7 @@ template <> struct Fam<FAM_F8> {
 template <> struct Fam<FAM_MXF8> {
     static constexpr int ESZ = 1, CPL = 2;
     static constexpr bool MX = true;
+    static constexpr int SCW = 1;   // 32-bit scale words per row per k-tile (4 blocks)
     using Out = __bf16;
     template <int OPSEL>
     static __device__ __forceinline__ void mma_mx(f32x16 &c, const u32x4 *x, const u32x4 *y,
@@ -124,6 +132,29 @@ template <> struct Fam<FAM_MXF8> {
             b[e] = (int)y[0][e]; b[e + 4] = (int)y[1][e];
         }
         c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPSEL, (int)sx, OPSEL,
+                                                             (int)sy);
+    }
+};
+
+// The 32x32x64 scaled MFMA with FP4 operands reads, in lane l, 16 bytes (32
+// elements) of row l%32 that all belong to hardware block l/32 -- its 64 K
+// positions are two 32-element blocks, one per lane half (lane layout
+// measured on gfx950) -- and takes the scale of (row r, block b) from lane
+// r + 32b as for FP8. Lane group g of substep s reads chunk 2s + g of the
+// k-tile's 128-byte row: exactly the k-tile's block 2s + g.
+template <> struct Fam<FAM_MXF4> {
+    static constexpr int ESZ = 1, CPL = 1;
+    static constexpr bool MX = true;
+    static constexpr int SCW = 2;   // 32-bit scale words per row per k-tile (8 blocks)
+    using Out = __bf16;
+    template <int OPSEL>
+    static __device__ __forceinline__ void mma_mx(f32x16 &c, const u32x4 *x, const u32x4 *y,
+                                                  uint32_t sx, uint32_t sy) {
+        const i32x8 a = {(int)x[0][0], (int)x[0][1], (int)x[0][2], (int)x[0][3], 0, 0, 0, 0};
+        const i32x8 b = {(int)y[0][0], (int)y[0][1], (int)y[0][2], (int)y[0][3], 0, 0, 0, 0};
+        // format 4 = FP4 E2M1 for both operands (the unused upper half of
+        // each operand is not read)
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, OPSEL, (int)sx, OPSEL,
                                                              (int)sy);
     }
 };
@@ -545,11 +576,13 @@ struct Tile {
     // LDS: [A stage 0 .. A stage S-1 | B stage 0 .. B stage S-1]
     static constexpr int A_BYTES = BM * KB, B_BYTES = BN * KB;
     static constexpr int B_OFF = STAGES * A_BYTES;
-    // MX: each stage also holds one 32-bit word of E8M0 scales (the k-tile's
-    // four blocks) per tile row of A and of B, each region padded to whole
-    // 64-lane copy instructions.
-    static constexpr int SC_A = MX ? (BM + 63) / 64 * 256 : 0;
-    static constexpr int SC_B = MX ? (BN + 63) / 64 * 256 : 0;
+    // MX: each stage also holds SCW 32-bit words of E8M0 scales per tile row
+    // of A and of B (the k-tile's 4 * SCW blocks; word w of row r at
+    // (w * rows + r) * 4, rows padded to whole 64-lane copy instructions).
+    static constexpr int SCW = MX ? Fam<FAM>::SCW : 0;
+    static constexpr int ROWS_A = (BM + 63) / 64 * 64, ROWS_B = (BN + 63) / 64 * 64;
+    static constexpr int SC_A = SCW * ROWS_A * 4;
+    static constexpr int SC_B = SCW * ROWS_B * 4;
     static constexpr int SC_OFF = STAGES * (A_BYTES + B_BYTES);
     static constexpr int LDS_BYTES = STAGES * (A_BYTES + B_BYTES + SC_A + SC_B);
     static_assert(CH == 8 || CH == 4, "64- or 128-byte LDS rows");
@@ -583,22 +616,25 @@ struct Tile {
 
     // MX: copy the k-tile's scale words of the tile's rows of A and B into
     // the stage (LDS DMA, 4 bytes a lane; rows past the edge read as zero).
-    // Byte b of a row's word is the scale of the k-tile's block b.
+    // Byte b of a row's word w is the scale of the k-tile's block 4w + b.
     static __device__ __forceinline__ void issue_scales(const Prob &p, int tm, int tn, int kt,
                                                         char *sc, int tid) {
-        constexpr int IA = SC_A / 256, IB = SC_B / 256, CW = COPY_NT / 64;
+        constexpr int GA = ROWS_A / 64, GB = ROWS_B / 64, CW = COPY_NT / 64;
+        constexpr int EPB = FAM == FAM_MXF4 ? 2 : 1;   // elements per operand byte
         const int lane = tid & 63, wave = uniform(tid >> 6);
-        const uint32_t nb = (uint32_t)(p.K >> 5);   // scale bytes per row
+        const uint32_t nb = (uint32_t)((p.K * EPB) >> 5);   // scale bytes per row
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.mx_a), rb = make_rsrc(p.mx_b);
-        for (int q = wave; q < IA + IB; q += CW) {
-            const bool is_a = q < IA;
-            const int row = (is_a ? q : q - IA) * 64 + lane;
+        for (int q = wave; q < SCW * (GA + GB); q += CW) {
+            const int w = q / (GA + GB), qq = q - w * (GA + GB);
+            const bool is_a = qq < GA;
+            const int row = (is_a ? qq : qq - GA) * 64 + lane;
             const int64_t g_row = is_a ? (int64_t)tm * BM + row : (int64_t)tn * BN + row;
             const bool ok = row < (is_a ? BM : BN) && g_row < (is_a ? p.M : p.N);
             const uint32_t voff = ok ? (uint32_t)g_row * nb : OOB_OFFSET;
+            char *dst = sc + (is_a ? 0 : SC_A) + (w * (is_a ? ROWS_A : ROWS_B) + row - lane) * 4;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                is_a ? ra : rb, (__attribute__((address_space(3))) void *)(sc + q * 256), 4, voff,
-                kt * 4, 0, 0);
+                is_a ? ra : rb, (__attribute__((address_space(3))) void *)dst, 4, voff,
+                kt * 4 * SCW + 4 * w, 0, 0);
         }
     }
 
@@ -765,18 +801,23 @@ struct Tile {
                                                    int lane, int wm, int wn,
                                                    const char *sSc = nullptr) {
         const int g = lane >> 5, r = lane & 31;
-        // MX: this lane's scale words, shifted so byte 2s is the block its
-        // lane group multiplies in substep s
-        uint32_t scx[FN], scy[FM];
+        // MX: this lane's scale words, shifted so byte 2(s % 2) of word s / 2
+        // is the block 2s + g its lane group multiplies in substep s
+        uint32_t scx[SCW > 0 ? SCW : 1][FN], scy[SCW > 0 ? SCW : 1][FM];
         if constexpr (MX) {
 #pragma unroll
-            for (int i = 0; i < FN; ++i)
-                scx[i] = *reinterpret_cast<const uint32_t *>(sSc + SC_A + (wn * WTN + i * 32 + r) * 4) >>
-                         (8 * g);
+            for (int w = 0; w < SCW; ++w) {
 #pragma unroll
-            for (int j = 0; j < FM; ++j)
-                scy[j] = *reinterpret_cast<const uint32_t *>(sSc + (wm * WTM + j * 32 + r) * 4) >>
-                         (8 * g);
+                for (int i = 0; i < FN; ++i)
+                    scx[w][i] = *reinterpret_cast<const uint32_t *>(
+                                    sSc + SC_A + (w * ROWS_B + wn * WTN + i * 32 + r) * 4) >>
+                                (8 * g);
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    scy[w][j] = *reinterpret_cast<const uint32_t *>(
+                                    sSc + (w * ROWS_A + wm * WTM + j * 32 + r) * 4) >>
+                                (8 * g);
+            }
         }
 #pragma unroll
         for (int s = 0; s < SUBSTEPS; ++s) {
@@ -802,8 +843,11 @@ struct Tile {
 #pragma unroll
                 for (int j = 0; j < FM; ++j) {
                     if constexpr (MX) {
-                        if (s == 0) F::template mma_mx<0>(acc.v[i][j], xf[i], yf[j], scx[i], scy[j]);
-                        else F::template mma_mx<2>(acc.v[i][j], xf[i], yf[j], scx[i], scy[j]);
+                        const int w = s / 2 < SCW ? s / 2 : 0;
+                        if (s % 2 == 0)
+                            F::template mma_mx<0>(acc.v[i][j], xf[i], yf[j], scx[w][i], scy[w][j]);
+                        else
+                            F::template mma_mx<2>(acc.v[i][j], xf[i], yf[j], scx[w][i], scy[w][j]);
                     } else {
                         F::mma(acc.v[i][j], xf[i], yf[j]);
                     }

@@ -51,6 +51,7 @@ const KernelEntry *entries_f16(int *count);
 const KernelEntry *entries_f32(int *count);
 const KernelEntry *entries_f8(int *count);
 const KernelEntry *entries_mxf8(int *count);
+const KernelEntry *entries_mxf4(int *count);
 
 // Scalar-load kernel for any alignment / stride (kernels_generic.hip).
 struct GenericArgs {

@@ -26,6 +26,13 @@ __device__ __forceinline__ float decode_e4m3(uint32_t u) {
     else v = __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
     return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) | s);
 }
+// OCP FP4 E2M1: sign, 2-bit exponent (bias 1), 1-bit fraction; exponent 0
+// holds 0 and 1/2, the largest magnitude is 6; no NaN or infinity.
+__device__ __forceinline__ float decode_e2m1(uint32_t u) {
+    const uint32_t e = (u >> 1) & 3u, m = u & 1u;
+    const float v = e == 0u ? 0.5f * (float)m : (float)(2u + m) * (float)(1u << e) * 0.25f;
+    return (u & 8u) ? -v : v;
+}
 // OCP MX E8M0 scale: 2^(c-127); c = 0 is the fp32 subnormal 2^-127, 255 is NaN.
 __device__ __forceinline__ float e8m0(uint32_t c) {
     if (c == 255u) return __builtin_nanf("");
@@ -38,6 +45,7 @@ template <> struct OutT<FAM_F16> { using T = _Float16; };
 template <> struct OutT<FAM_BF16> { using T = __bf16; };
 template <> struct OutT<FAM_F8> { using T = __bf16; };
 template <> struct OutT<FAM_MXF8> { using T = __bf16; };
+template <> struct OutT<FAM_MXF4> { using T = __bf16; };
 
 // Raw storage bits of one element (decoded only when staged into LDS, so
 // the loads of several k-steps can be in flight at once).
@@ -60,6 +68,11 @@ template <> __device__ __forceinline__ float decode_raw<FAM_BF16>(uint32_t b) {
 template <> __device__ __forceinline__ float decode_raw<FAM_F8>(uint32_t b) {
     return decode_e4m3(b & 0xFFu);
 }
+// FP4: the fetch already extracted the element's nibble
+template <> struct RawT<FAM_MXF4> { using T = uint8_t; };
+template <> __device__ __forceinline__ float decode_raw<FAM_MXF4>(uint32_t b) {
+    return decode_e2m1(b & 15u);
+}
 
 // k-steps whose loads are in flight ahead of the one being multiplied.
 constexpr int GPF = 4;
@@ -68,6 +81,7 @@ template <int FAM>
 __global__ void __launch_bounds__(256) gemm_generic(GenericArgs a) {
     using Out = typename OutT<FAM>::T;
     constexpr int LF = FAM == FAM_MXF8 ? FAM_F8 : FAM;   // element decoder
+    constexpr bool MX = FAM == FAM_MXF8 || FAM == FAM_MXF4;
     using Raw = typename RawT<LF>::T;
     __shared__ float As[GK][GT + 1];
     __shared__ float Bs[GK][GT + 1];
@@ -91,9 +105,16 @@ __global__ void __launch_bounds__(256) gemm_generic(GenericArgs a) {
             const int64_t k = k0 + kk;
             const int64_t m = m0 + rr, n = n0 + rr;
             const bool ina = k < p.K && m < p.M, inb = k < p.K && n < p.N;
-            va[u] = ina ? (uint32_t)Ar[a.la_row ? m * p.K + k : m + k * p.M] : 0u;
-            vb[u] = inb ? (uint32_t)Br[a.lb_row ? k * p.N + n : k + n * p.K] : 0u;
-            if constexpr (FAM == FAM_MXF8) {
+            const int64_t ia = a.la_row ? m * p.K + k : m + k * p.M;
+            const int64_t ib = a.lb_row ? k * p.N + n : k + n * p.K;
+            if constexpr (FAM == FAM_MXF4) {   // element t: nibble t & 1 of byte t / 2
+                va[u] = ina ? ((uint32_t)Ar[ia >> 1] >> (4 * (ia & 1))) & 15u : 0u;
+                vb[u] = inb ? ((uint32_t)Br[ib >> 1] >> (4 * (ib & 1))) & 15u : 0u;
+            } else {
+                va[u] = ina ? (uint32_t)Ar[ia] : 0u;
+                vb[u] = inb ? (uint32_t)Br[ib] : 0u;
+            }
+            if constexpr (MX) {
                 sa[u] = ina ? (uint32_t)p.mx_a[m * (p.K >> 5) + (k >> 5)] : 127u;
                 sb[u] = inb ? (uint32_t)p.mx_b[n * (p.K >> 5) + (k >> 5)] : 127u;
             }
@@ -113,7 +134,7 @@ __global__ void __launch_bounds__(256) gemm_generic(GenericArgs a) {
                 const int e = tid + w * 256;
                 const int kk = e / GT, rr = e % GT;
                 float av = decode_raw<LF>(ra[u][w]), bv = decode_raw<LF>(rb[u][w]);
-                if constexpr (FAM == FAM_MXF8) {
+                if constexpr (MX) {
                     // block scales of A's row and B's column (K % 32 == 0); a
                     // power of two, so the scaled element is exact
                     av *= e8m0(xa[u][w]);
@@ -181,6 +202,7 @@ hipError_t launch_generic(int fam, const GenericArgs &a, hipStream_t st) {
     case FAM_BF16: hipLaunchKernelGGL(gemm_generic<FAM_BF16>, grid, block, 0, st, a); break;
     case FAM_F8: hipLaunchKernelGGL(gemm_generic<FAM_F8>, grid, block, 0, st, a); break;
     case FAM_MXF8: hipLaunchKernelGGL(gemm_generic<FAM_MXF8>, grid, block, 0, st, a); break;
+    case FAM_MXF4: hipLaunchKernelGGL(gemm_generic<FAM_MXF4>, grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

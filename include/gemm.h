@@ -64,7 +64,10 @@ typedef enum {
     GEMM_F32 = 0,
     GEMM_F16 = 1,
     GEMM_BF16 = 2,
-    GEMM_F8_E4M3 = 3 /* OCP FP8 E4M3 (e4m3fn: bias 7, max 448, no Inf) */
+    GEMM_F8_E4M3 = 3, /* OCP FP8 E4M3 (e4m3fn: bias 7, max 448, no Inf) */
+    GEMM_F4_E2M1 = 4  /* OCP FP4 E2M1 (bias 1, max 6, no Inf/NaN), two per byte
+                         along K, element 2t in the low nibble of byte t; only
+                         as MX block-scaled elements (gemm_plan_run_mx) */
 } gemm_dtype;
 
 typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout;
@@ -118,7 +121,10 @@ typedef struct gemm_plan_s *gemm_plan_t;
 /* Create a plan binding the element types, layouts and epilogue.
  * Supported (element_A, element_B, element_C, element_D, element_accumulator):
  *   (F32, F32, F32, F32, F32), (F16, F16, F16, F16, F32),
- *   (BF16, BF16, BF16, BF16, F32), (F8_E4M3, F8_E4M3, BF16, BF16, F32).
+ *   (BF16, BF16, BF16, BF16, F32), (F8_E4M3, F8_E4M3, BF16, BF16, F32),
+ *   (F4_E2M1, F4_E2M1, BF16, BF16, F32) -- the last for MXFP4 runs only
+ *   (gemm_plan_run_mx; every other run call on it returns GEMM_UNSUPPORTED
+ *   unless K == 0).
  * Others return GEMM_UNSUPPORTED naming the tuple. Makes no device call.
  * On success *out owns host memory until gemm_plan_destroy. */
 gemm_status gemm_plan_create(gemm_plan_t *out, gemm_dtype element_a,
@@ -211,6 +217,12 @@ gemm_status gemm_plan_run_ex(gemm_plan_t plan, const void *A, const void *B,
  * K must be a multiple of 32 (else GEMM_INVALID_ARG); the MFMA tile kernels
  * run when K % 128 == 0 and both scale arrays are 4-byte aligned, otherwise
  * the scalar kernel does. bias as in gemm_plan_run_ex. No per-tensor scales.
+ * MXFP4 (the same section lists MXF4 beside MXFP8): on a (F4_E2M1, F4_E2M1,
+ * BF16, BF16, F32) plan A and B hold OCP FP4 E2M1 elements packed two per
+ * byte in their storage order (element 2t in the low nibble of byte t), the
+ * scales and the formula unchanged; the MFMA tile kernels take A RowMajor
+ * and B ColumnMajor (both packed along K) with K % 256 == 0, every other
+ * case runs on the scalar kernel.
  * A NULL scale array with M, N, K > 0 gives GEMM_INVALID_ARG; a plan of
  * another type tuple gives GEMM_UNSUPPORTED. Buffers stay the caller's. */
 gemm_status gemm_plan_run_mx(gemm_plan_t plan, const void *A, const void *B,

@@ -40,7 +40,8 @@ def tolerance(dtype_ab: str, dtype_d: str, ref, S) -> np.ndarray:
     S = np.asarray(S, dtype=np.float64)
     if dtype_d == "f32":
         return 1e-5 * S + 1e-6 + 2.0 * ulp("f32", ref)
-    rel = 1.5e-2 if dtype_ab == "f8e4m3" else 2e-3
+    # the fp8-input row of the tolerances also covers FP4 (MXFP4) inputs
+    rel = 1.5e-2 if dtype_ab in ("f8e4m3", "f4e2m1") else 2e-3
     return 2.0 * ulp(dtype_d, ref) + rel * S
 
 

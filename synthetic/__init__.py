@@ -310,9 +310,10 @@ def mx_quantize(x32: np.ndarray, emax: int = E4M3_EMAX) -> Tuple[np.ndarray, tor
 
 
 def mx_elements(q32: np.ndarray, layout: str, elem: str) -> torch.Tensor:
-    """Logical [R, K] MX elements (already divided by their block scales) ->
-    storage: e4m3 in ``layout``, or e2m1 codes packed two per byte along K
-    (A RowMajor / B ColumnMajor only)."""
+    """Logical MX elements (already divided by their block scales) ->
+    storage in ``layout``: e4m3, or e2m1 codes packed two per byte along the
+    storage's contiguous dimension (along K for A RowMajor / B ColumnMajor,
+    the layouts the FP4 tile kernels take)."""
     if elem == F8:
         return cast(to_storage(q32, layout), F8)
     return pack_e2m1(e2m1_codes(to_storage(q32, layout)))
@@ -324,8 +325,8 @@ def make_mx_problem(M: int, N: int, K: int, *, la: str = ROW, lb: str = COL, lc:
                     seed: int = 0, rng=None, elem: str = F8) -> Problem:
     """MXFP8 (elem f8e4m3) or MXFP4 (elem f4e2m1) problem: A, B ~ N(0,1) (B
     times std_b) quantized per 32-block of K; bf16 C / D. Draw order A, B, C,
-    bias as in make_problem. MXFP4 elements are packed along K, so A must be
-    RowMajor and B ColumnMajor."""
+    bias as in make_problem. MXFP4 elements are packed two per byte along
+    each operand's contiguous dimension (see mx_elements)."""
     rng = np.random.default_rng(seed) if rng is None else rng
     a32 = _draw(rng, (M, K), "normal")
     b32 = _draw(rng, (K, N), "normal", std_b)
@@ -334,13 +335,10 @@ def make_mx_problem(M: int, N: int, K: int, *, la: str = ROW, lb: str = COL, lc:
         c = cast(to_storage(_draw(rng, (M, N), dist_c), lc), BF16)
     bias = cast(_draw(rng, (N,), dist_bias), BF16) if dist_bias is not None else None
     emax = E4M3_EMAX if elem == F8 else E2M1_EMAX
-    if elem == F4:
-        assert la == ROW and lb == COL, "MXFP4 elements are packed along K"
     qa, xa = mx_quantize(a32, emax)
     qbt, xb = mx_quantize(np.ascontiguousarray(b32.T), emax)
     A = mx_elements(qa, la, elem)
-    B = mx_elements(np.ascontiguousarray(qbt.T), lb, elem) if elem == F8 else \
-        pack_e2m1(e2m1_codes(qbt))
+    B = mx_elements(np.ascontiguousarray(qbt.T), lb, elem)
     return Problem(M, N, K, A, B, c, alpha, beta, None, None, elem, BF16, la, lb, lc, bias,
                    xa, xb)
 
@@ -352,7 +350,7 @@ def mx_integer_problem(M: int, N: int, K: int, *, la: str = ROW, lb: str = COL,
     """MX problem with integer elements in [lo, hi] and scale codes
     127 + U{emin..emax}: every scaled product and partial sum is a small
     dyadic number, exact in fp32. For MXFP4 (elem f4e2m1) every integer in
-    [-4, 4] is an e2m1 value; A RowMajor and B ColumnMajor."""
+    [-4, 4] is an e2m1 value."""
     rng = np.random.default_rng(seed)
     a32 = rng.integers(lo, hi + 1, size=(M, K)).astype(np.float32)
     b32 = rng.integers(lo, hi + 1, size=(K, N)).astype(np.float32)
@@ -366,9 +364,9 @@ def mx_integer_problem(M: int, N: int, K: int, *, la: str = ROW, lb: str = COL,
     xa = torch.from_numpy((127 + rng.integers(emin, emax + 1, size=(M, nb))).astype(np.uint8))
     xb = torch.from_numpy((127 + rng.integers(emin, emax + 1, size=(N, nb))).astype(np.uint8))
     if elem == F4:
-        assert la == ROW and lb == COL and -4 <= lo <= hi <= 4
+        assert -4 <= lo <= hi <= 4
     A = mx_elements(a32, la, elem)
-    B = mx_elements(b32, lb, elem) if elem == F8 else pack_e2m1(e2m1_codes(np.ascontiguousarray(b32.T)))
+    B = mx_elements(b32, lb, elem)
     return Problem(M, N, K, A, B, c, 1.0, beta if with_c else 0.0, None, None, elem, BF16,
                    la, lb, lc, bias, xa, xb)
 
@@ -403,6 +401,52 @@ def mx_layer_device(name: str, device, seed: int = 0):
     del a
     w = torch.randn((N, K), generator=gen, device=device, dtype=torch.float32) * 0.02
     B, xb = mx_quantize_device(w)
+    return M, N, K, A, B, xa, xb
+
+
+def mx4_quantize_device(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The MXFP4 conversion of mx_quantize / e2m1_codes / pack_e2m1 done with
+    torch ops on x's device (full-size benchmark inputs): logical [R, K] rows
+    -> (e2m1 codes packed two per byte along K [R, K/2] uint8, E8M0 codes
+    [R, K/32] uint8); same shared-exponent rule (emax 2), RNE saturating
+    element cast with ties to the even code."""
+    R, K = x.shape
+    assert K % MX_BLOCK == 0
+    blk = x.float().reshape(R, K // MX_BLOCK, MX_BLOCK)
+    amax = blk.abs().amax(dim=2)
+    e = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax,
+                                                                  torch.ones_like(amax))))
+                    - E2M1_EMAX, torch.zeros_like(amax))
+    code = (e + 127).clamp(0, 254)
+    q = (blk / torch.exp2(code - 127).unsqueeze(2)).reshape(R, K)
+    del blk
+    grid = torch.tensor(E2M1_GRID, dtype=torch.float32, device=x.device)
+    a = q.abs().clamp(max=E2M1_MAX)
+    lo = (torch.bucketize(a, grid, right=True) - 1).clamp(0, 7)
+    hi = (lo + 1).clamp(max=7)
+    d_lo = a - grid[lo]
+    d_hi = grid[hi] - a
+    up = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    mag = torch.where(up, hi, lo).to(torch.uint8)
+    del a, d_lo, d_hi, up, lo, hi
+    c = mag | torch.where(torch.signbit(q) & (mag != 0), 8, 0).to(torch.uint8)
+    del q, mag
+    packed = (c[:, 0::2] & 15) | ((c[:, 1::2] & 15) << 4)
+    return packed.contiguous(), code.to(torch.uint8).contiguous()
+
+
+def mx4_layer_device(name: str, device, seed: int = 0):
+    """MXFP4 version of a transformer-layer GEMM, drawn on ``device`` like
+    mx_layer_device and MXFP4-quantized along K. Returns (M, N, K, A, B,
+    scales_a, scales_b) with A [M, K/2] and B [N, K/2] packed bytes."""
+    M, N, K = LAYER_SHAPES[name]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    a = torch.randn((M, K), generator=gen, device=device, dtype=torch.float32)
+    A, xa = mx4_quantize_device(a)
+    del a
+    w = torch.randn((N, K), generator=gen, device=device, dtype=torch.float32) * 0.02
+    B, xb = mx4_quantize_device(w)
     return M, N, K, A, B, xa, xb
 
 
