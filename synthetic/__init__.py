@@ -371,6 +371,38 @@ def mx_integer_problem(M: int, N: int, K: int, *, la: str = ROW, lb: str = COL,
                    la, lb, lc, bias, xa, xb)
 
 
+def config4_device(name: str, device, seed: int = 0, lb: str = COL):
+    """config4 drawn with torch on ``device`` (full-size benchmark inputs; the
+    same distributions, another generator): A ~ N(0,1) [M, K] bf16, W ~
+    N(0, 0.02^2) stored [N, K] (lb ColumnMajor) or [K, N] (lb RowMajor).
+    Returns (M, N, K, A, B)."""
+    M, N, K = LAYER_SHAPES[name]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    A = torch.randn((M, K), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    w = torch.randn((N, K), generator=gen, device=device, dtype=torch.float32).mul_(0.02)
+    B = (w if lb == COL else w.t()).to(torch.bfloat16).contiguous()
+    del w
+    return M, N, K, A, B
+
+
+def config5_device(M: int, N: int, K: int, device, seed: int = 0):
+    """config5 drawn with torch on ``device``: A [M, K] and B stored [N, K],
+    N(0,1) entries, each quantized to e4m3 with the per-tensor scale rule of
+    quantize_e4m3 (s = amax / 448). Returns (A, B, s_a, s_b)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = []
+    for shape in ((M, K), (N, K)):
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        amax = float(x.abs().max())
+        s = amax / E4M3_MAX if amax > 0 else 1.0
+        out.append((x.div_(s).to(torch.float8_e4m3fn), float(np.float32(s))))
+        del x
+    (A, sa), (B, sb) = out
+    return A, B, sa, sb
+
+
 def mx_quantize_device(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     """The MX conversion of mx_quantize done with torch ops on x's device
     (for full-size benchmark inputs): logical [R, K] rows -> (e4m3 elements
