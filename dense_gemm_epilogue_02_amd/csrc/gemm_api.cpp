@@ -924,6 +924,8 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
     a.s.split = d.split;
     a.s.partials = nullptr;
     a.s.counters = nullptr;
+    a.s.gdesc = nullptr;
+    a.s.gcount = 0;
     if (d.sk_tiles > 0 && d.split != 1) {
         const size_t pbytes = (size_t)2 * d.grid * d.e->bm * d.e->bn * sizeof(float);
         if (bt.noalloc) {
@@ -1216,13 +1218,22 @@ gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32
     if ((st = device_cus(dev, &cus)) != GEMM_OK) return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool a_kc = pl->la == GEMM_ROW_MAJOR, b_kc = pl->lb == GEMM_COL_MAJOR;
-    const KernelEntry *e = registry().find(pl->fam, a_kc, b_kc, TILE_128x128);
     const int esz = elem_bytes(pl->fam), osz = out_bytes(pl->fam);
     const EpiArgs ep = make_epi(pl, alpha, beta, nullptr, nullptr, nullptr);
 
-    std::vector<GroupDesc> table;
+    // Tile classes, one persistent launch each (256x256 only when the plan
+    // pins that tile; problems it cannot take fall back to 128x128).
+    struct Class {
+        const KernelEntry *e;
+        std::vector<GroupDesc> table;
+        int64_t total;
+    };
+    Class cls[2];
+    cls[0].e = registry().find(pl->fam, a_kc, b_kc, TILE_256x256);
+    cls[1].e = registry().find(pl->fam, a_kc, b_kc, TILE_128x128);
+    for (Class &c : cls) c.total = 0;
+    const bool generic_only = pl->tile == GEMM_TILE_GENERIC;
     std::vector<int32_t> scalar_path;
-    int64_t total = 0;
     // Tiles are dealt round-robin to the persistent workgroups in table
     // order; listing the problems by decreasing K (the cost of each of their
     // tiles) gives every round tiles of similar cost, so the workgroups finish
@@ -1235,15 +1246,26 @@ gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32
         const gemm_problem &q = problems[i];
         if (q.M == 0 || q.N == 0) continue;
         const void *C = beta == 0.0f ? nullptr : q.C;
-        const char *why = (e && e->fn_grouped && pl->tile != GEMM_TILE_GENERIC) ? nullptr : "no grouped kernel";
-        if (!why && q.K > 0) {
-            why = operand_vec_problem(q.A, a_kc, a_kc ? q.K : q.M, e->bm, esz, e->bk * esz);
-            if (!why) why = operand_vec_problem(q.B, b_kc, b_kc ? q.K : q.N, e->bn, esz, e->bk * esz);
+        // class: 128x128 (two workgroups per CU), which beat 256x256 tiles on
+        // grouped problem mixes up to 2048 x 4096 x 4096 (1.47x on the
+        // 64-problem fp16 benchmark, same-box); 256x256 when the plan pins it
+        const int want = pl->tile == GEMM_TILE_256x256 ? 0 : 1;
+        int c = -1;
+        for (int k = want; k < 2 && c < 0 && !generic_only; ++k) {
+            const KernelEntry *e = cls[k].e;
+            if (!e) continue;
+            const char *why = nullptr;
+            if (q.K > 0) {
+                why = operand_vec_problem(q.A, a_kc, a_kc ? q.K : q.M, e->bm, esz, e->bk * esz);
+                if (!why) why = operand_vec_problem(q.B, b_kc, b_kc ? q.K : q.N, e->bn, esz, e->bk * esz);
+            }
+            if (!why) c = k;
         }
-        if (why) {
+        if (c < 0) {
             scalar_path.push_back(i);
             continue;
         }
+        const KernelEntry *e = cls[c].e;
         GroupDesc g;
         std::memset(&g, 0, sizeof(g));
         Decision d;
@@ -1255,14 +1277,16 @@ gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32
                     (!C || reinterpret_cast<uintptr_t>(C) % (4 * osz) == 0))
                        ? 1 : 0;
         g.p = make_prob(q.A, q.B, C, q.D, q.M, q.N, q.K, d);
-        g.tile_start = (int)total;
-        total += (int64_t)d.tiles_m * d.tiles_n;
-        if (total > 0x7FFFFFFFLL) return fail(GEMM_UNSUPPORTED, "grouped_gemm_run: more than 2^31 tiles");
-        table.push_back(g);
+        g.tile_start = (int)cls[c].total;
+        cls[c].total += (int64_t)d.tiles_m * d.tiles_n;
+        if (cls[c].total > 0x7FFFFFFFLL)
+            return fail(GEMM_UNSUPPORTED, "grouped_gemm_run: more than 2^31 tiles");
+        cls[c].table.push_back(g);
     }
-    if (!table.empty()) {
-        const size_t bytes = table.size() * sizeof(GroupDesc);
-        if (table.size() > pl->gdesc_cap) {
+    const size_t n_desc = cls[0].table.size() + cls[1].table.size();
+    if (n_desc > 0) {
+        const size_t bytes = n_desc * sizeof(GroupDesc);
+        if (n_desc > pl->gdesc_cap) {
             if (pl->used || pl->gevent_pending) {
                 hipError_t he = hipStreamSynchronize(pl->last_stream);
                 if (he != hipSuccess) return hip_fail(he, "hipStreamSynchronize (descriptor growth)");
@@ -1273,7 +1297,7 @@ gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32
             pl->gdesc = nullptr;
             pl->ghost = nullptr;
             pl->gdesc_cap = 0;
-            const size_t cap = table.size() < 64 ? 64 : table.size();
+            const size_t cap = n_desc < 64 ? 64 : n_desc;
             hipError_t he = hipMalloc(reinterpret_cast<void **>(&pl->gdesc), cap * sizeof(GroupDesc));
             if (he != hipSuccess) {
                 (void)hipGetLastError();
@@ -1296,25 +1320,38 @@ gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32
             if (he != hipSuccess) return hip_fail(he, "hipEventSynchronize (descriptor staging)");
             pl->gevent_pending = false;
         }
-        std::memcpy(pl->ghost, table.data(), bytes);
+        // one upload: the 256x256 class's descriptors, then the 128x128 class's
+        std::memcpy(pl->ghost, cls[0].table.data(), cls[0].table.size() * sizeof(GroupDesc));
+        std::memcpy(pl->ghost + cls[0].table.size(), cls[1].table.data(),
+                    cls[1].table.size() * sizeof(GroupDesc));
         hipError_t he = hipMemcpyAsync(pl->gdesc, pl->ghost, bytes, hipMemcpyHostToDevice, hs);
         if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync (descriptor table)");
         he = hipEventRecord(pl->gevent, hs);
         if (he != hipSuccess) return hip_fail(he, "hipEventRecord");
         pl->gevent_pending = true;
-        int occ = 1;
-        if ((st = kernel_occupancy(dev, e->fn_grouped, e->nt, &occ)) != GEMM_OK) return st;
-        GroupArgs ga;
-        ga.desc = pl->gdesc;
-        ga.count = (int)table.size();
-        ga.total_tiles = (int)total;
-        const int64_t G = (int64_t)cus * occ;
-        ga.grid = (int)(total < G ? total : G);
-        ga.group_m = 4;
-        ga.xcd_remap = 1;
-        ga.e = ep;
-        he = e->run_grouped(ga, ga.grid, hs);
-        if (he != hipSuccess) return hip_fail(he, "grouped kernel launch");
+        size_t first = 0;
+        for (Class &c : cls) {
+            if (c.table.empty()) continue;
+            int occ = 1;
+            if ((st = kernel_occupancy(dev, c.e->fn_persistent, c.e->nt, &occ)) != GEMM_OK) return st;
+            // the persistent kernel with data-parallel tiles only; the kernel's
+            // own problem is a placeholder (each tile reads its descriptor)
+            KArgs ka;
+            std::memset(&ka, 0, sizeof(ka));
+            ka.p = c.table[0].p;
+            ka.p.batch = 1;
+            ka.e = ep;
+            const int64_t G = (int64_t)cus * occ;
+            ka.s.grid = (int)(c.total < G ? c.total : G);
+            ka.s.total_tiles = (int)c.total;
+            ka.s.group_m = c.e->bm >= 256 ? 8 : 4;
+            ka.s.xcd_remap = 1;
+            ka.s.gdesc = pl->gdesc + first;
+            ka.s.gcount = (int)c.table.size();
+            he = c.e->run(ka, ka.s.grid, hs);
+            if (he != hipSuccess) return hip_fail(he, "grouped kernel launch");
+            first += c.table.size();
+        }
         note_stream(pl, hs);
     }
     for (int32_t i : scalar_path) {

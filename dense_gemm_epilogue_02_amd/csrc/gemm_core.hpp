@@ -284,6 +284,13 @@ __device__ __forceinline__ float finish_aux(float v, float x, const EpiArgs &e, 
 // so the units of one tile, which run side by side, read neighbouring
 // segments of every operand row (DRAM page locality on skinny, HBM-bound
 // shapes).
+// Grouped GEMM: per-problem descriptors in device memory.
+struct GroupDesc {
+    Prob p;
+    int tile_start;   // prefix sum of tiles of the problems before this one
+    int pad[3];
+};
+
 struct Sched {
     int grid;
     int total_tiles;
@@ -300,6 +307,10 @@ struct Sched {
     int split;              // > 0: interleaved split-K, `split` units per tile
     float *partials;        // stream-K workspace: 2 * grid slots of BM*BN fp32
     int *counters;          // one arrival counter per stream-K tile (self-resetting)
+    // Grouped GEMM (gcount > 0; data-parallel tiles only): tile t belongs to
+    // the last of the gcount problems whose tile_start is <= t.
+    const GroupDesc *gdesc;
+    int gcount;
 };
 
 struct KArgs {
@@ -308,22 +319,6 @@ struct KArgs {
     Sched s;
 };
 
-// Grouped GEMM: per-problem descriptors in device memory.
-struct GroupDesc {
-    Prob p;
-    int tile_start;   // prefix sum of tiles of the problems before this one
-    int pad[3];
-};
-
-struct GroupArgs {
-    const GroupDesc *desc;
-    int count;
-    int total_tiles;
-    int grid;
-    int group_m;
-    int xcd_remap;
-    EpiArgs e;
-};
 
 // ---------------------------------------------------------------- helpers
 
@@ -339,6 +334,16 @@ __device__ __forceinline__ const void *uniform_ptr(const void *p) {
 }
 
 __device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// The thread index as a value the compiler cannot see through: per-lane
+// offsets derived from it are then computed where they are used instead of
+// being hoisted out of the persistent tile loop, where they would stay live
+// (and spill) through every main loop.
+__device__ __forceinline__ int opaque_tid() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(uniform_ptr(base)), (short)0,
@@ -548,8 +553,9 @@ template <int R, int ESZ, int NT, int CH> struct DirectStager {
 // (more than 2 only when both operands are K-contiguous).
 // PIPE: 0 = fragment reads scheduled by the compiler; 3 = the fragments of
 // substep s+1 are read (as one burst) before the MFMAs of substep s, with
-// scheduling fences; 7 = the register-streamed pipeline (mainloop_rs: both
-// operands K-contiguous, one wave per SIMD).
+// scheduling fences; 7 = the register-streamed pipeline (mainloop_rs: one
+// wave per SIMD; K-contiguous operands, or 16-bit M-/N-contiguous ones read
+// with transposing LDS loads).
 // COPY_WAVES: how many waves issue the LDS-DMA copies (0 = all). With half
 // of them (one per SIMD), the other wave of every SIMD starts its MFMAs right
 // after the barrier while its partner waits on the CU's copy queue, which
@@ -571,8 +577,10 @@ struct Tile {
     static constexpr bool MX = F::MX;
     static_assert(!MX || (CH == 8 && STAGES == 2 && PIPE == 0),
                   "MX tiles: 128-byte rows (four scale blocks per k-tile), two stages");
-    static_assert(PIPE != 7 || (A_KC && B_KC && CH == 8 && STAGES == 2 && COPY_WAVES == 0),
-                  "register-streamed pipeline: K-contiguous operands, 128-byte rows, two stages");
+    static_assert(PIPE != 7 || ((A_KC || ESZ == 2) && (B_KC || ESZ == 2) && !MX && CH == 8 &&
+                                STAGES == 2 && COPY_WAVES == 0),
+                  "register-streamed pipeline: K-contiguous or 16-bit operands, 128-byte rows, "
+                  "two stages");
     // LDS: [A stage 0 .. A stage S-1 | B stage 0 .. B stage S-1]
     static constexpr int A_BYTES = BM * KB, B_BYTES = BN * KB;
     static constexpr int B_OFF = STAGES * A_BYTES;
@@ -677,7 +685,7 @@ struct Tile {
 
     // The problem that schedule tile t belongs to (its batch entry's
     // operands) and the tile's coordinates within it.
-    static __device__ __forceinline__ Prob tile_problem(const Prob &p, int t, int group_m, int &tm,
+    static __device__ __forceinline__ Prob tile_problem(const Prob &p, const Sched &s, int t, int &tm,
                                                          int &tn);
 
     // Per-work-unit copy state: direct stagers for K-contiguous operands,
@@ -949,7 +957,10 @@ struct Tile {
     // register set each); the LDS writes of a k-tile spread over substeps
     // [0, RS_WSUB), which all precede the barrier; the global loads over
     // substeps [0, RS_LSUB), each after the write that frees its registers.
-    static constexpr int RS_DEPTH = 1;
+    // (Two on tiles of at most 128 x 128, whose accumulators leave room for
+    // a second register set: twice the loads in flight for the short-K and
+    // latency-bound shapes these tiles serve.)
+    static constexpr int RS_DEPTH = BM * BN <= 128 * 128 ? 2 : 1;
     static constexpr int RS_WSUB = SUBSTEPS - 1;
     static constexpr int RS_LSUB = SUBSTEPS;
     static_assert(RS_DEPTH == 1 || RS_DEPTH == 2, "register stages");
@@ -971,11 +982,14 @@ struct Tile {
         return c;
     }
 
+    // K-contiguous operand: row r of the tile (an M or N index) holds the
+    // k-tile's 128 bytes at lds_off<8>(r, chunk).
     template <int U> struct RsStream {
         const char *base;   // operand element (first row of the tile, k = 0), wave-uniform
         uint32_t voff;      // this lane's byte offset in the tile's first row step
         uint32_t step;      // bytes between a thread's consecutive chunks (32 rows), uniform
         int nval;           // chunks of this thread whose rows lie inside the operand
+        int kc;             // first k of this thread's chunks within a k-tile
         uint32_t lo[2];     // LDS byte offsets of chunk 0 and of chunk 1 minus one row step
         u32x4 r[RS_DEPTH][U];
 
@@ -986,40 +1000,121 @@ struct Tile {
             voff = (uint32_t)row0 * ld + (uint32_t)(c << 4);
             step = (uint32_t)uniform((int)(ld * RS_RSTEP));
             nval = r_left > row0 ? (r_left - row0 + RS_RSTEP - 1) / RS_RSTEP : 0;
+            kc = c * VEC;
             // rows row0 + 32u: the row swizzle repeats with period 2 in u
             lo[0] = lds_off<8>(row0, c);
             lo[1] = lds_off<8>(row0 + RS_RSTEP, c) - RS_RSTEP * KB;
         }
+        // byte offset of k-tile kt from the tile's origin
+        __device__ __forceinline__ size_t koff(int kt) const { return (size_t)kt * KB; }
         // chunk u of the k-tile whose resource starts at its first byte, into
-        // register set Q; kin: this thread's chunk lies inside K. The row
-        // step goes in the scalar offset; a lane outside the operand reads
-        // zeros (offset past the records).
+        // register set Q; kl: valid K elements of that k-tile (0: none). The
+        // row step goes in the scalar offset; a lane outside the operand
+        // reads zeros (offset past the records).
         template <int Q>
-        __device__ __forceinline__ void load(int u, __amdgpu_buffer_rsrc_t rs, bool kin) {
-            r[Q][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, kin && u < nval ? voff : OOB_OFFSET,
-                                                            u * step, 0);
+        __device__ __forceinline__ void load(int u, __amdgpu_buffer_rsrc_t rs, int kl) {
+            const bool in = (kc < kl) & (u < nval);
+            r[Q][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, in ? voff : OOB_OFFSET, u * step, 0);
         }
         template <int Q> __device__ __forceinline__ void store(int u, char *stage) const {
             *reinterpret_cast<u32x4 *>(stage + lo[u & 1] + u * RS_RSTEP * KB) = r[Q][u];
         }
     };
 
+    // M- or N-contiguous 16-bit operand (ColumnMajor A, RowMajor B): k-row k
+    // of a stage holds the tile's BMN elements, its 16-byte chunk c at slot
+    // c ^ mn_swz(k). A transposing fragment read covers, per 16 lanes, 32
+    // bytes of each of 4 consecutive k-rows (per 32 lanes, 64 bytes of
+    // each); the XOR puts those pieces on distinct banks whether the LDS
+    // serves 128 or 256 bytes a clock, and keeps each row's chunks a
+    // permutation within aligned groups of 16 for the 16-byte writes.
+    static __device__ __forceinline__ int mn_swz(int k) { return ((k & 3) << 2) | (k & 2); }
+
+    template <int U, int BMN> struct RsStreamMN {
+        static constexpr int ROWB = BMN * ESZ, CPR = ROWB / 16, RPU = NT / CPR;
+        static_assert(CPR >= 16 && RPU % 4 == 0 && RPU * U == BK, "MN register stream shape");
+        const char *base;   // operand element (k = 0, first M/N index of the tile), uniform
+        uint32_t voff;      // this lane's byte offset within the k-tile's first k-row step
+        uint32_t step;      // bytes between a thread's consecutive chunks (RPU k-rows), uniform
+        uint32_t kstep;     // bytes between k-tiles (BK k-rows), uniform
+        uint32_t lo;        // LDS byte offset of chunk 0 (the swizzle repeats every 4 k-rows)
+        int row0;           // k-row of chunk 0
+        u32x4 r[RS_DEPTH][U];
+
+        __device__ __forceinline__ void init(const char *tile_base, uint32_t ld, int mn_left, int tid) {
+            base = static_cast<const char *>(uniform_ptr(tile_base));
+            row0 = tid / CPR;
+            const int c = tid % CPR;
+            // a thread whose 8 elements lie outside the operand reads zeros
+            voff = c * VEC < mn_left ? (uint32_t)row0 * ld + (uint32_t)(c << 4) : OOB_OFFSET;
+            step = (uint32_t)uniform((int)(ld * RPU));
+            kstep = (uint32_t)uniform((int)(ld * BK));
+            lo = (uint32_t)(row0 * ROWB + ((c ^ mn_swz(row0)) << 4));
+        }
+        __device__ __forceinline__ size_t koff(int kt) const { return (size_t)kt * kstep; }
+        template <int Q>
+        __device__ __forceinline__ void load(int u, __amdgpu_buffer_rsrc_t rs, int kl) {
+            r[Q][u] = __builtin_amdgcn_raw_buffer_load_b128(
+                rs, row0 + u * RPU < kl ? voff : OOB_OFFSET, u * step, 0);
+        }
+        template <int Q> __device__ __forceinline__ void store(int u, char *stage) const {
+            *reinterpret_cast<u32x4 *>(stage + lo + u * RPU * ROWB) = r[Q][u];
+        }
+    };
+
+    // MFMA operand (8 consecutive k of one M/N index per lane, the same k
+    // split as the K-contiguous fragments) of the 32 M/N indices from mn0,
+    // substep s, read from an MN stage with two transposing loads: of a
+    // 16-lane group, lane r fetches 4 elements of k-row r/4, and the load
+    // hands lane r element r of the group's 16 columns for each of the 4
+    // k-rows (lane layout measured on gfx950).
+    template <int BMN>
+    static __device__ __forceinline__ u32x4 tr_frag(const char *stage, int mn0, int s, int lane) {
+        constexpr int ROWB = BMN * ESZ;
+        typedef __attribute__((ext_vector_type(4))) short s16x4;
+        const int r = lane & 15, g = lane >> 4;
+        const int mn = mn0 + ((g & 1) << 4) + ((r & 3) << 2);
+        u32x4 out;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = 8 * frag_chunk(s, g >> 1, 0) + 4 * h + (r >> 2);
+            const char *ptr = stage + k * ROWB + ((((mn >> 3) ^ mn_swz(k))) << 4) + ((mn & 7) << 1);
+            const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(ptr));
+            const u32x2 w = __builtin_bit_cast(u32x2, v);
+            out[2 * h] = w.x;
+            out[2 * h + 1] = w.y;
+        }
+        return out;
+    }
+    static constexpr int RS_READS = FN * (B_KC ? CPL : 2) + FM * (A_KC ? CPL : 2);
+
     // fragments of substep s of one stage
     static __device__ __forceinline__ void rs_frags(const char *sA, const char *sB, int s, Frags &f,
                                                     int lane, int wm, int wn) {
         const int g = lane >> 5, r = lane & 31;
 #pragma unroll
-        for (int i = 0; i < FN; ++i)
+        for (int i = 0; i < FN; ++i) {
+            if constexpr (B_KC) {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                f.x[i][c] = *reinterpret_cast<const u32x4 *>(
-                    sB + lds_off<CH>(wn * WTN + i * 32 + r, frag_chunk(s, g, c)));
+                for (int c = 0; c < CPL; ++c)
+                    f.x[i][c] = *reinterpret_cast<const u32x4 *>(
+                        sB + lds_off<CH>(wn * WTN + i * 32 + r, frag_chunk(s, g, c)));
+            } else {
+                f.x[i][0] = tr_frag<BN>(sB, wn * WTN + i * 32, s, lane);
+            }
+        }
 #pragma unroll
-        for (int j = 0; j < FM; ++j)
+        for (int j = 0; j < FM; ++j) {
+            if constexpr (A_KC) {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                f.y[j][c] = *reinterpret_cast<const u32x4 *>(
-                    sA + lds_off<CH>(wm * WTM + j * 32 + r, frag_chunk(s, g, c)));
+                for (int c = 0; c < CPL; ++c)
+                    f.y[j][c] = *reinterpret_cast<const u32x4 *>(
+                        sA + lds_off<CH>(wm * WTM + j * 32 + r, frag_chunk(s, g, c)));
+            } else {
+                f.y[j][0] = tr_frag<BM>(sA, wm * WTM + j * 32, s, lane);
+            }
+        }
     }
 
     // Scheduling pattern of one substep: the fragment reads ride on the
@@ -1056,9 +1151,8 @@ struct Tile {
         if (n <= 0) return;
         const int last = uniform(p.ipt) - 1;
         const int k_tail = uniform((int)(p.K - (int64_t)last * BK));
-        const int kc = (tid & 7) * VEC;   // first k of this thread's chunk within a k-tile
-        RsStream<RS_UA> sa;
-        RsStream<RS_UB> sb;
+        std::conditional_t<A_KC, RsStream<RS_UA>, RsStreamMN<RS_UA, BM>> sa;
+        std::conditional_t<B_KC, RsStream<RS_UB>, RsStreamMN<RS_UB, BN>> sb;
         {
             const char *base;
             uint32_t ld;
@@ -1068,18 +1162,19 @@ struct Tile {
             b_tile(p, tn, 0, base, ld, rl, kl);
             sb.init(base, ld, rl, tid);
         }
-        // k-tile j of this work unit (j >= n: none; every chunk reads zeros)
+        // valid K elements of k-tile j of this work unit (j >= n: none; every
+        // chunk reads zeros)
         auto kin = [&](int j) {
             const int kt = kt0 + j * stride;
-            return j < n && kc < (kt == last ? k_tail : BK);
+            return j < n ? (kt == last ? k_tail : BK) : 0;
         };
-        auto koff = [&](int j) { return (size_t)(kt0 + (j < n ? j : 0) * stride) * KB; };
+        auto ktile = [&](int j) { return kt0 + (j < n ? j : 0) * stride; };
         // every chunk of k-tile j into register set Q
         auto load_all = [&](auto qc, int j) {
             constexpr int Q = decltype(qc)::value;
-            const bool k = kin(j);
-            const __amdgpu_buffer_rsrc_t ra = make_rsrc(sa.base + koff(j));
-            const __amdgpu_buffer_rsrc_t rb = make_rsrc(sb.base + koff(j));
+            const int k = kin(j);
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(sa.base + sa.koff(ktile(j)));
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(sb.base + sb.koff(ktile(j)));
 #pragma unroll
             for (int u = 0; u < RS_UA; ++u) sa.template load<Q>(u, ra, k);
 #pragma unroll
@@ -1109,9 +1204,9 @@ struct Tile {
             const char *rA = lds + P * A_BYTES, *rB = lds + B_OFF + P * B_BYTES;
             char *wA = lds + (P ^ 1) * A_BYTES, *wB = lds + B_OFF + (P ^ 1) * B_BYTES;
             const int jn = i + 1 + RS_DEPTH;
-            const bool kn = kin(jn);
-            const __amdgpu_buffer_rsrc_t ra = make_rsrc(sa.base + koff(jn));
-            const __amdgpu_buffer_rsrc_t rb = make_rsrc(sb.base + koff(jn));
+            const int kn = kin(jn);
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(sa.base + sa.koff(ktile(jn)));
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(sb.base + sb.koff(ktile(jn)));
             auto substep = [&](auto sc) {
                 constexpr int S = decltype(sc)::value;
                 // fragments for the next substep: this stage, or (after the
@@ -1131,7 +1226,7 @@ struct Tile {
                     if (o < RS_UA) sa.template load<Q>(o, ra, kn);
                     else sb.template load<Q>(o - RS_UA, rb, kn);
                 }
-                rs_sched<FN * CPL + FM * CPL, rs_count_w(S), rs_count_l(S)>();
+                rs_sched<RS_READS, rs_count_w(S), rs_count_l(S)>();
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (S == SUBSTEPS - 2) {
                     // this wave's writes of k-tile i+1 and reads of k-tile i
@@ -1148,9 +1243,15 @@ struct Tile {
                 substep(std::integral_constant<int, 3>{});
             }
         };
+        // k-tiles in pairs (the stages, and with two register sets the sets,
+        // alternate). With two sets the second iteration is unconditional:
+        // a conditional one makes the compiler's wait counts for the other
+        // set conservative (one set of loads in flight instead of two); an
+        // odd count then ends with one iteration past the last k-tile, whose
+        // stage holds zeros (its loads read past K), leaving acc unchanged.
         for (int i = 0; i < n; i += 2) {
             iteration(std::integral_constant<int, 0>{}, i);
-            if (i + 1 < n) iteration(std::integral_constant<int, 1>{}, i + 1);
+            if (RS_DEPTH == 2 || i + 1 < n) iteration(std::integral_constant<int, 1>{}, i + 1);
         }
         __syncthreads();
     }
@@ -1243,8 +1344,7 @@ struct Tile {
         // copy of the thread index keeps the compiler from hoisting all of
         // them out of the persistent tile loop, where they would stay live
         // (64 registers) through every main loop
-        int tid = threadIdx.x;
-        asm volatile("" : "+v"(tid));
+        const int tid = opaque_tid();
         const int lane = tid & 63, wave = tid >> 6;
         // tile-local row / column of this lane's first group
         const int r_loc = (wave / WN) * WTM + (lane & 31), c_loc = (wave % WN) * WTN + (lane >> 5) * 4;
@@ -1548,14 +1648,26 @@ template <int FAM_, bool A_KC, bool B_KC, int BM_, int BN_, int WM_, int WN_, in
           int PIPE, int COPY_WAVES>
 __device__ __forceinline__ Prob
 Tile<FAM_, A_KC, B_KC, BM_, BN_, WM_, WN_, KB, STAGES, PIPE, COPY_WAVES>::tile_problem(
-    const Prob &p, int t, int group_m, int &tm, int &tn) {
+    const Prob &p, const Sched &s, int t, int &tm, int &tn) {
+    if (s.gcount > 0) {
+        int lo = 0, hi = s.gcount - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s.gdesc[mid].tile_start <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        lo = uniform(lo);
+        const Prob q = s.gdesc[lo].p;
+        tile_coords(t - s.gdesc[lo].tile_start, q.tiles_m, q.tiles_n, s.group_m, tm, tn);
+        return q;
+    }
     if (p.batch <= 1) {
-        tile_coords(t, p.tiles_m, p.tiles_n, group_m, tm, tn);
+        tile_coords(t, p.tiles_m, p.tiles_n, s.group_m, tm, tn);
         return p;
     }
     const int per = p.tiles_m * p.tiles_n;
     const int b = t / per;
-    tile_coords(t - b * per, p.tiles_m, p.tiles_n, group_m, tm, tn);
+    tile_coords(t - b * per, p.tiles_m, p.tiles_n, s.group_m, tm, tn);
     Prob q = p;
     q.A = p.A + (size_t)(b * p.stride_a) * ESZ;
     q.B = p.B + (size_t)(b * p.stride_b) * ESZ;
@@ -1616,7 +1728,7 @@ gemm_persistent(KArgs a) {
             t = dp_t;
             dp_t += s.grid;
             kt0 = 0;
-            n = p.ipt;
+            n = -1;   // every k-tile of the tile's problem
             stride = 1;
             mode = 0;
         } else {
@@ -1625,7 +1737,8 @@ gemm_persistent(KArgs a) {
         t = uniform(t);
         mode = uniform(mode);
         int tm, tn;
-        const Prob pt = TL::tile_problem(p, t, s.group_m, tm, tn);
+        const Prob pt = TL::tile_problem(p, s, t, tm, tn);
+        if (n < 0) n = pt.ipt;
         TL::mainloop(pt, tm, tn, kt0, n, stride, acc, lds);
         bool finish = mode == 0;
         int v0 = 0, v1 = 0;
@@ -1661,28 +1774,6 @@ gemm_persistent(KArgs a) {
                 __hip_atomic_store(&s.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (mode != 0) __syncthreads();
-    }
-}
-
-template <class TL>
-__global__ void __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::WAVES_PER_EU)))
-gemm_grouped(GroupArgs g) {
-    __shared__ __attribute__((aligned(16))) char lds[TL::LDS_BYTES];
-    const int v = uniform(virtual_id(blockIdx.x, g.grid, g.xcd_remap));
-    typename TL::Acc acc;
-    for (int t = v; t < g.total_tiles; t += g.grid) {
-        // last problem whose first tile is <= t
-        int lo = 0, hi = g.count - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (g.desc[mid].tile_start <= t) lo = mid;
-            else hi = mid - 1;
-        }
-        const Prob p = g.desc[lo].p;
-        int tm, tn;
-        tile_coords(t - g.desc[lo].tile_start, p.tiles_m, p.tiles_n, g.group_m, tm, tn);
-        TL::mainloop(p, tm, tn, 0, p.ipt, 1, acc, lds);
-        TL::epilogue(p, g.e, tm, tn, acc, lds);
     }
 }
 

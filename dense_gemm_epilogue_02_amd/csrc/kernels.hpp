@@ -10,15 +10,12 @@ namespace mg {
 enum TileId { TILE_256x256 = 1, TILE_128x128 = 2, TILE_64x256 = 3, TILE_32x256 = 4 };
 
 using PersistentLaunch = hipError_t (*)(const KArgs &, int grid, hipStream_t);
-using GroupedLaunch = hipError_t (*)(const GroupArgs &, int grid, hipStream_t);
 
 struct KernelEntry {
     int fam, a_kc, b_kc, tile;
     int bm, bn, bk, nt, lds_bytes;
     const void *fn_persistent;   // for occupancy queries
-    const void *fn_grouped;      // may be null
-    PersistentLaunch run;
-    GroupedLaunch run_grouped;   // may be null
+    PersistentLaunch run;        // single, batched and grouped GEMMs
 };
 
 template <class TL>
@@ -28,21 +25,10 @@ hipError_t launch_persistent(const KArgs &a, int grid, hipStream_t st) {
 }
 
 template <class TL>
-hipError_t launch_grouped(const GroupArgs &a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL(gemm_grouped<TL>, dim3(grid), dim3(TL::NT), 0, st, a);
-    return hipGetLastError();
-}
-
-template <class TL, bool GROUPED>
 KernelEntry make_entry(int tile, bool a_kc, bool b_kc) {
-    KernelEntry e{TL::FAM, a_kc ? 1 : 0, b_kc ? 1 : 0, tile, TL::BM, TL::BN, TL::BK, TL::NT,
-                  TL::LDS_BYTES, reinterpret_cast<const void *>(&gemm_persistent<TL>), nullptr,
-                  &launch_persistent<TL>, nullptr};
-    if constexpr (GROUPED) {
-        e.fn_grouped = reinterpret_cast<const void *>(&gemm_grouped<TL>);
-        e.run_grouped = &launch_grouped<TL>;
-    }
-    return e;
+    return KernelEntry{TL::FAM, a_kc ? 1 : 0, b_kc ? 1 : 0, tile, TL::BM, TL::BN, TL::BK, TL::NT,
+                       TL::LDS_BYTES, reinterpret_cast<const void *>(&gemm_persistent<TL>),
+                       &launch_persistent<TL>};
 }
 
 // Per-family tables (one translation unit each).

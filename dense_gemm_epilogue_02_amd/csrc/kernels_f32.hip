@@ -4,7 +4,7 @@
 namespace mg {
 
 static const KernelEntry kTable[] = {
-    MG_LAYOUTS(FAM_F32, TILE_128x128, 128, 128, 2, 2, true),
+    MG_LAYOUTS(FAM_F32, TILE_128x128, 128, 128, 2, 2),
 };
 
 const KernelEntry *entries_f32(int *count) {

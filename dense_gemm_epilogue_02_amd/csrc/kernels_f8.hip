@@ -4,10 +4,10 @@
 namespace mg {
 
 static const KernelEntry kTable[] = {
-    MG_LAYOUTS(FAM_F8, TILE_256x256, 256, 256, 2, 4, false),
-    MG_LAYOUTS(FAM_F8, TILE_128x128, 128, 128, 2, 2, true),
-    MG_LAYOUTS(FAM_F8, TILE_64x256, 64, 256, 1, 4, false),
-    MG_LAYOUTS(FAM_F8, TILE_32x256, 32, 256, 1, 4, false),
+    MG_LAYOUTS(FAM_F8, TILE_256x256, 256, 256, 2, 4),
+    MG_LAYOUTS(FAM_F8, TILE_128x128, 128, 128, 2, 2),
+    MG_LAYOUTS(FAM_F8, TILE_64x256, 64, 256, 1, 4),
+    MG_LAYOUTS(FAM_F8, TILE_32x256, 32, 256, 1, 4),
 };
 
 const KernelEntry *entries_f8(int *count) {

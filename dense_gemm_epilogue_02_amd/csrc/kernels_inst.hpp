@@ -25,17 +25,35 @@ template <> struct TileCfg<FAM_BF16, true, true, 256, 256, 2, 4> {
 template <> struct TileCfg<FAM_F16, true, true, 256, 256, 2, 4> {
     using type = Tile<FAM_F16, true, true, 256, 256, 2, 2, 128, 2, 7>;
 };
+// 16-bit types with an M- or N-contiguous operand: the same pipeline, that
+// operand kept k-row-major in LDS and read with transposing loads.
+template <int FAM, bool AKC, bool BKC> struct Rs256 {
+    using type = Tile<FAM, AKC, BKC, 256, 256, 2, 2, 128, 2, 7>;
+};
+template <> struct TileCfg<FAM_BF16, true, false, 256, 256, 2, 4> : Rs256<FAM_BF16, true, false> {};
+template <> struct TileCfg<FAM_BF16, false, true, 256, 256, 2, 4> : Rs256<FAM_BF16, false, true> {};
+template <> struct TileCfg<FAM_BF16, false, false, 256, 256, 2, 4> : Rs256<FAM_BF16, false, false> {};
+template <> struct TileCfg<FAM_F16, true, false, 256, 256, 2, 4> : Rs256<FAM_F16, true, false> {};
+template <> struct TileCfg<FAM_F16, false, true, 256, 256, 2, 4> : Rs256<FAM_F16, false, true> {};
+template <> struct TileCfg<FAM_F16, false, false, 256, 256, 2, 4> : Rs256<FAM_F16, false, false> {};
+// 128x128 (two workgroups per CU): four waves of 64 x 64, every layout.
+template <bool AKC, bool BKC> struct TileCfg<FAM_BF16, AKC, BKC, 128, 128, 2, 2> {
+    using type = Tile<FAM_BF16, AKC, BKC, 128, 128, 2, 2, 128, 2, 7>;
+};
+template <bool AKC, bool BKC> struct TileCfg<FAM_F16, AKC, BKC, 128, 128, 2, 2> {
+    using type = Tile<FAM_F16, AKC, BKC, 128, 128, 2, 2, 128, 2, 7>;
+};
 }  // namespace mg
 
 #define MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN) \
     typename mg::TileCfg<FAM, AKC, BKC, BM, BN, WM, WN>::type
 
-#define MG_ROW(FAM, AKC, BKC, TILEID, BM, BN, WM, WN, GROUPED) \
-    mg::make_entry<MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN), GROUPED>(TILEID, AKC, BKC)
+#define MG_ROW(FAM, AKC, BKC, TILEID, BM, BN, WM, WN) \
+    mg::make_entry<MG_TILE(FAM, AKC, BKC, BM, BN, WM, WN)>(TILEID, AKC, BKC)
 
 // The four operand-layout combinations of one tile shape.
-#define MG_LAYOUTS(FAM, TILEID, BM, BN, WM, WN, GROUPED)          \
-    MG_ROW(FAM, true, true, TILEID, BM, BN, WM, WN, GROUPED),     \
-    MG_ROW(FAM, true, false, TILEID, BM, BN, WM, WN, GROUPED),    \
-    MG_ROW(FAM, false, true, TILEID, BM, BN, WM, WN, GROUPED),    \
-    MG_ROW(FAM, false, false, TILEID, BM, BN, WM, WN, GROUPED)
+#define MG_LAYOUTS(FAM, TILEID, BM, BN, WM, WN)          \
+    MG_ROW(FAM, true, true, TILEID, BM, BN, WM, WN),     \
+    MG_ROW(FAM, true, false, TILEID, BM, BN, WM, WN),    \
+    MG_ROW(FAM, false, true, TILEID, BM, BN, WM, WN),    \
+    MG_ROW(FAM, false, false, TILEID, BM, BN, WM, WN)

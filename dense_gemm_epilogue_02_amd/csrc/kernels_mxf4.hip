@@ -7,10 +7,10 @@
 namespace mg {
 
 static const KernelEntry kTable[] = {
-    MG_ROW(FAM_MXF4, true, true, TILE_256x256, 256, 256, 2, 4, false),
-    MG_ROW(FAM_MXF4, true, true, TILE_128x128, 128, 128, 2, 2, false),
-    MG_ROW(FAM_MXF4, true, true, TILE_64x256, 64, 256, 1, 4, false),
-    MG_ROW(FAM_MXF4, true, true, TILE_32x256, 32, 256, 1, 4, false),
+    MG_ROW(FAM_MXF4, true, true, TILE_256x256, 256, 256, 2, 4),
+    MG_ROW(FAM_MXF4, true, true, TILE_128x128, 128, 128, 2, 2),
+    MG_ROW(FAM_MXF4, true, true, TILE_64x256, 64, 256, 1, 4),
+    MG_ROW(FAM_MXF4, true, true, TILE_32x256, 32, 256, 1, 4),
 };
 
 const KernelEntry *entries_mxf4(int *count) {

@@ -324,6 +324,27 @@ def test_grouped_integer_exact_mixed_alignment():
     plan.close()
 
 
+@pytest.mark.parametrize("dab", ["bf16", "f16"])
+@pytest.mark.parametrize("la,lb", [("row", "col"), ("row", "row"), ("col", "col"), ("col", "row")])
+def test_grouped_two_tile_classes_integer_exact(dab, la, lb):
+    """Problems that take 256x256 tiles (little padding) and 128x128 tiles
+    (M or N far from a multiple of 256) in one grouped call, two launches;
+    ragged M, N and K tails; every operand layout."""
+    shapes = [(768, 512, 136),    # 256x256 class, K tail
+              (520, 264, 64),     # 128x128 class
+              (256, 1024, 72),    # 256x256 class
+              (96, 128, 40),      # 128x128 class
+              (512, 1000, 200),   # 256x256 class, ragged N
+              (512, 776, 200)]    # 128x128 class (256x256 would pad over 1/8 more)
+    probs = [_int_problem(dab, dab, la, lb, "row", M=m, N=n, K=k, seed=40 + i)
+             for i, (m, n, k) in enumerate(shapes)]
+    plan = g.Plan(dab, la=la, lb=lb, lc="row")
+    outs = _grouped_run(plan, probs, beta=1.0)
+    for p, got in zip(probs, outs):
+        exact(got, p, what=f"grouped {dab} {la}/{lb} {p.M}x{p.N}x{p.K}")
+    plan.close()
+
+
 # ------------------------------------------------------------ edge cases
 
 def test_k_zero_gives_beta_c():
