@@ -313,6 +313,13 @@ struct Sched {
     int gcount;
 };
 
+// What the out-of-line epilogues need of a tile's problem.
+struct EpiOut {
+    char *D;
+    const char *C;
+    int64_t M, N;
+};
+
 struct KArgs {
     Prob p;
     EpiArgs e;
@@ -1400,7 +1407,8 @@ struct Tile {
     // kernels' own code and registers stay as they are without them. The
     // accumulators of fragment rows j0 .. j0+jc-1 arrive through the idle LDS:
     // group ((jj * FN + i) * 4 + q) of thread tid at vals[group * NT + tid].
-    static __device__ __noinline__ void epi_aux(const Prob &p, const EpiArgs &e, float alpha,
+    template <class PO, class EA>
+    static __device__ __noinline__ void epi_aux(PO p, EA e, float alpha,
                                                 int64_t m_base, int64_t n_base, const f32x4 *vals,
                                                 int j0, int jc) {
         Out *D = reinterpret_cast<Out *>(p.D);
@@ -1441,7 +1449,8 @@ struct Tile {
     // Edge tiles, ColumnMajor C/D or unaligned C/D: element by element, with
     // the accumulators of fragment rows j0 .. j0+jc-1 handed over through the
     // idle LDS exactly as for epi_aux (no private scratch array).
-    static __device__ __noinline__ void epi_slow(const Prob &p, const EpiArgs &e, float alpha,
+    template <class PO, class EA>
+    static __device__ __noinline__ void epi_slow(PO p, EA e, float alpha,
                                                  int64_t m_base, int64_t n_base, const f32x4 *vals,
                                                  int j0, int jc) {
         Out *D = reinterpret_cast<Out *>(p.D);
@@ -1507,8 +1516,22 @@ struct Tile {
                         buf[((jj * FN + i) * 4 + q) * NT + tid] =
                             f32x4{acc.v[i][j0 + jj][q * 4], acc.v[i][j0 + jj][q * 4 + 1],
                                   acc.v[i][j0 + jj][q * 4 + 2], acc.v[i][j0 + jj][q * 4 + 3]};
-            if (interior) epi_aux(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
-            else epi_slow(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
+            // The out-of-line paths take their arguments by value on tiles
+            // up to 128 x 128: a reference makes the kernel copy its
+            // arguments to private memory at entry and read them from there
+            // (several microseconds of a small GEMM). The 256 x 256 kernels
+            // keep references: their main loop's register allocation is
+            // spill-free only that way.
+            if constexpr (BM * BN <= 128 * 128) {
+                const EpiOut o{p.D, p.C, p.M, p.N};
+                if (interior) epi_aux<EpiOut, EpiArgs>(o, e, alpha, m_base, n_base, buf, j0, AUX_JC);
+                else epi_slow<EpiOut, EpiArgs>(o, e, alpha, m_base, n_base, buf, j0, AUX_JC);
+            } else {
+                if (interior)
+                    epi_aux<const Prob &, const EpiArgs &>(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
+                else
+                    epi_slow<const Prob &, const EpiArgs &>(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
+            }
         }
         __syncthreads();
     }
