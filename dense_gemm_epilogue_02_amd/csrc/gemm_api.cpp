@@ -425,15 +425,17 @@ const char *operand_vec_problem(const void *ptr, bool kc, int64_t contig, int64_
 }
 
 // `batch`: problems of this shape in one launch. The 256x256 tile needs a
-// full wave of them: on 16 x 1024^3 and 64 x 512^3 fp16 batches it ran
-// 1.2-1.4x faster than 128x128 tiles once the batch supplies the wave.
-gemm_tile pick_tile(int fam, int64_t M, int64_t N, int cus, int64_t batch = 1) {
+// full wave of tiles and a long K: its kernel pays ~20 us per workgroup and
+// tile outside the main loop, so on 16 x 1024^3 fp16 batches (one 256x256
+// tile per workgroup, 16 k-tiles) 128x128 tiles ran 1.38x faster (44 vs
+// 61 us, same box), while the K = 8192 layer GEMMs want 256x256.
+gemm_tile pick_tile(int fam, int64_t M, int64_t N, int64_t K, int cus, int64_t batch = 1) {
     if (fam == FAM_F32) return GEMM_TILE_128x128;
     // skinny M streams B once: 64-row tiles matched or beat 32-row ones for
     // every measured M <= 64 (fewer, longer B panels per workgroup)
     if (M <= 64) return GEMM_TILE_64x256;
     const int64_t big = cdiv(M, 256) * cdiv(N, 256) * (batch > 1 ? batch : 1);
-    return big >= cus ? GEMM_TILE_256x256 : GEMM_TILE_128x128;
+    return big >= cus && K >= 2048 ? GEMM_TILE_256x256 : GEMM_TILE_128x128;
 }
 
 gemm_tile tile_enum(int id) {
@@ -520,7 +522,7 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
                 reinterpret_cast<uintptr_t>(bias) % (4 * osz) == 0)
                    ? 1 : 0;
     if (cfg.tile != GEMM_TILE_GENERIC) {
-        gemm_tile t = cfg.tile == GEMM_TILE_AUTO ? pick_tile(fam, M, N, cus, batch) : cfg.tile;
+        gemm_tile t = cfg.tile == GEMM_TILE_AUTO ? pick_tile(fam, M, N, K, cus, batch) : cfg.tile;
         const KernelEntry *e = registry().find(fam, a_kc, b_kc, tile_id(t));
         if (!e) e = registry().find(fam, a_kc, b_kc, TILE_128x128);
         const char *why = nullptr;

@@ -143,16 +143,20 @@ def test_describe_small_and_skinny_use_stream_k():
     assert d["tile"] == "128x128" and d["schedule"] == "stream_k" and d["ipt"] == 16
     p.close()
     q = _plan("f8e4m3")
-    # decode GEMMs: 32-224 tiles for 512 workgroup slots, so stream-K over
-    # one workgroup per CU
+    # decode GEMMs on the four-stage fp8 tiles (one workgroup per CU): 32-64
+    # tiles for 256 slots, so stream-K over every CU
     for M, N, K, tile in ((16, 8192, 28672, "64x256"), (64, 8192, 28672, "64x256"),
-                          (128, 8192, 28672, "128x128"), (16, 57344, 8192, "64x256")):
+                          (128, 8192, 28672, "128x128")):
         d = q.describe(M, N, K)
         assert d["tile"] == tile and d["schedule"] == "stream_k", d
         assert d["grid"] == 256 and d["split"] == 0 and d["bk"] == 128, d
-    # 448 tiles of 128x128 fill 87.5% of the slots: data-parallel
+    # 224 tiles fill 87.5% of the slots: data-parallel
+    for M in (16, 64):
+        d = q.describe(M, 57344, 8192)
+        assert d["tile"] == "64x256" and d["schedule"] == "data_parallel" and d["grid"] == 224, d
+    # 448 tiles of 128x128 over 256 slots: one wave plus a stream-K remainder
     d = q.describe(128, 57344, 8192)
-    assert d["tile"] == "128x128" and d["schedule"] == "data_parallel" and d["grid"] == 448, d
+    assert d["tile"] == "128x128" and d["schedule"] == "hybrid" and d["grid"] == 256, d
     q.close()
 
 
@@ -391,16 +395,19 @@ def test_profile_validation_before_any_device_call():
 
 
 def test_describe_batched_tile_choice():
-    """A batch that supplies a full wave of 256x256 tiles gets them (the
-    single 1024^3 problem does not), and the tile count covers the batch."""
+    """A batch that supplies a full wave of 256x256 tiles gets them when K is
+    long (K >= 2048); with K = 1024 it keeps 128x128 tiles, and the tile count
+    covers the batch."""
     h = g.gemm_plan_create_simple(g.Dtype.F16, g.Layout.ROW_MAJOR, g.Epilogue.LINEAR)
     try:
         one = g.gemm_plan_describe_batched(h, 1024, 1024, 1024, 1)
         assert one == g.gemm_plan_describe(h, 1024, 1024, 1024)
         assert one["tile"] == "128x128"
         b16 = g.gemm_plan_describe_batched(h, 1024, 1024, 1024, 16)
-        assert b16["tile"] == "256x256" and b16["tiles"] == 256
+        assert b16["tile"] == "128x128" and b16["tiles"] == 1024
         assert b16["schedule"] == "data_parallel"
+        b16k = g.gemm_plan_describe_batched(h, 1024, 1024, 2048, 16)
+        assert b16k["tile"] == "256x256" and b16k["tiles"] == 256
         assert g.gemm_plan_describe_batched(h, 64, 1024, 1024, 64)["tile"] == "64x256"
         assert g.lib.gemm_plan_describe_batched(h, 8, 8, 8, 0, 0, ctypes.create_string_buffer(64),
                                                 64) == g.Status.INVALID_ARG

@@ -192,7 +192,7 @@ def test_random_tolerance(dab, dcd, la, lb, lc):
 
 @pytest.mark.parametrize("M,N,K,tile,sched,sk_grid", [
     # AUTO resolves to hybrid with fewer stream-K iterations than workgroups
-    (4352, 4096, 256, T.AUTO, S.AUTO, 0),        # 272 tiles of 256^2: 16 stream-K, ipt 4
+    (4352, 4096, 256, T.AUTO, S.AUTO, 0),        # 1088 tiles of 128^2 (K < 2048): 64 stream-K, ipt 4
     (3072, 3200, 256, T.T128x128, S.HYBRID, 0),  # 600 tiles of 128^2 over 2/CU
     (4352, 4096, 512, T.T256x256, S.HYBRID, 0),  # ipt 8: 128 iterations
     (2304, 2560, 256, T.T256x256, S.HYBRID, 0),  # 90 tiles < grid: resolves to stream-K
