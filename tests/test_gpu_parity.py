@@ -16,7 +16,8 @@ import dense_gemm_epilogue_02_amd as g
 import oracle
 from oracle import acceptance
 import synthetic as syn
-from gpu_util import (DEV, device_operands, full_size_samples, logical, make_out, run, scales)
+from gpu_util import (DEV, check_guards, device_operands, full_size_samples, logical, make_out,
+                      run, scales)
 
 pytestmark = pytest.mark.gpu
 
@@ -321,6 +322,36 @@ def test_grouped_integer_exact_mixed_alignment():
     outs = _grouped_run(plan, probs, beta=1.0)
     for p, got in zip(probs, outs):
         exact(got, p, what=f"grouped int {p.M}x{p.N}x{p.K}")
+    plan.close()
+
+
+def test_grouped_repeated_and_changed_problem_lists():
+    """Back-to-back grouped calls with the same list reuse the uploaded
+    descriptors; a changed list (another output, another shape) must not:
+    every call's outputs are compared with the oracle, NaN-prefilled."""
+    probs = syn.config3(seed=21, count=6)
+    plan = g.Plan("f16", la="row", lb="row", lc="row")
+    ops = [device_operands(p) for p in probs]
+    outs = [make_out(p) for p in probs]
+
+    def call(order):
+        for i in order:
+            outs[i][1].fill_(float("nan"))
+        plan.run_grouped([(probs[i].M, probs[i].N, probs[i].K, ops[i][0], ops[i][1], None,
+                           outs[i][1]) for i in order], 1.0, 0.0)
+        torch.cuda.synchronize()
+        for i in order:
+            close(logical(outs[i][1], probs[i]), probs[i], what=f"grouped repeat #{i}")
+            check_guards(outs[i][0], probs[i])
+
+    call(range(6))
+    call(range(6))           # same list: descriptors reused
+    call(range(6))
+    call([0, 2, 4])          # a different list
+    out5 = make_out(probs[5])
+    outs[5] = out5           # same shapes, another output tensor
+    call(range(6))
+    call(range(6))
     plan.close()
 
 
