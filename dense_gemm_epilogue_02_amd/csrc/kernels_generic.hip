@@ -83,8 +83,11 @@ __global__ void __launch_bounds__(256) gemm_generic(GenericArgs a) {
     constexpr int LF = FAM == FAM_MXF8 ? FAM_F8 : FAM;   // element decoder
     constexpr bool MX = FAM == FAM_MXF8 || FAM == FAM_MXF4;
     using Raw = typename RawT<LF>::T;
-    __shared__ float As[GK][GT + 1];
-    __shared__ float Bs[GK][GT + 1];
+    // k-rows of 64 floats: a thread's 4 consecutive rows / columns are one
+    // 16-byte read (4x fewer LDS instructions than element reads: fp32
+    // 128x64x256 33 -> 29 us)
+    __shared__ __attribute__((aligned(16))) float As[GK][GT];
+    __shared__ __attribute__((aligned(16))) float Bs[GK][GT];
     const Prob &p = a.p;
     const int tiles_n = (int)((p.N + GT - 1) / GT);
     const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * GT;
@@ -148,11 +151,9 @@ __global__ void __launch_bounds__(256) gemm_generic(GenericArgs a) {
             if (s + GPF < steps) fetch((s + GPF) * GK, ra[u], rb[u], xa[u], xb[u]);
 #pragma unroll
             for (int kk = 0; kk < GK; ++kk) {
-                float x[4], y[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = As[kk][ty * 4 + i];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) y[j] = Bs[kk][tx * 4 + j];
+                const f32x4 xv = *reinterpret_cast<const f32x4 *>(&As[kk][ty * 4]);
+                const f32x4 yv = *reinterpret_cast<const f32x4 *>(&Bs[kk][tx * 4]);
+                const float x[4] = {xv.x, xv.y, xv.z, xv.w}, y[4] = {yv.x, yv.y, yv.z, yv.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
