@@ -1420,24 +1420,32 @@ struct Tile {
         const int tid = threadIdx.x;
         for (int jj = 0; jj < jc; ++jj) {
             const int64_t row = (m_base + (j0 + jj) * 32) * p.N;
-            for (int i = 0; i < FN; ++i)
+            for (int i = 0; i < FN; ++i) {
+                // the loads of a column block's four groups first, so they
+                // are in flight together (one at a time, each waited for,
+                // this epilogue cost ~130 us per 256 x 256 tile)
+                float c[4][4] = {}, b[4][4] = {}, x[4][4] = {};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t col = n_base + i * 32 + q * 8;
+                    if (e.beta != 0.0f) load4(C, row + col, c[q]);
+                    if (bias) load4(bias, col, b[q]);
+                    if (X) load4(X, row + col, x[q]);
+                }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int64_t idx = row + n_base + i * 32 + q * 8;
-                    float v[4], c[4] = {0.0f, 0.0f, 0.0f, 0.0f}, b[4] = {0.0f, 0.0f, 0.0f, 0.0f},
-                                x[4] = {0.0f, 0.0f, 0.0f, 0.0f}, z[4];
+                    float v[4], z[4];
                     const f32x4 a = vals[((jj * FN + i) * 4 + q) * NT + tid];
-                    if (e.beta != 0.0f) load4(C, idx, c);
-                    if (bias) load4(bias, n_base + i * 32 + q * 8, b);
-                    if (X) load4(X, idx, x);
 #pragma unroll
                     for (int t4 = 0; t4 < 4; ++t4) {
-                        const float lin = __builtin_fmaf(alpha, a[t4], e.beta * c[t4]) + b[t4];
-                        v[t4] = finish_aux_branch(lin, x[t4], e.aux_op, e.act, pre, post, z[t4]);
+                        const float lin = __builtin_fmaf(alpha, a[t4], e.beta * c[q][t4]) + b[q][t4];
+                        v[t4] = finish_aux_branch(lin, x[q][t4], e.aux_op, e.act, pre, post, z[t4]);
                     }
                     if (Z) store4(Z, idx, z);
                     store4(D, idx, v);
                 }
+            }
         }
     }
 
