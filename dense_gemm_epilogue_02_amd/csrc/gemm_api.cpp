@@ -370,6 +370,7 @@ struct gemm_plan_s {
     GroupDesc *ghost;
     hipEvent_t gevent;
     bool gevent_pending;
+    unsigned int *gqueue;      // grouped launches' tile queues (9 words, zero between launches)
     hipStream_t last_stream;
     bool used;
     // Tuned configurations (from gemm_plan_profile or an imported cache),
@@ -930,6 +931,7 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
     a.s.counters = nullptr;
     a.s.gdesc = nullptr;
     a.s.gcount = 0;
+    a.s.queue = nullptr;
     if (d.sk_tiles > 0 && d.split != 1) {
         const size_t pbytes = (size_t)2 * d.grid * d.e->bm * d.e->bn * sizeof(float);
         if (bt.noalloc) {
@@ -1085,6 +1087,7 @@ gemm_status gemm_plan_destroy(gemm_plan_t p) {
     if (p->gdesc) (void)hipFree(p->gdesc);
     if (p->gevent) (void)hipEventDestroy(p->gevent);
     if (p->ghost) (void)hipHostFree(p->ghost);
+    if (p->gqueue) (void)hipFree(p->gqueue);
     p->magic = 0;
     delete p;
     return st == GEMM_OK ? ok() : st;
@@ -1238,10 +1241,10 @@ gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32
     for (Class &c : cls) c.total = 0;
     const bool generic_only = pl->tile == GEMM_TILE_GENERIC;
     std::vector<int32_t> scalar_path;
-    // Tiles are dealt round-robin to the persistent workgroups in table
-    // order; listing the problems by decreasing K (the cost of each of their
-    // tiles) gives every round tiles of similar cost, so the workgroups finish
-    // together. Results do not depend on the order.
+    // Workgroups claim tiles in table order as they finish earlier ones;
+    // listing the problems by decreasing K (the cost of each of their tiles)
+    // hands out the costly tiles first and leaves the cheap ones to even out
+    // the finish (longest-first). Results do not depend on the order.
     std::vector<int32_t> order((size_t)count);
     for (int32_t i = 0; i < count; ++i) order[(size_t)i] = i;
     std::stable_sort(order.begin(), order.end(),
@@ -1345,6 +1348,17 @@ gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32
         pl->gdesc_count = n_desc;
         pl->gdesc_stream = hs;
     }
+    if (n_desc > 0 && !pl->gqueue) {
+        // zeroed once here; each launch leaves it zeroed for the next
+        hipError_t he = hipMalloc(reinterpret_cast<void **>(&pl->gqueue), 9 * sizeof(unsigned int));
+        if (he != hipSuccess) {
+            (void)hipGetLastError();
+            pl->gqueue = nullptr;
+            return fail(GEMM_OUT_OF_MEMORY, "grouped tile queue: %s", hipGetErrorString(he));
+        }
+        he = launch_zero_u32(pl->gqueue, 9, hs);
+        if (he != hipSuccess) return hip_fail(he, "zeroing the grouped tile queue");
+    }
     if (n_desc > 0) {
         hipError_t he;
         size_t first = 0;
@@ -1366,6 +1380,11 @@ gemm_status grouped_gemm_run(gemm_plan_t pl, const gemm_problem *problems, int32
             ka.s.xcd_remap = 1;
             ka.s.gdesc = pl->gdesc + first;
             ka.s.gcount = (int)c.table.size();
+            // tiles of the problems' different K cost different times: a
+            // workgroup takes the next unclaimed tile when it is done with
+            // one (problems are listed by decreasing K, so the costly tiles
+            // go first)
+            ka.s.queue = pl->gqueue;
             he = c.e->run(ka, ka.s.grid, hs);
             if (he != hipSuccess) return hip_fail(he, "grouped kernel launch");
             first += c.table.size();

@@ -311,6 +311,17 @@ struct Sched {
     // the last of the gcount problems whose tile_start is <= t.
     const GroupDesc *gdesc;
     int gcount;
+    // Optional work queues for the data-parallel tiles (schedules without
+    // stream-K or split-K): each workgroup takes tile v first, then the next
+    // unclaimed tile when it finishes one, so tiles of unequal cost (grouped
+    // problems of different K) spread evenly. With the XCD remap one queue
+    // per XCD: the tiles past the first `grid` go in chunks of grid / 8
+    // consecutive tiles to the XCDs in turn, so the workgroups of one XCD
+    // stay on neighbouring tiles (shared panels in its L2). queue[0 .. 7]
+    // count claims, queue[8] finished workgroups; the last workgroup to
+    // finish zeroes all nine, so they start at zero for the next launch on
+    // the stream.
+    unsigned int *queue;
 };
 
 // What the out-of-line epilogues need of a tile's problem.
@@ -1675,6 +1686,28 @@ __device__ __forceinline__ int sk_owner(int64_t x, int64_t T, int G) {
     return (int)(((x + 1) * G + T - 1) / T) - 1;
 }
 
+// The tile after `claim` (the queue's count before this workgroup's claim),
+// handed to every thread of the workgroup through the first word of the idle
+// LDS: the first barrier waits for the waves still reading the LDS (output
+// staging), the last keeps the next copy into LDS from overwriting the word
+// before every wave has read it. total_tiles when the queue is exhausted.
+__device__ __forceinline__ int queue_count(const Sched &s) {
+    return s.xcd_remap && (s.grid & 7) == 0 ? 8 : 1;
+}
+__device__ __forceinline__ int queue_next(unsigned int claim, const Sched &s, char *lds) {
+    int *slot = reinterpret_cast<int *>(lds);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int nq = queue_count(s), chunk = s.grid / nq, x = nq == 8 ? (int)(blockIdx.x & 7) : 0;
+        const int64_t t = s.grid + ((int64_t)(claim / chunk) * nq + x) * chunk + claim % chunk;
+        *slot = t < s.total_tiles ? (int)t : s.total_tiles;
+    }
+    __syncthreads();
+    const int t = *slot;
+    __syncthreads();
+    return t;
+}
+
 // Count this workgroup's arrival at `counter` (after its partial is stored);
 // true in every thread of the workgroup that arrives last, i.e. sees
 // `expected` earlier arrivals. The flag passes through the first word of the
@@ -1750,6 +1783,7 @@ gemm_persistent(KArgs a) {
     const int S = s.split;
     bool split_pending = S > 0 && v < s.sk_tiles * S;
     int dp_t = S > 0 ? s.total_tiles : s.sk_tiles + v;
+    const bool dyn = s.queue != nullptr;
 
     for (;;) {
         int t, kt0, n, stride;
@@ -1774,7 +1808,7 @@ gemm_persistent(KArgs a) {
             it = tile_it0 + k1;
         } else if (dp_t < s.total_tiles) {
             t = dp_t;
-            dp_t += s.grid;
+            dp_t = dyn ? s.total_tiles : dp_t + s.grid;
             kt0 = 0;
             n = -1;   // every k-tile of the tile's problem
             stride = 1;
@@ -1788,6 +1822,12 @@ gemm_persistent(KArgs a) {
         const Prob pt = TL::tile_problem(p, s, t, tm, tn);
         if (n < 0) n = pt.ipt;
         TL::mainloop(pt, tm, tn, kt0, n, stride, acc, lds);
+        // claim the next tile now; its number is needed only after the
+        // epilogue, whose stores hide the atomic's round trip
+        unsigned int claim = 0;
+        if (dyn && threadIdx.x == 0)
+            claim = __hip_atomic_fetch_add(s.queue + (queue_count(s) == 8 ? (blockIdx.x & 7) : 0), 1u,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         bool finish = mode == 0;
         int v0 = 0, v1 = 0;
         if (mode != 0) {
@@ -1822,6 +1862,17 @@ gemm_persistent(KArgs a) {
                 __hip_atomic_store(&s.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (mode != 0) __syncthreads();
+        if (dyn) dp_t = queue_next(claim, s, lds);
+    }
+    if (dyn && threadIdx.x == 0) {
+        // every claim of this workgroup has been made (its last one came back
+        // past the end); the last workgroup to get here resets the queue
+        const unsigned int done =
+            __hip_atomic_fetch_add(s.queue + 8, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == (unsigned int)s.grid - 1) {
+            for (int q = 0; q < 9; ++q)
+                __hip_atomic_store(s.queue + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 

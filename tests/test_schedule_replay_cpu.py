@@ -123,3 +123,54 @@ def test_forced_schedules_replay_clean_over_many_shapes():
         for p in list(plans.values()) + [f8, f32]:
             p.close()
     assert checked > 1000
+
+
+# ---- the grouped launches' tile queues ---------------------------------------
+#
+# With a queue, workgroup v (virtual id) runs tile v first; every later tile
+# comes from a claim on its XCD's queue (blockIdx & 7 when the grid is a
+# multiple of 8 and the XCD remap is on, else one queue). Claim c of queue x
+# is tile grid + ((c // chunk) * nq + x) * chunk + c % chunk, chunk = grid / nq;
+# a claim past the last tile ends the workgroup. The replay interleaves the
+# workgroups' claims in an arbitrary order (a seeded shuffle of who claims
+# next) and checks that every tile runs exactly once and that each queue's
+# claims run out only after all of its tiles were handed out.
+
+def queue_replay(total, grid, remap, order_seed):
+    import random
+    nq = 8 if remap and grid % 8 == 0 else 1
+    chunk = grid // nq
+    claims = [0] * nq
+    ran = {}
+    rng = random.Random(order_seed)
+    live = list(range(grid))           # blockIdx values still claiming
+    for w in live:
+        v = (w & 7) * (grid >> 3) + (w >> 3) if nq == 8 else w
+        ran[v] = ran.get(v, 0) + 1     # the first tile, no claim
+    claimed_total = 0
+    while live:
+        w = rng.choice(live)
+        x = (w & 7) if nq == 8 else 0
+        c = claims[x]
+        claims[x] += 1
+        claimed_total += 1
+        t = grid + ((c // chunk) * nq + x) * chunk + c % chunk
+        if t >= total:
+            live.remove(w)
+            continue
+        ran[t] = ran.get(t, 0) + 1
+    return ran, claimed_total, nq
+
+
+@pytest.mark.parametrize("remap", [0, 1])
+def test_tile_queue_runs_every_tile_once(remap):
+    for total, grid in [(1, 1), (7, 7), (8, 8), (9, 8), (512, 512), (513, 512), (5011, 512),
+                        (5011, 256), (1000, 24), (777, 40), (4096, 512), (130, 16)]:
+        grid = min(grid, total)
+        for seed in range(3):
+            ran, claimed, nq = queue_replay(total, grid, remap, seed)
+            assert sorted(ran) == list(range(total)), (total, grid, remap)
+            assert all(n == 1 for n in ran.values()), (total, grid, remap)
+            # one claim per tile run (the first tiles need none, and every
+            # workgroup makes one claim that comes back past the end)
+            assert claimed == total, (total, grid, claimed)
