@@ -66,6 +66,7 @@ class Tile(IntEnum):
     T64x256 = 3
     T32x256 = 4
     GENERIC = 5
+    WHOLEK = 6
 
 
 class GemmError(RuntimeError):

@@ -20,8 +20,9 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmi355_gemm.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["gemm_api.cpp", "kernels_generic.hip", "kernels_f32.hip", "kernels_f16.hip",
-           "kernels_bf16.hip", "kernels_f8.hip", "kernels_mxf8.hip", "kernels_mxf4.hip"]
+SOURCES = ["gemm_api.cpp", "kernels_generic.hip", "kernels_wholek.hip", "kernels_f32.hip",
+           "kernels_f16.hip", "kernels_bf16.hip", "kernels_f8.hip", "kernels_mxf8.hip",
+           "kernels_mxf4.hip"]
 
 ARCH = "gfx950"
 

@@ -172,12 +172,13 @@ const char *tile_enum_name(gemm_tile t) {
     case GEMM_TILE_64x256: return "64x256";
     case GEMM_TILE_32x256: return "32x256";
     case GEMM_TILE_GENERIC: return "generic";
+    case GEMM_TILE_WHOLEK: return "wholek";
     default: return "auto";
     }
 }
 
 bool parse_tile(const std::string &s, gemm_tile *t) {
-    for (int v = GEMM_TILE_AUTO; v <= GEMM_TILE_GENERIC; ++v)
+    for (int v = GEMM_TILE_AUTO; v <= GEMM_TILE_WHOLEK; ++v)
         if (s == tile_enum_name((gemm_tile)v)) { *t = (gemm_tile)v; return true; }
     return false;
 }
@@ -409,6 +410,7 @@ struct Decision {
     int sk_grid = 0;   // workgroups sharing the stream-K iterations (<= grid, <= sk_iters)
     int group_m = 4;
     int vec_cd = 0;
+    int wholek = 0;   // > 0: the whole-K kernel, this many MFMA steps per wave (e is null)
     const char *why_generic = "";
 };
 
@@ -425,6 +427,28 @@ const char *operand_vec_problem(const void *ptr, bool kc, int64_t contig, int64_
     const int64_t span = kc ? rows * contig * esz : (int64_t)kbytes * contig;
     if (span + 16 > 0x7FFFFFFFLL) return "operand row stride too large for 32-bit offsets";
     return nullptr;
+}
+
+// Why the whole-K kernel cannot take this problem (null: it can). It loads
+// K-contiguous operands 16 bytes at a time and addresses every operand with
+// 32-bit byte offsets.
+const char *wholek_problem(int fam, const void *A, const void *B, bool a_kc, bool b_kc, int64_t M,
+                           int64_t N, int64_t K, int64_t batch, bool mx) {
+    if (batch != 1 || mx) return "batched or MX-scaled";
+    if (K < 1 || wholek_steps(fam, K) == 0) return "K too long or unsupported element type";
+    const int esz = elem_bytes(fam);
+    if ((a_kc && (reinterpret_cast<uintptr_t>(A) % 16 || (K * esz) % 16)) ||
+        (b_kc && (reinterpret_cast<uintptr_t>(B) % 16 || (K * esz) % 16)))
+        return "K-contiguous operand not in 16-byte rows";
+    if (M * K * esz + 16 > 0x7FFFFFFFLL || N * K * esz + 16 > 0x7FFFFFFFLL)
+        return "operand beyond 32-bit offsets";
+    return nullptr;
+}
+
+// AUTO takes the whole-K kernel when 128x128 tiles would leave most CUs
+// idle and K is short enough for it (fp16 1024^3 + ReLU: 64 tiles).
+bool wholek_auto(int fam, int64_t M, int64_t N, int64_t K, int cus) {
+    return wholek_steps(fam, K) > 0 && cdiv(M, 128) * cdiv(N, 128) < cus;
 }
 
 // `batch`: problems of this shape in one launch. The 256x256 tile needs a
@@ -524,8 +548,28 @@ gemm_status decide(const gemm_plan_s *pl, const void *A, const void *B, const vo
                 (beta == 0.0f || reinterpret_cast<uintptr_t>(C) % (4 * osz) == 0) &&
                 reinterpret_cast<uintptr_t>(bias) % (4 * osz) == 0)
                    ? 1 : 0;
+    // (AUTO picks it only when the schedule is AUTO too: a pinned schedule
+    // asks for the tile kernels)
+    const bool want_wk = cfg.tile == GEMM_TILE_WHOLEK ||
+                         (cfg.tile == GEMM_TILE_AUTO && cfg.sched == GEMM_SCHED_AUTO && batch == 1 &&
+                          !mx_a && wholek_auto(fam, M, N, K, cus));
+    if (want_wk && !wholek_problem(fam, A, B, a_kc, b_kc, M, N, K, batch, mx_a != nullptr)) {
+        d.wholek = wholek_steps(fam, K);
+        d.sched = GEMM_SCHED_DATA_PARALLEL;
+        d.tiles_m = (int)cdiv(M, 32);
+        d.tiles_n = (int)cdiv(N, 32);
+        if ((int64_t)d.tiles_m * d.tiles_n > 0x7FFFFFFFLL)
+            return fail(GEMM_UNSUPPORTED, "whole-K kernel: more than 2^31 blocks");
+        d.total = d.tiles_m * d.tiles_n;
+        d.grid = d.total;
+        d.ipt = 1;
+        return GEMM_OK;
+    }
     if (cfg.tile != GEMM_TILE_GENERIC) {
-        gemm_tile t = cfg.tile == GEMM_TILE_AUTO ? pick_tile(fam, M, N, K, cus, batch) : cfg.tile;
+        // (a whole-K request it cannot take falls back to the heuristic tile)
+        gemm_tile t = cfg.tile == GEMM_TILE_AUTO || cfg.tile == GEMM_TILE_WHOLEK
+                          ? pick_tile(fam, M, N, K, cus, batch)
+                          : cfg.tile;
         const KernelEntry *e = registry().find(fam, a_kc, b_kc, tile_id(t));
         if (!e) e = registry().find(fam, a_kc, b_kc, TILE_128x128);
         const char *why = nullptr;
@@ -900,6 +944,18 @@ gemm_status run_one(gemm_plan_s *pl, const void *A, const void *B, const void *C
     p.mx_a = bt.mx_a;
     p.mx_b = bt.mx_b;
     const EpiArgs ep = make_epi(pl, alpha, beta, sa, sb, bias, bt);
+    if (d.wholek) {
+        GenericArgs g;
+        g.p = p;
+        g.e = ep;
+        g.la_row = pl->la == GEMM_ROW_MAJOR;
+        g.lb_row = pl->lb == GEMM_ROW_MAJOR;
+        hipError_t he = launch_wholek(fam, pl->la == GEMM_ROW_MAJOR, pl->lb == GEMM_COL_MAJOR,
+                                      d.wholek, g, hs);
+        if (he != hipSuccess) return hip_fail(he, "whole-K kernel launch");
+        note_stream(pl, hs);
+        return ok();
+    }
     if (!d.e) {
         if (batched) {   // the scalar kernel takes one problem per launch
             for (int64_t b = 0; b < bt.count && st == GEMM_OK; ++b) {
@@ -1097,7 +1153,7 @@ gemm_status gemm_plan_set_config(gemm_plan_t p, gemm_schedule s, gemm_tile t, in
     if (!plan_ok(p)) return fail(GEMM_NOT_INITIALIZED, "gemm_plan_set_config: invalid plan handle");
     if (s < GEMM_SCHED_AUTO || s > GEMM_SCHED_SPLIT_K)
         return fail(GEMM_INVALID_ARG, "gemm_plan_set_config: unknown schedule %d", (int)s);
-    if (t < GEMM_TILE_AUTO || t > GEMM_TILE_GENERIC)
+    if (t < GEMM_TILE_AUTO || t > GEMM_TILE_WHOLEK)
         return fail(GEMM_INVALID_ARG, "gemm_plan_set_config: unknown tile %d", (int)t);
     if (sk_grid < 0) return fail(GEMM_INVALID_ARG, "gemm_plan_set_config: sk_grid < 0");
     p->sched = s;
@@ -1430,7 +1486,9 @@ gemm_status gemm_plan_describe_batched(gemm_plan_t pl, int64_t M, int64_t N, int
              "{\"kernel\": \"%s\", \"tile\": \"%s\", \"bk\": %d, \"waves\": %d, \"schedule\": \"%s\", "
              "\"tiles\": %d, \"ipt\": %d, \"sk_tiles\": %d, \"split\": %d, \"grid\": %d, "
              "\"sk_grid\": %d, \"sk_iters\": %lld, \"generic_reason\": \"%s\"}",
-             d.e ? "tile" : "generic", tile_name(d.e), d.e ? d.e->bk : 16, d.e ? d.e->nt / 64 : 4,
+             d.wholek ? "wholek" : d.e ? "tile" : "generic", d.wholek ? "wholek32x32" : tile_name(d.e),
+             d.wholek ? 8 * d.wholek * (pl->fam == FAM_F32 ? 4 : 8) : d.e ? d.e->bk : 16,
+             d.e ? d.e->nt / 64 : 4,
              sched_name(d.sched), d.total, d.ipt, d.sk_tiles, d.split, d.grid, d.sk_grid,
              (long long)d.sk_iters, d.why_generic);
     return ok();
@@ -1460,7 +1518,7 @@ gemm_status gemm_plan_profile(gemm_plan_t pl, const void *A, const void *B, cons
     struct Cand {
         gemm_config c;
         const KernelEntry *e;
-        int sched, grid, split;
+        int sched, grid, split, wholek;
     };
     std::vector<Cand> done;
     hipEvent_t ev[2] = {nullptr, nullptr};
@@ -1473,7 +1531,7 @@ gemm_status gemm_plan_profile(gemm_plan_t pl, const void *A, const void *B, cons
     const int osz = out_bytes(pl->fam);
     std::vector<uint8_t> ref((size_t)(M * N) * osz), got((size_t)(M * N) * osz);
     const gemm_tile tiles[] = {GEMM_TILE_256x256, GEMM_TILE_128x128, GEMM_TILE_64x256,
-                               GEMM_TILE_32x256, GEMM_TILE_GENERIC};
+                               GEMM_TILE_32x256, GEMM_TILE_GENERIC, GEMM_TILE_WHOLEK};
     const gemm_schedule scheds[] = {GEMM_SCHED_DATA_PARALLEL, GEMM_SCHED_STREAM_K,
                                     GEMM_SCHED_HYBRID, GEMM_SCHED_SPLIT_K};
     for (gemm_tile t : tiles) {
@@ -1496,13 +1554,13 @@ gemm_status gemm_plan_profile(gemm_plan_t pl, const void *A, const void *B, cons
             bool dup = false;
             for (const Cand &c : done)
                 dup |= c.e == d.e && c.sched == (int)d.sched && c.grid == d.grid &&
-                       c.split == d.split;
+                       c.split == d.split && c.wholek == d.wholek;
             if (dup) continue;
             // the resolved choice (the registry may fall back to another
             // tile), so the report names what ran and a cached entry
             // reproduces this launch
             pl->sched = d.sched;
-            pl->tile = d.e ? tile_enum(d.e->tile) : GEMM_TILE_GENERIC;
+            pl->tile = d.wholek ? GEMM_TILE_WHOLEK : d.e ? tile_enum(d.e->tile) : GEMM_TILE_GENERIC;
             // the untimed run writes into a NaN-filled D, and its result must
             // match the first candidate's (up to summation order) before this
             // launch may be timed and cached: an output the launch fails to
@@ -1522,7 +1580,8 @@ gemm_status gemm_plan_profile(gemm_plan_t pl, const void *A, const void *B, cons
                         const int64_t j = pl->lc == GEMM_ROW_MAJOR ? bad % N : bad / M;
                         st = fail(GEMM_HIP_ERROR,
                                   "gemm_plan_profile: %s %s (grid %d) disagrees with %s %s at D[%lld][%lld]",
-                                  tile_name(d.e), sched_name(d.sched), d.grid, tile_name(done[0].e),
+                                  d.wholek ? "wholek32x32" : tile_name(d.e), sched_name(d.sched), d.grid,
+                                  done[0].wholek ? "wholek32x32" : tile_name(done[0].e),
                                   sched_name((gemm_schedule)done[0].sched), (long long)i, (long long)j);
                         break;
                     }
@@ -1547,6 +1606,7 @@ gemm_status gemm_plan_profile(gemm_plan_t pl, const void *A, const void *B, cons
             c.sched = (int)d.sched;
             c.grid = d.grid;
             c.split = d.split;
+            c.wholek = d.wholek;
             done.push_back(c);
         }
         if (st != GEMM_OK || he != hipSuccess) break;

@@ -1563,13 +1563,23 @@ struct Tile {
 
     static constexpr int SC1 = 16;   // cache-policy bit: device scope
 
-    static __device__ __forceinline__ void store_partial(float *slot, const Acc &acc) {
-        const int tid = threadIdx.x;
+    // A partial tile is stored group-major (16-byte group g of thread tid at
+    // (g * NT + tid) * 16). Lanes whose M row lies past the problem (rows
+    // mrows .. BM-1 of an edge tile, e.g. all but 16 of a 64-row tile for a
+    // 16-token decode GEMM) neither store nor load their groups: their lane
+    // offset is out of the buffer's range, so the hardware drops the store
+    // and returns zeros to the load, and the epilogue never writes those rows.
+    static __device__ __forceinline__ uint32_t part_voff(int j, int mrows) {
+        const int tid = threadIdx.x, wave = tid >> 6, wm = wave / WN;
+        return wm * WTM + j * 32 + (tid & 31) < mrows ? (uint32_t)(tid * 16) : OOB_OFFSET;
+    }
+    static __device__ __forceinline__ void store_partial(float *slot, const Acc &acc, int mrows) {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot);
 #pragma unroll
-        for (int i = 0; i < FN; ++i)
+        for (int j = 0; j < FM; ++j) {
+            const uint32_t vo = part_voff(j, mrows);
 #pragma unroll
-            for (int j = 0; j < FM; ++j)
+            for (int i = 0; i < FN; ++i)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int grp = (i * FM + j) * 4 + q;
@@ -1577,9 +1587,10 @@ struct Tile {
                                   acc.v[i][j][q * 4 + 3]};
                     // the group's offset in the scalar offset: one lane
                     // offset for all groups instead of one register each
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t), rs,
-                                                           (uint32_t)(tid * 16), grp * NT * 16, SC1);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t), rs, vo,
+                                                           grp * NT * 16, SC1);
                 }
+        }
     }
 
     // acc = sum of the partials slot(0) .. slot(n-1), added in that order.
@@ -1587,13 +1598,14 @@ struct Tile {
     // dependent load round trips (the sum and its rounding are unchanged).
     static constexpr bool PAIRED_FIXUP = FN * FM <= 4;
 
-    static __device__ __forceinline__ void load_partial(const float *slot, f32x4 (&t)[FN * FM * 4]) {
-        const int tid = threadIdx.x;
+    static __device__ __forceinline__ void load_partial(const float *slot, f32x4 (&t)[FN * FM * 4],
+                                                        int mrows) {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot);
 #pragma unroll
         for (int g = 0; g < FN * FM * 4; ++g)
             t[g] = __builtin_bit_cast(
-                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((g * NT + tid) * 16), 0, SC1));
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, part_voff((g >> 2) % FM, mrows),
+                                                             g * NT * 16, SC1));
     }
     static __device__ __forceinline__ void accumulate(const f32x4 (&t)[FN * FM * 4], Acc &acc, bool first) {
 #pragma unroll
@@ -1610,30 +1622,30 @@ struct Tile {
     }
 
     template <class SlotFn>
-    static __device__ __forceinline__ void add_partials(SlotFn slot, int n, Acc &acc) {
+    static __device__ __forceinline__ void add_partials(SlotFn slot, int n, Acc &acc, int mrows) {
         if constexpr (PAIRED_FIXUP) {
             int u = 0;
             for (; u + 1 < n; u += 2) {
                 f32x4 t0[FN * FM * 4], t1[FN * FM * 4];
-                load_partial(slot(u), t0);
-                load_partial(slot(u + 1), t1);
+                load_partial(slot(u), t0, mrows);
+                load_partial(slot(u + 1), t1, mrows);
                 accumulate(t0, acc, u == 0);
                 accumulate(t1, acc, false);
             }
             if (u < n) {
                 f32x4 t0[FN * FM * 4];
-                load_partial(slot(u), t0);
+                load_partial(slot(u), t0, mrows);
                 accumulate(t0, acc, u == 0);
             }
         } else {
-            for (int u = 0; u < n; ++u) add_partial(slot(u), acc, u == 0);
+            for (int u = 0; u < n; ++u) add_partial(slot(u), acc, u == 0, mrows);
         }
     }
 
     // One partial added into acc, its 16-byte groups fetched eight at a time
     // (eight device-scope loads in flight per round trip instead of one).
-    static __device__ __forceinline__ void add_partial(const float *slot, Acc &acc, bool first) {
-        const int tid = threadIdx.x;
+    static __device__ __forceinline__ void add_partial(const float *slot, Acc &acc, bool first,
+                                                       int mrows) {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot);
         constexpr int NG = FN * FM * 4, CHUNK = 8;
         static_assert(NG % CHUNK == 0, "partial groups");
@@ -1643,8 +1655,8 @@ struct Tile {
 #pragma unroll
             for (int c = 0; c < CHUNK; ++c)
                 t[c] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(tid * 16),
-                                                                 (g0 + c) * NT * 16, SC1));
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               rs, part_voff(((g0 + c) >> 2) % FM, mrows), (g0 + c) * NT * 16, SC1));
 #pragma unroll
             for (int c = 0; c < CHUNK; ++c) {
                 const int grp = g0 + c, q = grp & 3, ij = grp >> 2, i = ij / FM, j = ij % FM;
@@ -1834,7 +1846,8 @@ gemm_persistent(KArgs a) {
             // every contributor publishes its partial; the last to arrive
             // sums all of them in contributor order (deterministic)
             const int my_slot = mode == 2 ? v : 2 * v + (t == first_tile ? 0 : 1);
-            TL::store_partial(s.partials + (size_t)my_slot * slot_elems, acc);
+            const int mrows = (int)imin64(pt.M - (int64_t)tm * TL::BM, TL::BM);
+            TL::store_partial(s.partials + (size_t)my_slot * slot_elems, acc, mrows);
             wait_vmcnt<0>();   // this thread's device-scope stores are complete
             __syncthreads();   // ... and every thread's, before the arrival is counted
             if (mode == 2) {
@@ -1853,7 +1866,7 @@ gemm_persistent(KArgs a) {
                         const int ft = (int)(((int64_t)u * T / G) / p.ipt);
                         return s.partials + (size_t)(2 * u + (t == ft ? 0 : 1)) * slot_elems;
                     },
-                    v1 - v0 + 1, acc);
+                    v1 - v0 + 1, acc, mrows);
             }
         }
         if (finish) {

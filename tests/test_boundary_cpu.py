@@ -139,9 +139,25 @@ def test_describe_transformer_layer_schedules():
 
 def test_describe_small_and_skinny_use_stream_k():
     p = g.Plan("f16", la="row", lb="row", lc="row", relu=True)
+    # 64 tiles of 128x128 for 256 CUs and K = 1024: the whole-K kernel, one
+    # workgroup per 32x32 block, 16 MFMA steps per wave (4 x 256 of K)
     d = p.describe(1024, 1024, 1024)
-    assert d["tile"] == "128x128" and d["schedule"] == "stream_k" and d["ipt"] == 16
+    assert d["kernel"] == "wholek" and d["tile"] == "wholek32x32" and d["grid"] == 1024, d
+    assert d["bk"] == 1024 and d["schedule"] == "data_parallel", d
+    # K = 2048 is past its reach: 128x128 tiles under stream-K
+    d = p.describe(1024, 1024, 2048)
+    assert d["tile"] == "128x128" and d["schedule"] == "stream_k" and d["ipt"] == 32, d
+    # the 128x128 tile on the 1024^3 problem, when pinned
+    p.set_config(g.Schedule.AUTO, g.Tile.T128x128, 0)
+    d = p.describe(1024, 1024, 1024)
+    assert d["tile"] == "128x128" and d["schedule"] == "stream_k" and d["ipt"] == 16, d
     p.close()
+    f = g.Plan("f32", la="row", lb="row", lc="row")
+    d = f.describe(128, 64, 256)
+    assert d["kernel"] == "wholek" and d["grid"] == 8 and d["bk"] == 256, d
+    d = f.describe(128, 64, 1024)   # fp32 whole-K reaches K = 512
+    assert d["kernel"] == "tile", d
+    f.close()
     q = _plan("f8e4m3")
     # decode GEMMs on the four-stage fp8 tiles (one workgroup per CU): 32-64
     # tiles for 256 slots, so stream-K over every CU
@@ -397,12 +413,13 @@ def test_profile_validation_before_any_device_call():
 def test_describe_batched_tile_choice():
     """A batch that supplies a full wave of 256x256 tiles gets them when K is
     long (K >= 2048); with K = 1024 it keeps 128x128 tiles, and the tile count
-    covers the batch."""
+    covers the batch. (A single 1024^3 problem goes to the whole-K kernel,
+    which takes no batches.)"""
     h = g.gemm_plan_create_simple(g.Dtype.F16, g.Layout.ROW_MAJOR, g.Epilogue.LINEAR)
     try:
         one = g.gemm_plan_describe_batched(h, 1024, 1024, 1024, 1)
         assert one == g.gemm_plan_describe(h, 1024, 1024, 1024)
-        assert one["tile"] == "128x128"
+        assert one["tile"] == "wholek32x32"
         b16 = g.gemm_plan_describe_batched(h, 1024, 1024, 1024, 16)
         assert b16["tile"] == "128x128" and b16["tiles"] == 1024
         assert b16["schedule"] == "data_parallel"

@@ -92,7 +92,8 @@ def test_aux_integer_exact_ops(op, pos, dtype_ab, dtype_cd, lc):
     exact(p, "relu", f"{op}/{pos} {dtype_ab} {lc}")
 
 
-@pytest.mark.parametrize("tile", [T.T256x256, T.T128x128, T.T64x256, T.T32x256, T.GENERIC])
+@pytest.mark.parametrize("tile", [T.T256x256, T.T128x128, T.T64x256, T.T32x256, T.GENERIC,
+                                  T.WHOLEK])
 @pytest.mark.parametrize("la,lb", [("row", "col"), ("row", "row"), ("col", "col")])
 def test_aux_integer_exact_tiles(tile, la, lb):
     p = syn.integer_problem(300, 520, 136, dtype_ab="bf16", dtype_cd="bf16", la=la, lb=lb,

@@ -37,7 +37,8 @@ def test_profile_times_every_launch_and_caches_the_fastest(M, N, K):
     best = res[0]
     desc = plan.describe(M, N, K)
     names = {g.Tile.T256x256: "256x256", g.Tile.T128x128: "128x128", g.Tile.T64x256: "64x256",
-             g.Tile.T32x256: "32x256", g.Tile.GENERIC: "generic64x64"}
+             g.Tile.T32x256: "32x256", g.Tile.GENERIC: "generic64x64",
+             g.Tile.WHOLEK: "wholek32x32"}
     assert desc["tile"] == names[best["tile"]]
     ent = json.loads(plan.cache_export())["entries"]
     assert [(e["m"], e["n"], e["k"]) for e in ent] == [(M, N, K)]
