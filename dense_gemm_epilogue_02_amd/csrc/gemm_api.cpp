@@ -1488,7 +1488,7 @@ gemm_status gemm_plan_describe_batched(gemm_plan_t pl, int64_t M, int64_t N, int
              "\"sk_grid\": %d, \"sk_iters\": %lld, \"generic_reason\": \"%s\"}",
              d.wholek ? "wholek" : d.e ? "tile" : "generic", d.wholek ? "wholek32x32" : tile_name(d.e),
              d.wholek ? 8 * d.wholek * (pl->fam == FAM_F32 ? 4 : 8) : d.e ? d.e->bk : 16,
-             d.e ? d.e->nt / 64 : 4,
+             d.e ? d.e->nt / 64 : d.wholek == 32 ? 8 : 4,
              sched_name(d.sched), d.total, d.ipt, d.sk_tiles, d.split, d.grid, d.sk_grid,
              (long long)d.sk_iters, d.why_generic);
     return ok();

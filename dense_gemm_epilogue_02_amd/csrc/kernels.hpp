@@ -49,11 +49,11 @@ hipError_t launch_generic(int fam, const GenericArgs &a, hipStream_t st);
 
 // Whole-K kernel for small problems (kernels_wholek.hip): 32x32 blocks of D,
 // each of a workgroup's four waves loading its quarter of K at once. Steps:
-// MFMA steps per wave (1, 2, 4, 8 or 16), from wholek_steps (0: K too long
-// or not an fp32/fp16/bf16 family). K-contiguous operands need 16-byte
-// aligned bases and K * element size % 16 == 0; every operand's byte span
-// must stay below 2^31.
-constexpr int WHOLEK_MAX_STEPS = 16;
+// MFMA steps per wave (1, 2, 4, 8 or 16; 32 = eight waves of 16, fp32
+// only), from wholek_steps (0: K too long or not an fp32/fp16/bf16
+// family): K <= 32 * steps * (fp32 ? 4 : 8). K-contiguous operands need
+// 16-byte aligned bases and K * element size % 16 == 0; every operand's
+// byte span must stay below 2^31.
 int wholek_steps(int fam, int64_t K);
 hipError_t launch_wholek(int fam, bool a_kc, bool b_kc, int steps, const GenericArgs &a,
                          hipStream_t st);

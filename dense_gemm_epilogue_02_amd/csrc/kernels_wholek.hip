@@ -66,15 +66,20 @@ __device__ __forceinline__ u32x4 wk_load(__amdgpu_buffer_rsrc_t rs, int64_t row,
     }
 }
 
-template <int FAM, bool A_KC, bool B_KC, int T>
-__global__ void __launch_bounds__(256) gemm_wholek(GenericArgs a) {
+template <int FAM, bool A_KC, bool B_KC, int T, int W>
+__global__ void __launch_bounds__(64 * W) gemm_wholek(GenericArgs a) {
     using Out = typename WkOut<FAM>::T;
     constexpr int VPL = wk_vpl<FAM>(), KW = 2 * VPL * T;   // K per wave
-    __shared__ float part[4][32][33];   // [wave][m][n], rows padded against bank conflicts
+    constexpr int NT = 64 * W, OPT = 1024 / NT;             // threads; outputs per thread
+    __shared__ float part[W][32][33];   // [wave][m][n], rows padded against bank conflicts
     const Prob &p = a.p;
-    const int tiles_n = (int)((p.N + 31) / 32);
-    const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * 32;
-    const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * 32;
+    // blocks in groups of 8 block-rows, and each XCD (workgroups are dealt
+    // to the 8 XCDs in turn) on one contiguous run of them: the operand
+    // panels an XCD reads fit its L2
+    const int tiles_m = (int)((p.M + 31) / 32), tiles_n = (int)((p.N + 31) / 32);
+    int bm, bn;
+    tile_coords(virtual_id((int)blockIdx.x, (int)gridDim.x, 1), tiles_m, tiles_n, 8, bm, bn);
+    const int64_t m0 = (int64_t)bm * 32, n0 = (int64_t)bn * 32;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 31, h = lane >> 5;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A), rb = make_rsrc(p.B);
     const int64_t kb = (int64_t)w * KW + h * VPL;
@@ -102,14 +107,16 @@ __global__ void __launch_bounds__(256) gemm_wholek(GenericArgs a) {
     if (a.e.scale_b) alpha *= *a.e.scale_b;
     Out *D = reinterpret_cast<Out *>(p.D);
     const Out *C = reinterpret_cast<const Out *>(p.C);
-    // four outputs per thread, consecutive in D's contiguous dimension
-    const int i0 = tid >> 3, j0 = (tid & 7) * 4;
+    // OPT outputs per thread, consecutive in D's contiguous dimension
+    const int i0 = tid / (32 / OPT), j0 = (tid % (32 / OPT)) * OPT;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < OPT; ++u) {
         const int mm = a.e.lc_row ? i0 : j0 + u, nn = a.e.lc_row ? j0 + u : i0;
         const int64_t m = m0 + mm, n = n0 + nn;
         if (m >= p.M || n >= p.N) continue;
-        const float s = ((part[0][mm][nn] + part[1][mm][nn]) + part[2][mm][nn]) + part[3][mm][nn];
+        float s = part[0][mm][nn];   // the waves' partial sums in wave order
+#pragma unroll
+        for (int q = 1; q < W; ++q) s += part[q][mm][nn];
         const int64_t idx = a.e.lc_row ? m * p.N + n : m + n * p.M;
         float v = alpha * s;
         if (a.e.beta != 0.0f) v = __builtin_fmaf(alpha, s, a.e.beta * (float)C[idx]);
@@ -123,12 +130,19 @@ __global__ void __launch_bounds__(256) gemm_wholek(GenericArgs a) {
 
 template <int FAM, bool A_KC, bool B_KC>
 hipError_t launch_t(int steps, dim3 grid, const GenericArgs &a, hipStream_t st) {
+    const dim3 b4(256), b8(512);
     switch (steps) {
-    case 1: hipLaunchKernelGGL((gemm_wholek<FAM, A_KC, B_KC, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((gemm_wholek<FAM, A_KC, B_KC, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((gemm_wholek<FAM, A_KC, B_KC, 4>), grid, dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((gemm_wholek<FAM, A_KC, B_KC, 8>), grid, dim3(256), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((gemm_wholek<FAM, A_KC, B_KC, 16>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((gemm_wholek<FAM, A_KC, B_KC, 1, 4>), grid, b4, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((gemm_wholek<FAM, A_KC, B_KC, 2, 4>), grid, b4, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((gemm_wholek<FAM, A_KC, B_KC, 4, 4>), grid, b4, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((gemm_wholek<FAM, A_KC, B_KC, 8, 4>), grid, b4, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((gemm_wholek<FAM, A_KC, B_KC, 16, 4>), grid, b4, 0, st, a); break;
+    case 32:   // eight waves of 16 steps (fp32 only)
+        if constexpr (FAM == FAM_F32) {
+            hipLaunchKernelGGL((gemm_wholek<FAM, A_KC, B_KC, 16, 8>), grid, b8, 0, st, a);
+            break;
+        }
+        return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -145,11 +159,15 @@ hipError_t launch_fam(bool a_kc, bool b_kc, int steps, dim3 grid, const GenericA
 
 }  // namespace
 
+// 16-step waves need at most 152 registers (220 with an element-loaded
+// 16-bit operand); fp32, whose MFMA takes 4 K per step, gets an
+// eight-wave form (K <= 1024) reported as 32 steps.
 int wholek_steps(int fam, int64_t K) {
     if (fam != FAM_F32 && fam != FAM_F16 && fam != FAM_BF16) return 0;
     const int64_t per_step = 8 * (fam == FAM_F32 ? 4 : 8);   // K of one step over 4 waves x 2 halves
-    for (int t = 1; t <= WHOLEK_MAX_STEPS; t *= 2)
+    for (int t = 1; t <= 16; t *= 2)
         if ((int64_t)t * per_step >= K) return t;
+    if (fam == FAM_F32 && 32 * per_step >= K) return 32;
     return 0;
 }
 

@@ -115,7 +115,7 @@ typedef enum {
     GEMM_TILE_32x256 = 4,
     GEMM_TILE_GENERIC = 5,  /* the scalar-load kernel, for any alignment */
     GEMM_TILE_WHOLEK = 6    /* 32x32 blocks, all of K loaded at once: small problems with
-                               K <= 512 (fp32) or 1024 (fp16/bf16); batch 1, no MX scales */
+                               K <= 1024 (fp32, fp16, bf16); batch 1, no MX scales */
 } gemm_tile;
 
 typedef struct gemm_plan_s *gemm_plan_t;

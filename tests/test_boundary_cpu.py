@@ -155,7 +155,9 @@ def test_describe_small_and_skinny_use_stream_k():
     f = g.Plan("f32", la="row", lb="row", lc="row")
     d = f.describe(128, 64, 256)
     assert d["kernel"] == "wholek" and d["grid"] == 8 and d["bk"] == 256, d
-    d = f.describe(128, 64, 1024)   # fp32 whole-K reaches K = 512
+    d = f.describe(1024, 1024, 1024)   # eight waves of 128 K each
+    assert d["kernel"] == "wholek" and d["bk"] == 1024 and d["waves"] == 8, d
+    d = f.describe(128, 64, 1040)   # fp32 whole-K reaches K = 1024
     assert d["kernel"] == "tile", d
     f.close()
     q = _plan("f8e4m3")

@@ -1,8 +1,8 @@
 """GPU parity of the whole-K kernel (GEMM_TILE_WHOLEK) against the CPU oracle.
 
 Each workgroup owns a 32x32 block of D and its four waves load a quarter of K
-each, all at once; the kernel takes fp32 problems with K <= 512 and fp16 /
-bf16 ones with K <= 1024. Bars as elsewhere: bit-exact on integer-valued data,
+each, all at once (fp32 beyond K = 512: eight waves of an eighth); it takes
+problems with K <= 1024. Bars as elsewhere: bit-exact on integer-valued data,
 the oracle's tolerances otherwise. Every case first checks (host-only
 describe) that the launch really is the whole-K kernel, so a silent fallback
 to the tile kernels cannot pass for it.
@@ -56,10 +56,9 @@ def test_wholek_integer_exact_all_layouts(dab, dcd, la, lb, lc):
 
 @pytest.mark.parametrize("dab,dcd", FAMS)
 def test_wholek_k_extents(dab, dcd):
-    kmax = 512 if dab == "f32" else 1024
-    # K = 8: one step, three waves past K; 40: waves ending mid-range; the
-    # longest K the kernel takes (16 steps per wave)
-    for K in (8, 40, kmax - 8, kmax):
+    # K = 8: one step, three waves past K; 40: waves ending mid-range; 512
+    # and 1024 - 8, 1024: 16 steps per wave (fp32: four, then eight waves)
+    for K in (8, 40, 504, 512, 520, 1016, 1024):
         _exact(_int(dab, dcd, M=33, N=64, K=K, seed=K), what=f"{dab} K={K}")
 
 
@@ -104,6 +103,14 @@ def test_wholek_random_tolerance(dtype):
                            f"{dtype} 200x136x1000 whole-K")
 
 
+def test_wholek_fp32_eight_waves_ones_closed_form():
+    # the all-ones 1024^3 fp32 problem: D = K + 1 everywhere
+    p = syn.config1_ones(1024, "f32")
+    d = _is_wholek(p)
+    assert d["waves"] == 8
+    assert (run(p, tile=T.WHOLEK) == 1025.0).all()
+
+
 def test_wholek_deterministic():
     p = syn.make_problem(96, 80, 512, dtype_ab="f32", dtype_cd="f32", dist_c="normal", seed=4)
     a = run(p, tile=T.WHOLEK)
@@ -112,9 +119,9 @@ def test_wholek_deterministic():
 
 
 def test_wholek_falls_back_when_it_cannot_take_the_problem():
-    # fp32 K = 520 is past its reach; K-contiguous fp16 rows of 13 elements are
+    # K = 1040 is past its reach; K-contiguous fp16 rows of 13 elements are
     # not 16-byte rows: both run on the other kernels, still exact
-    for p in (_int("f32", "f32", K=520), _int("f16", "f16", la="row", lb="col", K=13)):
+    for p in (_int("f32", "f32", K=1040), _int("f16", "f16", la="row", lb="col", K=13)):
         plan = g.Plan(p.dtype_ab, p.dtype_cd, p.la, p.lb, p.lc)
         plan.set_config(S.AUTO, T.WHOLEK, 0)
         d = plan.describe(p.M, p.N, p.K)
