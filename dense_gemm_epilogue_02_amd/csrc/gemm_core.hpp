@@ -1594,9 +1594,11 @@ struct Tile {
     }
 
     // acc = sum of the partials slot(0) .. slot(n-1), added in that order.
-    // Small accumulators fetch two partials per round, halving the number of
-    // dependent load round trips (the sum and its rounding are unchanged).
-    static constexpr bool PAIRED_FIXUP = FN * FM <= 4;
+    // Small accumulators fetch several partials per round (four for at most
+    // two fragments, two for at most four), cutting the number of dependent
+    // load round trips (the sum and its rounding are unchanged).
+    static constexpr int FIXUP_BATCH = FN * FM <= 2 ? 4 : FN * FM <= 4 ? 2 : 1;
+    static constexpr bool PAIRED_FIXUP = FIXUP_BATCH > 1;
 
     static __device__ __forceinline__ void load_partial(const float *slot, f32x4 (&t)[FN * FM * 4],
                                                         int mrows) {
@@ -1624,18 +1626,24 @@ struct Tile {
     template <class SlotFn>
     static __device__ __forceinline__ void add_partials(SlotFn slot, int n, Acc &acc, int mrows) {
         if constexpr (PAIRED_FIXUP) {
+            constexpr int R = FIXUP_BATCH;
             int u = 0;
-            for (; u + 1 < n; u += 2) {
-                f32x4 t0[FN * FM * 4], t1[FN * FM * 4];
-                load_partial(slot(u), t0, mrows);
-                load_partial(slot(u + 1), t1, mrows);
-                accumulate(t0, acc, u == 0);
-                accumulate(t1, acc, false);
+            for (; u + R - 1 < n; u += R) {
+                f32x4 t[R][FN * FM * 4];
+#pragma unroll
+                for (int b = 0; b < R; ++b) load_partial(slot(u + b), t[b], mrows);
+#pragma unroll
+                for (int b = 0; b < R; ++b) accumulate(t[b], acc, u + b == 0);
             }
-            if (u < n) {
-                f32x4 t0[FN * FM * 4];
-                load_partial(slot(u), t0, mrows);
-                accumulate(t0, acc, u == 0);
+            if (u < n) {   // the last 1 .. R-1 partials, also in one round
+                const int rem = n - u;
+                f32x4 t[R - 1][FN * FM * 4];
+#pragma unroll
+                for (int b = 0; b < R - 1; ++b)
+                    if (b < rem) load_partial(slot(u + b), t[b], mrows);
+#pragma unroll
+                for (int b = 0; b < R - 1; ++b)
+                    if (b < rem) accumulate(t[b], acc, u + b == 0);
             }
         } else {
             for (int u = 0; u < n; ++u) add_partial(slot(u), acc, u == 0, mrows);
