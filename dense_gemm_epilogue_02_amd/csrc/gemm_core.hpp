@@ -1419,7 +1419,7 @@ struct Tile {
     // accumulators of fragment rows j0 .. j0+jc-1 arrive through the idle LDS:
     // group ((jj * FN + i) * 4 + q) of thread tid at vals[group * NT + tid].
     template <class PO, class EA>
-    static __device__ __noinline__ void epi_aux(PO p, EA e, float alpha,
+    static __device__ __forceinline__ void epi_aux_i(PO p, EA e, float alpha,
                                                 int64_t m_base, int64_t n_base, const f32x4 *vals,
                                                 int j0, int jc) {
         Out *D = reinterpret_cast<Out *>(p.D);
@@ -1459,6 +1459,12 @@ struct Tile {
             }
         }
     }
+    template <class PO, class EA>
+    static __device__ __noinline__ void epi_aux(PO p, EA e, float alpha,
+                                                int64_t m_base, int64_t n_base, const f32x4 *vals,
+                                                int j0, int jc) {
+        epi_aux_i<PO, EA>(p, e, alpha, m_base, n_base, vals, j0, jc);
+    }
 
     // Fragment rows per LDS hand-off to epi_aux: as many as the tile's LDS holds.
     static constexpr int AUX_JC_FIT = LDS_BYTES / (NT * FN * 4 * 16);
@@ -1469,7 +1475,7 @@ struct Tile {
     // the accumulators of fragment rows j0 .. j0+jc-1 handed over through the
     // idle LDS exactly as for epi_aux (no private scratch array).
     template <class PO, class EA>
-    static __device__ __noinline__ void epi_slow(PO p, EA e, float alpha,
+    static __device__ __forceinline__ void epi_slow_i(PO p, EA e, float alpha,
                                                  int64_t m_base, int64_t n_base, const f32x4 *vals,
                                                  int j0, int jc) {
         Out *D = reinterpret_cast<Out *>(p.D);
@@ -1499,6 +1505,12 @@ struct Tile {
                     }
                 }
         }
+    }
+    template <class PO, class EA>
+    static __device__ __noinline__ void epi_slow(PO p, EA e, float alpha,
+                                                 int64_t m_base, int64_t n_base, const f32x4 *vals,
+                                                 int j0, int jc) {
+        epi_slow_i<PO, EA>(p, e, alpha, m_base, n_base, vals, j0, jc);
     }
 
     // `lds`: the tile's LDS, idle here (the main loop ends with a barrier);
@@ -1547,9 +1559,9 @@ struct Tile {
                 else epi_slow<EpiOut, EpiArgs>(o, e, alpha, m_base, n_base, buf, j0, AUX_JC);
             } else {
                 if (interior)
-                    epi_aux<const Prob &, const EpiArgs &>(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
+                    epi_aux_i<const Prob &, const EpiArgs &>(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
                 else
-                    epi_slow<const Prob &, const EpiArgs &>(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
+                    epi_slow_i<const Prob &, const EpiArgs &>(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
             }
         }
         __syncthreads();
