@@ -255,7 +255,7 @@ __device__ __forceinline__ float finish_aux(float v, float x, int op, int act, b
     return post ? s : d;
 }
 // finish_aux with the op and activation chosen by (uniform) branches: only
-// the selected arithmetic runs. For the out-of-line epilogue, where the
+// the selected arithmetic runs. For the general epilogues, where the
 // branches stay few.
 __device__ __forceinline__ float aux_op_branch(float y, float x, int op) {
     switch (op) {
@@ -322,13 +322,6 @@ struct Sched {
     // finish zeroes all nine, so they start at zero for the next launch on
     // the stream.
     unsigned int *queue;
-};
-
-// What the out-of-line epilogues need of a tile's problem.
-struct EpiOut {
-    char *D;
-    const char *C;
-    int64_t M, N;
 };
 
 struct KArgs {
@@ -1358,9 +1351,8 @@ struct Tile {
     // act(alpha acc) per lane (four
     // consecutive n of one m for each (i, j, q)) into the LDS (idle on
     // entry), which the workgroup then writes back as whole rows with
-    // 16-byte stores (D 16-byte aligned, rows a multiple of 16 bytes). The
-    // one inlined epilogue of a kernel, kept this small so the main loop's
-    // register allocation is unaffected; the other cases run out of line.
+    // 16-byte stores (D 16-byte aligned, rows a multiple of 16 bytes): the
+    // common case, kept small; the other cases take epi_aux or epi_slow.
     static __device__ __forceinline__ void epi_fast(const Prob &p, const EpiArgs &e, float alpha,
                                                     int64_t m_base, int64_t n_base, const Acc &acc,
                                                     char *lds, int tm, int tn) {
@@ -1413,15 +1405,13 @@ struct Tile {
         __syncthreads();
     }
 
-    // Interior tile with auxiliary tensors: the same vector accesses as
-    // epi_fast (X read like C, Z written like D), out of line so the tile
-    // kernels' own code and registers stay as they are without them. The
+    // Interior tile with C, bias or auxiliary tensors: the same vector
+    // accesses as epi_fast (X read like C, Z written like D). The
     // accumulators of fragment rows j0 .. j0+jc-1 arrive through the idle LDS:
     // group ((jj * FN + i) * 4 + q) of thread tid at vals[group * NT + tid].
-    template <class PO, class EA>
-    static __device__ __forceinline__ void epi_aux_i(PO p, EA e, float alpha,
-                                                int64_t m_base, int64_t n_base, const f32x4 *vals,
-                                                int j0, int jc) {
+    static __device__ __forceinline__ void epi_aux(const Prob &p, const EpiArgs &e, float alpha,
+                                                   int64_t m_base, int64_t n_base, const f32x4 *vals,
+                                                   int j0, int jc) {
         Out *D = reinterpret_cast<Out *>(p.D);
         const Out *C = reinterpret_cast<const Out *>(p.C);
         const Out *bias = reinterpret_cast<const Out *>(e.bias);
@@ -1459,13 +1449,6 @@ struct Tile {
             }
         }
     }
-    template <class PO, class EA>
-    static __device__ __noinline__ void epi_aux(PO p, EA e, float alpha,
-                                                int64_t m_base, int64_t n_base, const f32x4 *vals,
-                                                int j0, int jc) {
-        epi_aux_i<PO, EA>(p, e, alpha, m_base, n_base, vals, j0, jc);
-    }
-
     // Fragment rows per LDS hand-off to epi_aux: as many as the tile's LDS holds.
     static constexpr int AUX_JC_FIT = LDS_BYTES / (NT * FN * 4 * 16);
     static constexpr int AUX_JC = AUX_JC_FIT >= FM ? FM : AUX_JC_FIT;
@@ -1474,10 +1457,9 @@ struct Tile {
     // Edge tiles, ColumnMajor C/D or unaligned C/D: element by element, with
     // the accumulators of fragment rows j0 .. j0+jc-1 handed over through the
     // idle LDS exactly as for epi_aux (no private scratch array).
-    template <class PO, class EA>
-    static __device__ __forceinline__ void epi_slow_i(PO p, EA e, float alpha,
-                                                 int64_t m_base, int64_t n_base, const f32x4 *vals,
-                                                 int j0, int jc) {
+    static __device__ __forceinline__ void epi_slow(const Prob &p, const EpiArgs &e, float alpha,
+                                                    int64_t m_base, int64_t n_base, const f32x4 *vals,
+                                                    int j0, int jc) {
         Out *D = reinterpret_cast<Out *>(p.D);
         const Out *C = reinterpret_cast<const Out *>(p.C);
         const int tid = threadIdx.x;
@@ -1506,13 +1488,6 @@ struct Tile {
                 }
         }
     }
-    template <class PO, class EA>
-    static __device__ __noinline__ void epi_slow(PO p, EA e, float alpha,
-                                                 int64_t m_base, int64_t n_base, const f32x4 *vals,
-                                                 int j0, int jc) {
-        epi_slow_i<PO, EA>(p, e, alpha, m_base, n_base, vals, j0, jc);
-    }
-
     // `lds`: the tile's LDS, idle here (the main loop ends with a barrier);
     // every path but the interior vector one hands the accumulators over
     // through it and closes with a barrier before the next tile's copies may
@@ -1547,22 +1522,11 @@ struct Tile {
                         buf[((jj * FN + i) * 4 + q) * NT + tid] =
                             f32x4{acc.v[i][j0 + jj][q * 4], acc.v[i][j0 + jj][q * 4 + 1],
                                   acc.v[i][j0 + jj][q * 4 + 2], acc.v[i][j0 + jj][q * 4 + 3]};
-            // The out-of-line paths take their arguments by value on tiles
-            // up to 128 x 128: a reference makes the kernel copy its
-            // arguments to private memory at entry and read them from there
-            // (several microseconds of a small GEMM). The 256 x 256 kernels
-            // keep references: their main loop's register allocation is
-            // spill-free only that way.
-            if constexpr (BM * BN <= 128 * 128) {
-                const EpiOut o{p.D, p.C, p.M, p.N};
-                if (interior) epi_aux<EpiOut, EpiArgs>(o, e, alpha, m_base, n_base, buf, j0, AUX_JC);
-                else epi_slow<EpiOut, EpiArgs>(o, e, alpha, m_base, n_base, buf, j0, AUX_JC);
-            } else {
-                if (interior)
-                    epi_aux_i<const Prob &, const EpiArgs &>(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
-                else
-                    epi_slow_i<const Prob &, const EpiArgs &>(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
-            }
+            // inline: an out-of-line call made the kernel save and restore
+            // its live accumulators through scratch around every call
+            // (256x256 layer GEMMs +2.4 %, 64-problem grouped +2.7 %)
+            if (interior) epi_aux(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
+            else epi_slow(p, e, alpha, m_base, n_base, buf, j0, AUX_JC);
         }
         __syncthreads();
     }
@@ -1574,6 +1538,7 @@ struct Tile {
     // invalidate (what a __threadfence() costs) is needed.
 
     static constexpr int SC1 = 16;   // cache-policy bit: device scope
+
 
     // A partial tile is stored group-major (16-byte group g of thread tid at
     // (g * NT + tid) * 16). Lanes whose M row lies past the problem (rows
