@@ -376,6 +376,37 @@ def test_grouped_two_tile_classes_integer_exact(dab, la, lb):
     plan.close()
 
 
+def test_grouped_many_problems_tile_queue_integer_exact():
+    """150 problems of uneven cost (K from 8 to 1032, M and N from 1 to 300):
+    more tiles than the persistent grid, so most tiles come from the per-XCD
+    claim queues; three calls in a row (the queue words reset themselves at
+    the end of each launch) and a plain single GEMM in between on the same
+    plan. Every output exact, NaN-prefilled, guards intact."""
+    rng = np.random.default_rng(77)
+    shapes = [(int(rng.integers(1, 301)), int(rng.integers(1, 301)), int(rng.integers(1, 130)) * 8)
+              for _ in range(150)]
+    probs = [_int_problem("f16", "f16", "row", "row", "row", M=m, N=n, K=k, seed=500 + i)
+             for i, (m, n, k) in enumerate(shapes)]
+    want = [oracle.gemm(p).d_exact for p in probs]
+    plan = g.Plan("f16", la="row", lb="row", lc="row")
+    ops = [device_operands(p) for p in probs]
+    outs = [make_out(p) for p in probs]
+    for rep in range(3):
+        for buf, D in outs:
+            D.fill_(float("nan"))
+        print(f"[gpu] grouped 150 problems, call {rep}", flush=True)
+        plan.run_grouped([(p.M, p.N, p.K, o[0], o[1], o[2], d[1])
+                          for p, o, d in zip(probs, ops, outs)], 1.0, 1.0)
+        torch.cuda.synchronize()
+        for p, w, (buf, D) in zip(probs, want, outs):
+            acceptance.check_exact(logical(D, p), w, f"grouped queue call {rep} {p.M}x{p.N}x{p.K}")
+            check_guards(buf, p)
+        if rep == 1:   # a single GEMM on the same plan between grouped calls
+            q = _int_problem("f16", "f16", "row", "row", "row", M=300, N=200, K=64, seed=9)
+            exact(run(q, plan=plan), q, what="single between grouped calls")
+    plan.close()
+
+
 # ------------------------------------------------------------ edge cases
 
 def test_k_zero_gives_beta_c():
