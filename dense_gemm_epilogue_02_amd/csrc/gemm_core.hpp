@@ -55,6 +55,7 @@ enum Family { FAM_F32 = 0, FAM_F16 = 1, FAM_BF16 = 2, FAM_F8 = 3, FAM_MXF8 = 4, 
 
 constexpr uint32_t OOB_OFFSET = 0x80000000u;
 constexpr int NUM_RECORDS = 0x7FFFFFFF;
+constexpr int ST_POLICY = 2;   // buffer store cache policy: non-temporal (nt)
 constexpr int RSRC_FLAGS = 0x00020000;   // gfx9 raw buffer, 32-bit data format
 
 // ---------------------------------------------------------------- per-family
@@ -1395,12 +1396,27 @@ struct Tile {
         __syncthreads();
         char *Dt = p.D + ((int64_t)tm * BM * p.N + (int64_t)tn * BN) * OSZ;
         const int64_t ld = p.N * OSZ;
+        // streaming (non-temporal) stores when the tile's rows stay within
+        // 32-bit buffer offsets: D is not read again by this kernel
+        if ((int64_t)BM * ld < 0x7FFF0000LL) {
+            const __amdgpu_buffer_rsrc_t rd = make_rsrc(Dt);
+            const uint32_t ld32 = (uint32_t)ld;
 #pragma unroll 8
-        for (int it = 0; it < BM * OCPR / NT; ++it) {
-            const int c = tid + it * NT;
-            const int r = c / OCPR, k = c - (c / OCPR) * OCPR;
-            const u32x4 val = *reinterpret_cast<const u32x4 *>(lds + out_off(r, k * 16));
-            *reinterpret_cast<u32x4 *>(Dt + r * ld + k * 16) = val;
+            for (int it = 0; it < BM * OCPR / NT; ++it) {
+                const int c = tid + it * NT;
+                const int r = c / OCPR, k = c - (c / OCPR) * OCPR;
+                const u32x4 val = *reinterpret_cast<const u32x4 *>(lds + out_off(r, k * 16));
+                __builtin_amdgcn_raw_buffer_store_b128(val, rd, (uint32_t)r * ld32 + (uint32_t)(k * 16),
+                                                       0, ST_POLICY);
+            }
+        } else {
+#pragma unroll 8
+            for (int it = 0; it < BM * OCPR / NT; ++it) {
+                const int c = tid + it * NT;
+                const int r = c / OCPR, k = c - (c / OCPR) * OCPR;
+                const u32x4 val = *reinterpret_cast<const u32x4 *>(lds + out_off(r, k * 16));
+                *reinterpret_cast<u32x4 *>(Dt + r * ld + k * 16) = val;
+            }
         }
         __syncthreads();
     }
