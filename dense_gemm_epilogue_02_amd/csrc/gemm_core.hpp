@@ -1143,10 +1143,10 @@ struct Tile {
     // (issued early, they have the rest of the substep to land: 2-5 % faster
     // than over the first half, 5-10 % faster than over all of it), the
     // first half of the 4 on 64x64 wave tiles (a quarter measured no
-    // better there); the LDS writes, then the global loads, on the rest
-    // (the writes go to the other stage, but the compiler cannot prove that,
-    // so they stay behind the reads), spread evenly, so the memory
-    // instructions issue in the MFMAs' shadow.
+    // better there); the LDS writes and the global loads on the rest (the
+    // writes go to the other stage, but the compiler cannot prove that, so
+    // they stay behind the reads), spread evenly, so the memory instructions
+    // issue in the MFMAs' shadow.
     template <int NREAD, int NW, int NL, int Q = 0>
     static __device__ __forceinline__ void rs_sched() {
         constexpr int NMMA = FN * FM;
@@ -1159,8 +1159,13 @@ struct Tile {
             } else {
                 constexpr int W = NMMA - H, h = Q - H, TOT = NW + NL;
                 constexpr int e0 = h * TOT / W, e1 = (h + 1) * TOT / W;
-                constexpr int nw = (e1 < NW ? e1 : NW) - (e0 < NW ? e0 : NW);
-                constexpr int nl = (e1 - e0) - nw;
+                // 128x128 wave tiles of K-contiguous operands: writes and
+                // loads interleaved in proportion (1-2 % faster than all
+                // writes first); otherwise writes first (no gain measured)
+                constexpr bool MIX = NMMA >= 16 && A_KC && B_KC;
+                constexpr int nw = MIX ? NW * (h + 1) / W - NW * h / W
+                                       : (e1 < NW ? e1 : NW) - (e0 < NW ? e0 : NW);
+                constexpr int nl = MIX ? NL * (h + 1) / W - NL * h / W : (e1 - e0) - nw;
                 if constexpr (nw > 0) __builtin_amdgcn_sched_group_barrier(0x200, nw, 0);   // DS write
                 if constexpr (nl > 0) __builtin_amdgcn_sched_group_barrier(0x020, nl, 0);   // VMEM read
             }
