@@ -44,7 +44,8 @@
  *     address or contiguous extent do not allow 16-byte vector loads run on a
  *     slower, scalar-load kernel with the same arithmetic contract.
  *   - A plan owns one device workspace (stream-K / split-K partial tiles and
- *     their arrival counters, the grouped descriptor table) that every run
+ *     their arrival counters, the grouped descriptor table and tile queues)
+ *     that every run
  *     call of the plan shares. A plan must therefore not run on two streams
  *     at once, for any run call: two overlapping runs of one plan race on
  *     the workspace (wrong D, counters left dirty). Create one plan per
@@ -115,7 +116,8 @@ typedef enum {
     GEMM_TILE_32x256 = 4,
     GEMM_TILE_GENERIC = 5,  /* the scalar-load kernel, for any alignment */
     GEMM_TILE_WHOLEK = 6    /* 32x32 blocks, all of K loaded at once: small problems with
-                               K <= 1024 (fp32, fp16, bf16); batch 1, no MX scales */
+                               K <= 1024 (fp32, fp16, bf16); batch 1, no MX scales; a
+                               problem it cannot take runs on the heuristic tile */
 } gemm_tile;
 
 typedef struct gemm_plan_s *gemm_plan_t;
@@ -309,8 +311,11 @@ typedef struct {
  * layouts and epilogue, and shared alpha/beta, in one persistent launch.
  * `problems` is a host array, copied before the call returns (the caller may
  * free it at once). Problems with M, N or K == 0 follow the single-GEMM
- * rules. The plan keeps a device copy of the descriptor table: one plan must
- * not run grouped calls on two streams at once. */
+ * rules. Workgroups take their first tile, then claim further tiles from
+ * per-XCD queues (so problems of different K finish together); results do
+ * not depend on which workgroup ran a tile. The plan keeps a device copy of
+ * the descriptor table and the queue words (zeroed by each launch for the
+ * next): one plan must not run grouped calls on two streams at once. */
 gemm_status grouped_gemm_run(gemm_plan_t plan, const gemm_problem *problems,
                              int32_t count, float alpha, float beta,
                              void *stream);
