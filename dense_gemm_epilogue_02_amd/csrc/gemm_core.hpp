@@ -1147,7 +1147,7 @@ struct Tile {
     // writes go to the other stage, but the compiler cannot prove that, so
     // they stay behind the reads), spread evenly, so the memory instructions
     // issue in the MFMAs' shadow.
-    template <int NREAD, int NW, int NL, int Q = 0>
+    template <int NREAD, int NW, int NL, int Q = 0, bool MIXOK = true>
     static __device__ __forceinline__ void rs_sched() {
         constexpr int NMMA = FN * FM;
         constexpr int H = NMMA >= 16 ? NMMA / 4 : NMMA / 2;
@@ -1161,15 +1161,18 @@ struct Tile {
                 constexpr int e0 = h * TOT / W, e1 = (h + 1) * TOT / W;
                 // 128x128 wave tiles of K-contiguous operands: writes and
                 // loads interleaved in proportion (1-2 % faster than all
-                // writes first); otherwise writes first (no gain measured)
-                constexpr bool MIX = NMMA >= 16 && A_KC && B_KC;
+                // writes first), except in the substep that ends at the
+                // barrier, whose writes go first so the wait before the
+                // barrier is short (another 1-2 %); otherwise writes first
+                // (no gain measured)
+                constexpr bool MIX = NMMA >= 16 && A_KC && B_KC && MIXOK;
                 constexpr int nw = MIX ? NW * (h + 1) / W - NW * h / W
                                        : (e1 < NW ? e1 : NW) - (e0 < NW ? e0 : NW);
                 constexpr int nl = MIX ? NL * (h + 1) / W - NL * h / W : (e1 - e0) - nw;
                 if constexpr (nw > 0) __builtin_amdgcn_sched_group_barrier(0x200, nw, 0);   // DS write
                 if constexpr (nl > 0) __builtin_amdgcn_sched_group_barrier(0x020, nl, 0);   // VMEM read
             }
-            rs_sched<NREAD, NW, NL, Q + 1>();
+            rs_sched<NREAD, NW, NL, Q + 1, MIXOK>();
         }
     }
 
@@ -1256,7 +1259,7 @@ struct Tile {
                     if (o < RS_UA) sa.template load<Q>(o, ra, kn);
                     else sb.template load<Q>(o - RS_UA, rb, kn);
                 }
-                rs_sched<RS_READS, rs_count_w(S), rs_count_l(S)>();
+                rs_sched<RS_READS, rs_count_w(S), rs_count_l(S), 0, S != SUBSTEPS - 2>();
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (S == SUBSTEPS - 2) {
                     // this wave's writes of k-tile i+1 and reads of k-tile i
