@@ -14,7 +14,7 @@ import dense_gemm_epilogue_02_amd as g
 import oracle
 from oracle import acceptance
 import synthetic as syn
-from gpu_util import DEV, check_guards, logical, make_out, scales
+from gpu_util import DEV, check_guards, full_size_samples, logical, make_out, scales
 
 pytestmark = pytest.mark.gpu
 S, T = g.Schedule, g.Tile
@@ -171,16 +171,20 @@ def test_aux_k_zero():
     exact(q, "relu", "K=0")
 
 
-@pytest.mark.parametrize("M,N,K", [(4096, 8192, 8192), (16, 8192, 28672)])
-def test_aux_full_size_sampled(M, N, K):
-    """Layer shapes (O projection with a residual add; a decode row count)."""
+@pytest.mark.parametrize("M,N,K", [(4096, 8192, 8192), (4096, 8192, 28672), (16, 8192, 28672)])
+def test_aux_full_size_every_block(M, N, K):
+    """The residual-add workload's shapes (O and down projections with the
+    residual stream as the auxiliary tensor) and a decode row count: every
+    output written, one oracle entry in every 32 x 32 block of D and Z plus
+    the corners of every tile."""
     p = syn.make_problem(M, N, K, dtype_ab="bf16", dtype_cd="bf16", lb="col", std_b=0.02,
                          seed=136)
     syn.add_aux(p, "add", "before", seed=137)
     d, z = run_aux(p, act="identity")
-    rng = np.random.default_rng(138)
-    ii, jj = rng.integers(0, M, 64), rng.integers(0, N, 64)
-    ii[:2], jj[:2] = (0, M - 1), (0, N - 1)
+    plan = g.Plan("bf16", la="row", lb="col", lc="row")
+    desc = plan.describe(M, N, K)
+    plan.close()
+    ii, jj = full_size_samples(M, N, 138, desc)
     r = oracle.gemm_entries(p, ii, jj)
     acceptance.check_close(d[ii, jj], r.ref, r.S, "bf16", "bf16", f"{M}x{N}x{K} D")
     acceptance.check_close(z[ii, jj], r.z_ref, r.z_S, "bf16", "bf16", f"{M}x{N}x{K} Z")
