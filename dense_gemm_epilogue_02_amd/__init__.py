@@ -376,6 +376,24 @@ def _need(t, n: int, name: str, dtype: Dtype):
         raise ValueError(f"{name} holds {t.numel() * per} elements, needs {n}")
 
 
+class GroupedProblems:
+    """A grouped problem list checked against a plan once and packed into the
+    C array of gemm_problem (the tensors are kept alive with it), so repeated
+    launches of the same list cost no per-problem Python work."""
+
+    def __init__(self, plan: "Plan", problems: Iterable[tuple], beta: float = 0.0):
+        probs = list(problems)
+        for (M, N, K, A, B, C, D) in probs:
+            plan.check(A, B, C, D, M, N, K, beta)
+        self.plan = plan
+        self.beta = beta
+        self.count = len(probs)
+        self.arr = (gemm_problem * max(1, len(probs)))()
+        for i, (M, N, K, A, B, C, D) in enumerate(probs):
+            self.arr[i] = gemm_problem(M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(D))
+        self._keep = probs
+
+
 class Plan:
     """A plan bound to element types, layouts and epilogue (reusable across shapes)."""
 
@@ -518,7 +536,22 @@ class Plan:
         gemm_plan_run_batched(self.handle, A, B, C, D, bias, M, N, K, batch, sa, sb, sc, sd,
                               alpha, beta, scale_a, scale_b, stream)
 
-    def run_grouped(self, problems: Iterable[tuple], alpha=1.0, beta=0.0, stream=None):
+    def prepare_grouped(self, problems: Iterable[tuple], beta=0.0) -> "GroupedProblems":
+        """Check a grouped problem list once and pack it into the C array
+        grouped_gemm_run takes; run_grouped with the result skips both."""
+        return GroupedProblems(self, problems, beta)
+
+    def run_grouped(self, problems, alpha=1.0, beta=0.0, stream=None):
+        """problems: a sequence of (M, N, K, A, B, C, D), or a GroupedProblems
+        prepared by this plan (checked for a beta that reads C)."""
+        if isinstance(problems, GroupedProblems):
+            if problems.plan is not self:
+                raise ValueError("GroupedProblems was prepared for another plan")
+            if beta != 0.0 and problems.beta == 0.0:
+                raise ValueError("GroupedProblems was prepared for beta == 0: C was not checked")
+            _check(lib.grouped_gemm_run(self.handle, problems.arr, problems.count, alpha, beta,
+                                        _stream(stream)))
+            return
         probs = list(problems)
         for (M, N, K, A, B, C, D) in probs:
             self.check(A, B, C, D, M, N, K, beta)

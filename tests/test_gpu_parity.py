@@ -376,6 +376,38 @@ def test_grouped_two_tile_classes_integer_exact(dab, la, lb):
     plan.close()
 
 
+def test_grouped_prepared_list_matches_and_guards():
+    """A problem list checked and packed once (Plan.prepare_grouped) runs
+    bitwise like the plain list, repeatedly; it refuses another plan and a
+    beta that would read an unchecked C."""
+    probs = [_int_problem("f16", "f16", "row", "row", "row", M=m, N=n, K=k, seed=60 + i)
+             for i, (m, n, k) in enumerate([(300, 200, 64), (64, 520, 136), (1, 33, 8), (257, 256, 512)])]
+    plan = g.Plan("f16", la="row", lb="row", lc="row")
+    ops = [device_operands(p) for p in probs]
+    a_out = [make_out(p) for p in probs]
+    b_out = [make_out(p) for p in probs]
+    plan.run_grouped([(p.M, p.N, p.K, o[0], o[1], o[2], d[1]) for p, o, d in zip(probs, ops, a_out)],
+                     1.0, 1.0)
+    prep = plan.prepare_grouped([(p.M, p.N, p.K, o[0], o[1], o[2], d[1])
+                                 for p, o, d in zip(probs, ops, b_out)], 1.0)
+    for _ in range(3):
+        plan.run_grouped(prep, 1.0, 1.0)
+    torch.cuda.synchronize()
+    for p, (ba, Da), (bb, Db) in zip(probs, a_out, b_out):
+        assert torch.equal(Da, Db)
+        exact(logical(Db, p), p, what=f"prepared grouped {p.M}x{p.N}x{p.K}")
+        check_guards(bb, p)
+    prep0 = plan.prepare_grouped([(p.M, p.N, p.K, o[0], o[1], None, d[1])
+                                  for p, o, d in zip(probs, ops, b_out)], 0.0)
+    with pytest.raises(ValueError):
+        plan.run_grouped(prep0, 1.0, 1.0)
+    other = g.Plan("f16", la="row", lb="row", lc="row")
+    with pytest.raises(ValueError):
+        other.run_grouped(prep, 1.0, 1.0)
+    other.close()
+    plan.close()
+
+
 def test_grouped_many_problems_tile_queue_integer_exact():
     """150 problems of uneven cost (K from 8 to 1032, M and N from 1 to 300):
     more tiles than the persistent grid, so most tiles come from the per-XCD
