@@ -488,3 +488,41 @@ def test_config_cache_import_survives_random_mutations():
         assert g.lib.gemm_plan_cache_import(h, ("[" * 100000).encode()) == g.Status.INVALID_ARG
     finally:
         g.gemm_plan_destroy(h)
+
+
+def test_describe_wholek_eligibility():
+    """Host-only: when the whole-K kernel is chosen (AUTO) or taken when
+    pinned, and when a request for it falls back to the tile kernels."""
+    def d(plan, M, N, K):
+        return plan.describe(M, N, K)
+    f16 = g.Plan("f16", la="row", lb="row", lc="row")
+    # AUTO: few 128x128 tiles and K <= 1024 -> whole-K, one block per 32x32
+    x = d(f16, 200, 136, 1000)
+    assert x["kernel"] == "wholek" and x["grid"] == 7 * 5, x
+    # K-contiguous A with rows that are not whole 16-byte chunks: not whole-K
+    assert d(f16, 200, 136, 1001)["kernel"] != "wholek"
+    # long K, or enough tiles to fill the GPU: the tile kernels
+    assert d(f16, 200, 136, 1088)["kernel"] == "tile"
+    assert d(f16, 4096, 4096, 512)["kernel"] == "tile"
+    # a pinned schedule asks for the tile kernels even when whole-K could run
+    f16.set_config(g.Schedule.STREAM_K, g.Tile.AUTO, 0)
+    assert d(f16, 200, 136, 1000)["kernel"] == "tile"
+    # pinned whole-K on a problem it cannot take: the heuristic tile
+    f16.set_config(g.Schedule.AUTO, g.Tile.WHOLEK, 0)
+    assert d(f16, 4096, 4096, 512)["kernel"] == "wholek"     # K fits: taken even when large
+    assert d(f16, 64, 64, 2048)["kernel"] == "tile"
+    # batched calls never take it
+    assert f16.describe_batched(200, 136, 1000, 4)["kernel"] == "tile"
+    f16.close()
+    # M/N-contiguous operands load element by element: any K up to the limit
+    cc = g.Plan("bf16", la="col", lb="row", lc="row")
+    assert d(cc, 40, 31, 13)["kernel"] == "wholek"
+    cc.close()
+    # fp8 has no whole-K form
+    f8 = g.Plan("f8e4m3", la="row", lb="col", lc="row")
+    assert d(f8, 64, 64, 256)["kernel"] == "tile"
+    f8.close()
+    # fp32: four waves up to K = 512, eight up to 1024
+    f32 = g.Plan("f32", la="row", lb="row", lc="row")
+    assert d(f32, 128, 64, 512)["waves"] == 4 and d(f32, 128, 64, 1024)["waves"] == 8
+    f32.close()
