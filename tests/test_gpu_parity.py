@@ -569,3 +569,36 @@ def test_bias_without_activation_equals_shifted_linear():
     shifted = run(p)
     want = np.tile(p.bias.to(torch.float64).numpy(), (p.M, 1))
     assert np.array_equal(shifted - base, want)
+
+
+def test_grouped_same_k_round_robin_integer_exact():
+    """Problems that all share K take the static round robin instead of the
+    claim queues: 140 problems of K = 96 with M and N from 1 to 384 (more
+    tiles than the persistent grid, so workgroups run several), two calls in
+    a row, then a mixed-K call on the same plan (queue path) and the same-K
+    list again. Every output exact, NaN-prefilled, guards intact."""
+    rng = np.random.default_rng(78)
+    same = [(int(rng.integers(1, 385)), int(rng.integers(1, 385)), 96) for _ in range(140)]
+    mixed = [(64, 200, 8), (300, 64, 1032), (129, 129, 96)]
+    plan = g.Plan("f16", la="row", lb="row", lc="row")
+
+    def call(shapes, seed0, what):
+        probs = [_int_problem("f16", "f16", "row", "row", "row", M=m, N=n, K=k, seed=seed0 + i)
+                 for i, (m, n, k) in enumerate(shapes)]
+        ops = [device_operands(p) for p in probs]
+        outs = [make_out(p) for p in probs]
+        for buf, D in outs:
+            D.fill_(float("nan"))
+        print(f"[gpu] grouped {what}: {len(probs)} problems", flush=True)
+        plan.run_grouped([(p.M, p.N, p.K, o[0], o[1], o[2], d[1])
+                          for p, o, d in zip(probs, ops, outs)], 1.0, 1.0)
+        torch.cuda.synchronize()
+        for p, (buf, D) in zip(probs, outs):
+            acceptance.check_exact(logical(D, p), oracle.gemm(p).d_exact, f"{what} {p.M}x{p.N}x{p.K}")
+            check_guards(buf, p)
+
+    call(same, 700, "same K, call 0")
+    call(same, 700, "same K, call 1")
+    call(mixed, 900, "mixed K")
+    call(same, 1000, "same K after the queue path")
+    plan.close()
