@@ -316,7 +316,7 @@ struct Sched {
     // stream-K or split-K): each workgroup takes tile v first, then the next
     // unclaimed tile when it finishes one, so tiles of unequal cost (grouped
     // problems of different K) spread evenly. With the XCD remap one queue
-    // per XCD: the tiles past the first `grid` go in chunks of grid / 8
+    // per XCD: the tiles past the first `grid` go in chunks of QUEUE_CHUNK
     // consecutive tiles to the XCDs in turn, so the workgroups of one XCD
     // stay on neighbouring tiles (shared panels in its L2). queue[0 .. 7]
     // count claims, queue[8] finished workgroups; the last workgroup to
@@ -1716,6 +1716,12 @@ __device__ __forceinline__ int sk_owner(int64_t x, int64_t T, int G) {
 // LDS: the first barrier waits for the waves still reading the LDS (output
 // staging), the last keeps the next copy into LDS from overwriting the word
 // before every wave has read it. total_tiles when the queue is exhausted.
+// Tiles per chunk of a per-XCD queue. Small enough that the costly tiles at
+// the head of a grouped list spread over the eight XCDs (the XCD that drew
+// one chunk more of them finished last with chunks of grid / 8 = 64 tiles:
+// 64-problem fp16 mix 362-369 -> 348-354 us with 16, same box), large enough
+// for four raster columns of neighbouring tiles.
+constexpr int QUEUE_CHUNK = 16;
 __device__ __forceinline__ int queue_count(const Sched &s) {
     return s.xcd_remap && (s.grid & 7) == 0 ? 8 : 1;
 }
@@ -1723,7 +1729,8 @@ __device__ __forceinline__ int queue_next(unsigned int claim, const Sched &s, ch
     int *slot = reinterpret_cast<int *>(lds);
     __syncthreads();
     if (threadIdx.x == 0) {
-        const int nq = queue_count(s), chunk = s.grid / nq, x = nq == 8 ? (int)(blockIdx.x & 7) : 0;
+        const int nq = queue_count(s), chunk = nq == 8 ? QUEUE_CHUNK : s.grid;
+        const int x = nq == 8 ? (int)(blockIdx.x & 7) : 0;
         const int64_t t = s.grid + ((int64_t)(claim / chunk) * nq + x) * chunk + claim % chunk;
         *slot = t < s.total_tiles ? (int)t : s.total_tiles;
     }

@@ -130,7 +130,8 @@ def test_forced_schedules_replay_clean_over_many_shapes():
 # With a queue, workgroup v (virtual id) runs tile v first; every later tile
 # comes from a claim on its XCD's queue (blockIdx & 7 when the grid is a
 # multiple of 8 and the XCD remap is on, else one queue). Claim c of queue x
-# is tile grid + ((c // chunk) * nq + x) * chunk + c % chunk, chunk = grid / nq;
+# is tile grid + ((c // chunk) * nq + x) * chunk + c % chunk (chunk = 16 with
+# eight queues, grid with one);
 # a claim past the last tile ends the workgroup. The replay interleaves the
 # workgroups' claims in an arbitrary order (a seeded shuffle of who claims
 # next) and checks that every tile runs exactly once and that each queue's
@@ -139,7 +140,7 @@ def test_forced_schedules_replay_clean_over_many_shapes():
 def queue_replay(total, grid, remap, order_seed):
     import random
     nq = 8 if remap and grid % 8 == 0 else 1
-    chunk = grid // nq
+    chunk = 16 if nq == 8 else grid
     claims = [0] * nq
     ran = {}
     rng = random.Random(order_seed)
