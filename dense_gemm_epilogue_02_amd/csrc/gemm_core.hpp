@@ -1711,20 +1711,21 @@ __device__ __forceinline__ int sk_owner(int64_t x, int64_t T, int G) {
     return (int)(((x + 1) * G + T - 1) / T) - 1;
 }
 
-// The tile after `claim` (the queue's count before this workgroup's claim),
-// handed to every thread of the workgroup through the first word of the idle
-// LDS: the first barrier waits for the waves still reading the LDS (output
-// staging), the last keeps the next copy into LDS from overwriting the word
-// before every wave has read it. total_tiles when the queue is exhausted.
 // Tiles per chunk of a per-XCD queue. Small enough that the costly tiles at
 // the head of a grouped list spread over the eight XCDs (the XCD that drew
 // one chunk more of them finished last with chunks of grid / 8 = 64 tiles:
 // 64-problem fp16 mix 362-369 -> 348-354 us with 16, same box), large enough
 // for four raster columns of neighbouring tiles.
 constexpr int QUEUE_CHUNK = 16;
+// Queues of a launch: one per XCD with the remap and a grid of whole XCDs.
 __device__ __forceinline__ int queue_count(const Sched &s) {
     return s.xcd_remap && (s.grid & 7) == 0 ? 8 : 1;
 }
+// The tile after `claim` (the queue's count before this workgroup's claim),
+// handed to every thread of the workgroup through the first word of the idle
+// LDS: the first barrier waits for the waves still reading the LDS (output
+// staging), the last keeps the next copy into LDS from overwriting the word
+// before every wave has read it. total_tiles when the queue is exhausted.
 __device__ __forceinline__ int queue_next(unsigned int claim, const Sched &s, char *lds) {
     int *slot = reinterpret_cast<int *>(lds);
     __syncthreads();

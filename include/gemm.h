@@ -313,8 +313,9 @@ typedef struct {
  * free it at once). Problems with M, N or K == 0 follow the single-GEMM
  * rules. Workgroups take their first tile, then claim further tiles from
  * per-XCD queues (so problems of different K finish together), or, when all
- * problems have the same K, take every grid-th tile; results do not depend on
- * which workgroup ran a tile. The plan keeps a device copy of
+ * problems need the same number of k-tiles (the same K up to the kernel's k
+ * step), take every grid-th tile; results do not depend on which workgroup
+ * ran a tile. The plan keeps a device copy of
  * the descriptor table and the queue words (zeroed by each launch for the
  * next): one plan must not run grouped calls on two streams at once. */
 gemm_status grouped_gemm_run(gemm_plan_t plan, const gemm_problem *problems,
