@@ -394,6 +394,30 @@ class GroupedProblems:
         self._keep = probs
 
 
+class PreparedRun:
+    """One gemm_plan_run call checked against its plan once, its C arguments
+    converted once (the tensors are kept alive with it, the stream is the one
+    given or current when prepared): calling it launches the GEMM again on
+    the same buffers with no per-call Python checks. For small, launch-bound
+    problems run many times, as a serving loop holds its buffers; the
+    buffers' contents may change between calls, their shapes and addresses
+    may not."""
+
+    def __init__(self, plan: "Plan", A, B, C, D, M: int, N: int, K: int, alpha: float = 1.0,
+                 beta: float = 0.0, stream=None):
+        plan.check(A, B, C, D, M, N, K, beta)
+        self.plan = plan
+        vals = (plan.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(D), M, N, K, alpha, beta,
+                _stream(stream))
+        self._args = tuple(t(v) for t, v in zip(lib.gemm_plan_run.argtypes, vals))
+        self._keep = (A, B, C, D)
+
+    def __call__(self) -> None:
+        if self.plan.handle is None:   # the packed handle would be a dangling one
+            raise GemmError(Status.NOT_INITIALIZED, "PreparedRun: its plan was closed")
+        _check(lib.gemm_plan_run(*self._args))
+
+
 class Plan:
     """A plan bound to element types, layouts and epilogue (reusable across shapes)."""
 
@@ -458,6 +482,11 @@ class Plan:
         else:
             gemm_plan_run_scaled(self.handle, A, B, C, D, M, N, K, alpha, beta, scale_a,
                                  scale_b, stream)
+
+    def prepare(self, A, B, C, D, M, N, K, alpha=1.0, beta=0.0, stream=None) -> PreparedRun:
+        """run(A, B, C, D, M, N, K, alpha, beta) checked and packed once; the
+        returned PreparedRun launches it when called."""
+        return PreparedRun(self, A, B, C, D, M, N, K, alpha, beta, stream)
 
     def run_noalloc(self, A, B, C, D, M, N, K, alpha=1.0, beta=0.0, stream=None):
         """gemm_plan_run_noalloc: run() without any device allocation (the

@@ -602,3 +602,29 @@ def test_grouped_same_k_round_robin_integer_exact():
     call(mixed, 900, "mixed K")
     call(same, 1000, "same K after the queue path")
     plan.close()
+
+
+def test_prepared_run_matches_run_and_follows_buffer_contents():
+    """Plan.prepare checks and packs one run() once: calling it gives run()'s
+    result bitwise (exact against the oracle on integer data), sees new
+    contents written into the same buffers, and refuses to run once its plan
+    is closed."""
+    p = _int_problem("f32", "f32", "row", "row", "row", M=128, N=64, K=256, seed=41)
+    plan = g.Plan("f32", la="row", lb="row", lc="row")
+    A, B, C = (x.to(DEV) for x in (p.A, p.B, p.C))
+    D_run = torch.empty_like(C)
+    D_prep = torch.full_like(C, float("nan"))
+    prep = plan.prepare(A, B, C, D_prep, p.M, p.N, p.K, p.alpha, p.beta)
+    for rep in range(2):
+        if rep == 1:
+            A.mul_(-1.0)   # new contents, same buffer: the oracle's problem follows
+            p.A = -p.A
+        plan.run(A, B, C, D_run, p.M, p.N, p.K, p.alpha, p.beta)
+        D_prep.fill_(float("nan"))
+        prep()
+        torch.cuda.synchronize()
+        assert torch.equal(D_prep, D_run), f"prepared != run (call {rep})"
+        exact(D_prep.cpu().numpy().astype(np.float64), p, what=f"prepared call {rep}")
+    plan.close()
+    with pytest.raises(g.GemmError):
+        prep()
